@@ -1,0 +1,267 @@
+"""CPU oracle for the Global-QSGD compression operator -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library
+(``allreduce_compatible_gradient_amd``) never does, and shares no code with
+it: the arithmetic lives in ``gq_oracle.c`` (plain scalar C), and this module
+only marshals numpy arrays into it.
+
+Method: "Global-QSGD: Practical Floatless Quantization for Distributed
+Learning with Theoretical Guarantees" -- Sec. 2 for the (q,p)-norm, Sec. 3 for
+Global-Q and its two level families (standard dithering Global-L_s,
+exponential dithering Global-E_s), Sec. 6 for the quantize / integer
+Allreduce / dequantize pipeline.  The exact rules each function follows are
+written next to the C function it calls.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gq_oracle.c")
+_LIB_PATH = os.environ.get("GQ_ORACLE_LIB") or os.path.join(_HERE, "libgq_oracle.so")
+
+SCHEME_L = 0
+SCHEME_E = 1
+F32 = 0
+BF16 = 1
+
+_i64 = ctypes.c_int64
+_u64 = ctypes.c_uint64
+_int = ctypes.c_int
+_f32 = ctypes.c_float
+_vp = ctypes.c_void_p
+
+
+def build() -> str:
+    """Compile gq_oracle.c with gcc into libgq_oracle.so (plain C11, no FP contraction)."""
+    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wextra", _SRC, "-o", _LIB_PATH, "-lm"]
+    subprocess.run(cmd, check=True)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.oracle_philox4x32_10.argtypes = [_vp, _vp, _vp]
+        L.oracle_uniform32.argtypes = [_u64, _u64, _u64]
+        L.oracle_uniform32.restype = ctypes.c_uint32
+        L.oracle_global_norm.argtypes = [_vp, _int, _i64, _i64, _f32, _f32, _vp]
+        L.oracle_global_norm.restype = _f32
+        L.oracle_top_code.argtypes = [_int, _int]
+        L.oracle_top_code.restype = _i64
+        L.oracle_scale_params.argtypes = [_f32, _i64, _int, _int, _vp, _vp, _vp]
+        L.oracle_bracket.argtypes = [_f32, _f32, _f32, _int, _int, _int, _vp, _vp, _vp]
+        L.oracle_code.argtypes = [_f32, _f32, _f32, _int, _int, _int, ctypes.c_uint32]
+        L.oracle_code.restype = ctypes.c_int32
+        L.oracle_quantize.argtypes = [_vp, _int, _i64, _i64, _f32, _int, _int, _u64, _i64, _vp]
+        L.oracle_min_code_bits.argtypes = [_i64, _int, _int]
+        L.oracle_min_code_bits.restype = _int
+        L.oracle_row_bytes.argtypes = [_i64, _int]
+        L.oracle_row_bytes.restype = _i64
+        L.oracle_pack.argtypes = [_vp, _i64, _i64, _int, _vp]
+        L.oracle_unpack.argtypes = [_vp, _i64, _i64, _int, _vp]
+        L.oracle_sum_codes.argtypes = [_vp, _i64, _i64, _vp]
+        L.oracle_dequantize.argtypes = [_vp, _i64, _i64, _f32, _int, _int, _vp]
+        L.oracle_compress_mean_cols.argtypes = [_vp, _int, _i64, _i64, _f32, _int, _int, _u64,
+                                                _vp, _i64, _vp, _vp]
+        L.oracle_compress_mean.argtypes = [_vp, _int, _i64, _i64, _int, _f32, _f32, _int, _u64,
+                                           _vp, _vp]
+        L.oracle_compress_mean.restype = _f32
+        L.oracle_qsgd_local_mean.argtypes = [_vp, _int, _i64, _i64, _int, _u64, _vp, _vp, _vp]
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_vp)
+
+
+def _x_dtype(x: np.ndarray) -> int:
+    """fp32 arrays are fp32; uint16 arrays carry bf16 bit patterns."""
+    if x.dtype == np.float32:
+        return F32
+    if x.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle inputs are float32 or bf16 bits in uint16, got {x.dtype}")
+
+
+def _rows(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    if x.ndim != 2:
+        raise ValueError("x must be [n, d]")
+    return x
+
+
+def _order(v) -> float:
+    v = float(v)
+    if v == 2.0 or math.isinf(v):
+        return v
+    raise ValueError("q and p are 2 or inf")
+
+
+# ---------------------------------------------------------------------------
+# Random numbers
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    c = np.asarray(ctr, dtype=np.uint32).copy()
+    k = np.asarray(key, dtype=np.uint32).copy()
+    out = np.zeros(4, dtype=np.uint32)
+    lib().oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def uniform32(seed: int, worker: int, j: int) -> int:
+    return int(lib().oracle_uniform32(seed, worker, j))
+
+
+# ---------------------------------------------------------------------------
+# Norm, scalars, bracketing
+
+
+def global_norm(x: np.ndarray, q, p):
+    """Returns (N as np.float32, per-worker partials: sum of squares or max |x|)."""
+    x = _rows(x)
+    n, d = x.shape
+    pw = np.zeros(n, dtype=np.float64)
+    N = lib().oracle_global_norm(_ptr(x), _x_dtype(x), n, d, _order(q), _order(p), _ptr(pw))
+    return np.float32(N), pw
+
+
+def top_code(s: int, scheme: int) -> int:
+    return int(lib().oracle_top_code(s, scheme))
+
+
+def scale_params(N, n: int, s: int, scheme: int):
+    """(pre, sigma, kappa) for a norm N: pre-scale, fp32 scale, fp64 dequant factor."""
+    pre = np.zeros(1, np.float32)
+    sig = np.zeros(1, np.float32)
+    kap = np.zeros(1, np.float64)
+    lib().oracle_scale_params(float(N), n, s, scheme, _ptr(pre), _ptr(sig), _ptr(kap))
+    return pre[0], sig[0], kap[0]
+
+
+def bracket(xv, N, n: int, s: int, scheme: int):
+    """(m_lo, m_hi, F): the two candidate code magnitudes and the 32-bit threshold.
+
+    The code magnitude is m_hi with probability F / 2^32, else m_lo."""
+    pre, sig, _ = scale_params(N, n, s, scheme)
+    lo = np.zeros(1, np.int32)
+    hi = np.zeros(1, np.int32)
+    F = np.zeros(1, np.uint32)
+    lib().oracle_bracket(float(np.float32(xv)), float(pre), float(sig), int(np.float32(N) == 0),
+                         s, scheme, _ptr(lo), _ptr(hi), _ptr(F))
+    return int(lo[0]), int(hi[0]), int(F[0])
+
+
+def code(xv, N, n: int, s: int, scheme: int, u: int) -> int:
+    pre, sig, _ = scale_params(N, n, s, scheme)
+    return int(lib().oracle_code(float(np.float32(xv)), float(pre), float(sig),
+                                 int(np.float32(N) == 0), s, scheme, u))
+
+
+# ---------------------------------------------------------------------------
+# Pipeline pieces
+
+
+def quantize(x: np.ndarray, N, s: int, scheme: int, seed: int, worker_base: int = 0) -> np.ndarray:
+    x = _rows(x)
+    n, d = x.shape
+    codes = np.zeros((n, d), dtype=np.int32)
+    lib().oracle_quantize(_ptr(x), _x_dtype(x), n, d, float(N), s, scheme, seed, worker_base,
+                          _ptr(codes))
+    return codes
+
+
+def min_code_bits(n: int, s: int, scheme: int) -> int:
+    return int(lib().oracle_min_code_bits(n, s, scheme))
+
+
+def row_bytes(d: int, W: int) -> int:
+    return int(lib().oracle_row_bytes(d, W))
+
+
+def pack(codes: np.ndarray, W: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.int32)
+    if codes.ndim == 1:
+        codes = codes.reshape(1, -1)
+    n, d = codes.shape
+    out = np.zeros((n, row_bytes(d, W)), dtype=np.uint8)
+    lib().oracle_pack(_ptr(codes), n, d, W, _ptr(out))
+    return out
+
+
+def unpack(packed: np.ndarray, n: int, d: int, W: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    if packed.size != n * row_bytes(d, W):
+        raise ValueError("packed buffer has the wrong size")
+    codes = np.zeros((n, d), dtype=np.int32)
+    lib().oracle_unpack(_ptr(packed), n, d, W, _ptr(codes))
+    return codes
+
+
+def sum_codes(codes: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.int32)
+    n, d = codes.shape
+    sums = np.zeros(d, dtype=np.int64)
+    lib().oracle_sum_codes(_ptr(codes), n, d, _ptr(sums))
+    return sums
+
+
+def dequantize(sums: np.ndarray, n: int, N, s: int, scheme: int) -> np.ndarray:
+    sums = np.ascontiguousarray(sums, dtype=np.int64)
+    mean = np.zeros(sums.shape[0], dtype=np.float32)
+    lib().oracle_dequantize(_ptr(sums), n, sums.shape[0], float(N), s, scheme, _ptr(mean))
+    return mean
+
+
+def compress_mean(x: np.ndarray, s: int, q, p, scheme: int, seed: int):
+    """Whole pipeline. Returns (N, sums int64 [d], mean float32 [d])."""
+    x = _rows(x)
+    n, d = x.shape
+    sums = np.zeros(d, dtype=np.int64)
+    mean = np.zeros(d, dtype=np.float32)
+    N = lib().oracle_compress_mean(_ptr(x), _x_dtype(x), n, d, s, _order(q), _order(p), scheme,
+                                   seed, _ptr(sums), _ptr(mean))
+    return np.float32(N), sums, mean
+
+
+def compress_mean_cols(x: np.ndarray, N, s: int, scheme: int, seed: int, cols) -> tuple:
+    """Selected coordinates of the pipeline given the norm: (sums int64, mean float32)."""
+    x = _rows(x)
+    n, d = x.shape
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if cols.size and (cols.min() < 0 or cols.max() >= d):
+        raise IndexError("column out of range")
+    sums = np.zeros(cols.size, dtype=np.int64)
+    mean = np.zeros(cols.size, dtype=np.float32)
+    lib().oracle_compress_mean_cols(_ptr(x), _x_dtype(x), n, d, float(N), s, scheme, seed,
+                                    _ptr(cols), cols.size, _ptr(sums), _ptr(mean))
+    return sums, mean
+
+
+def qsgd_local_mean(x: np.ndarray, s: int, seed: int):
+    """Local-norm QSGD ablation. Returns (norms float32 [n], codes int32 [n, d], mean [d])."""
+    x = _rows(x)
+    n, d = x.shape
+    norms = np.zeros(n, dtype=np.float32)
+    codes = np.zeros((n, d), dtype=np.int32)
+    mean = np.zeros(d, dtype=np.float32)
+    lib().oracle_qsgd_local_mean(_ptr(x), _x_dtype(x), n, d, s, seed, _ptr(norms), _ptr(codes),
+                                 _ptr(mean))
+    return norms, codes, mean

@@ -1,0 +1,438 @@
+/*
+ * gq_oracle.c -- CPU oracle for the Global-QSGD compression operator.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is a plain, slow, scalar C
+ * implementation of what the HIP library computes.  Only the test suite,
+ * the smoke check and the CPU-baseline leg of the benchmark load it; the
+ * product library never does.  It shares no source, header, table or helper
+ * with the HIP path (allreduce_compatible_gradient_amd/csrc).
+ *
+ * What it follows (all from "Global-QSGD: Practical Floatless Quantization
+ * for Distributed Learning with Theoretical Guarantees", Xin, Canini,
+ * Richtarik, Horvath):
+ *   - Sec. 2 (notation): the l_p norm of one vector and the (q,p)-norm of the
+ *     concatenation x = [x_1..x_n], outer sum over the n workers.
+ *   - Sec. 3 (Global-Q definition, stripped from the page; taken in the
+ *     QSGD / dithering form the section builds on): every coordinate is
+ *     divided by ONE global norm, then rounded at random, without bias, to
+ *     one of the two neighbouring levels.
+ *   - Sec. 3 (the two level families): standard dithering Global-L_s with
+ *     levels (s-i)/s, and exponential dithering Global-E_s with levels
+ *     {0} and the powers of two 2^-k, k = 0..s-1.
+ *   - Sec. 6 (implementation): quantize, integer Allreduce (here: an exact
+ *     sum over the n simulated workers), dequantize once.
+ * Philox4x32-10 follows Salmon, Moraes, Dror, Shaw, "Parallel Random
+ * Numbers: As Easy as 1, 2, 3" (SC'11), Sec. on the Philox family.
+ *
+ * Readings where the pages leave a step open (all listed in the design
+ * notes of the repository): scale sigma and dequant factor kappa formed in
+ * fp64 and rounded once; fp32 per-element decisions; 32-bit threshold
+ * F = floor(f * 2^32) compared with a 32-bit uniform u (round up iff u < F);
+ * E-scheme codes are fixed-point integers (level 2^-k -> 2^(s-1-k));
+ * norms below 2^-64 are handled by an exact 2^64 pre-scale.
+ *
+ * Build: gcc -std=c11 -O2 -fPIC -shared -ffp-contract=off gq_oracle.c -lm
+ * (no -ffast-math: every float operation here is one IEEE-rounded step).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_SCHEME_L 0
+#define ORACLE_SCHEME_E 1
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* ------------------------------------------------------------------------ */
+/* Philox4x32-10 (SC'11).  Two 32x32->64 products per round on counter words
+ * 0 and 2; the new state takes the high halves xor-ed with the other counter
+ * words and the round key, and the low halves as they are.  The key is
+ * advanced by the Weyl constants before every round after the first.       */
+
+static void philox_round(uint32_t c[4], uint32_t k0, uint32_t k1)
+{
+    uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c[0];
+    uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)c[2];
+    uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    uint32_t n0 = hi1 ^ c[1] ^ k0;
+    uint32_t n1 = lo1;
+    uint32_t n2 = hi0 ^ c[3] ^ k1;
+    uint32_t n3 = lo0;
+    c[0] = n0; c[1] = n1; c[2] = n2; c[3] = n3;
+}
+
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        philox_round(c, k0, k1);
+    }
+    out[0] = c[0]; out[1] = c[1]; out[2] = c[2]; out[3] = c[3];
+}
+
+/* The 32-bit uniform used for element j of worker `worker`.
+ * Block b = j / 8 of a worker's row owns two Philox outputs:
+ *   A = Philox(key = seed, ctr = (lo32(b), hi32(b), worker, 0))
+ *   B = Philox(key = seed, ctr = (lo32(b), hi32(b), worker, 1))
+ * Element e = j % 8 takes 16-bit half (e % 2) of word e / 2 of A as the high
+ * half of u, and the same half of B as the low half.                       */
+uint32_t oracle_uniform32(uint64_t seed, uint64_t worker, uint64_t j)
+{
+    uint64_t b = j / 8;
+    unsigned e = (unsigned)(j % 8);
+    uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
+    uint32_t ca[4] = {(uint32_t)(b & 0xFFFFFFFFu), (uint32_t)(b >> 32), (uint32_t)worker, 0u};
+    uint32_t cb[4] = {(uint32_t)(b & 0xFFFFFFFFu), (uint32_t)(b >> 32), (uint32_t)worker, 1u};
+    uint32_t A[4], B[4];
+    oracle_philox4x32_10(ca, key, A);
+    oracle_philox4x32_10(cb, key, B);
+    unsigned shift = 16u * (e % 2u);
+    uint32_t hi16 = (A[e / 2] >> shift) & 0xFFFFu;
+    uint32_t lo16 = (B[e / 2] >> shift) & 0xFFFFu;
+    return (hi16 << 16) | lo16;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Inputs: row-major x[n][d], fp32 or bf16 (bf16 widened exactly).           */
+
+static float load_x(const void *x, int dtype, uint64_t idx)
+{
+    if (dtype == ORACLE_F32)
+        return ((const float *)x)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t *)x)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+static uint32_t float_bits(float f)
+{
+    uint32_t b;
+    memcpy(&b, &f, sizeof b);
+    return b;
+}
+
+/* Compensated (Neumaier) running sum in fp64: the result is the exact sum
+ * of the terms up to a couple of fp64 roundings, independent of length.   */
+typedef struct { double s, c; } nsum;
+
+static void nsum_add(nsum *a, double v)
+{
+    double t = a->s + v;
+    if (fabs(a->s) >= fabs(v))
+        a->c += (a->s - t) + v;
+    else
+        a->c += (v - t) + a->s;
+    a->s = t;
+}
+
+/* ------------------------------------------------------------------------ */
+/* (q,p)-norm of the concatenation, Sec. 2.  q selects the per-worker norm
+ * (2 or infinity), p the norm taken over the n per-worker norms.
+ * per_worker[i] receives sum_j x_ij^2 (q = 2) or max_j |x_ij| (q = inf).   */
+
+static int is_inf_order(float v) { return isinf(v) && v > 0; }
+
+float oracle_global_norm(const void *x, int dtype, int64_t n, int64_t d,
+                         float q, float p, double *per_worker)
+{
+    int q_inf = is_inf_order(q), p_inf = is_inf_order(p);
+    for (int64_t i = 0; i < n; ++i) {
+        if (q_inf) {
+            float m = 0.0f;
+            for (int64_t j = 0; j < d; ++j) {
+                float a = fabsf(load_x(x, dtype, (uint64_t)(i * d + j)));
+                if (a > m)
+                    m = a;
+            }
+            per_worker[i] = (double)m;
+        } else {
+            nsum acc = {0.0, 0.0};
+            for (int64_t j = 0; j < d; ++j) {
+                double v = (double)load_x(x, dtype, (uint64_t)(i * d + j));
+                nsum_add(&acc, v * v); /* exact: a 24-bit significand squared */
+            }
+            per_worker[i] = acc.s + acc.c;
+        }
+    }
+    /* combine over workers */
+    if (p_inf) {
+        double m = 0.0;
+        for (int64_t i = 0; i < n; ++i)
+            if (per_worker[i] > m)
+                m = per_worker[i];
+        return q_inf ? (float)m : (float)sqrt(m);
+    }
+    nsum tot = {0.0, 0.0};
+    for (int64_t i = 0; i < n; ++i)
+        nsum_add(&tot, q_inf ? per_worker[i] * per_worker[i] : per_worker[i]);
+    return (float)sqrt(tot.s + tot.c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Scalars of one quantization: pre-scale, scale sigma, dequant factor kappa.
+ *   M      = s (L) or 2^(s-1) (E): the integer code of the top level 1.
+ *   pre    = 2^64 if N < 2^-64, else 1 (exact; keeps sigma finite).
+ *   sigma  = fp32(s / (N*pre)) for L, fp32(1 / (N*pre)) for E, both in fp64.
+ *   kappa  = fp64(N / (n*M)): the value of one code unit in the mean.       */
+
+int64_t oracle_top_code(int s, int scheme)
+{
+    return scheme == ORACLE_SCHEME_L ? (int64_t)s : ((int64_t)1 << (s - 1));
+}
+
+void oracle_scale_params(float N, int64_t n, int s, int scheme,
+                         float *pre, float *sigma, double *kappa)
+{
+    float pr = (N < 0x1p-64f) ? 0x1p64f : 1.0f;
+    float Np = N * pr;
+    double num = (scheme == ORACLE_SCHEME_L) ? (double)s : 1.0;
+    *pre = pr;
+    *sigma = (float)(num / (double)Np);
+    *kappa = (double)N / ((double)n * (double)oracle_top_code(s, scheme));
+}
+
+/* The deterministic half of the rounding for one coordinate: the two integer
+ * codes (magnitudes) that bracket |x|/N on the level grid and the 32-bit
+ * threshold F.  The random half picks m_hi with probability F / 2^32.
+ *   L: t = min(fp32(|x|*pre*sigma), s); m_lo = floor(t); m_hi = m_lo + 1;
+ *      F = floor((t - floor(t)) * 2^32).
+ *   E: r = min(fp32(|x|*pre*sigma), 1), c = 2^(1-s).
+ *      r >= c, r = 2^e (1 + phi): m_lo = 2^(e+s-1), m_hi = 2 m_lo,
+ *      F = phi * 2^32 (exact: the 23 fraction bits of r, shifted).
+ *      r <  c: m_lo = 0, m_hi = 1, F = floor(r 2^(s-1) 2^32).
+ * N == 0 gives m_lo = m_hi = 0, F = 0.                                    */
+void oracle_bracket(float xv, float pre, float sigma, int zero_norm, int s, int scheme,
+                    int32_t *m_lo, int32_t *m_hi, uint32_t *F)
+{
+    if (zero_norm) {
+        *m_lo = 0; *m_hi = 0; *F = 0u;
+        return;
+    }
+    float a = fabsf(xv);
+    float t = (a * pre) * sigma;
+    if (scheme == ORACLE_SCHEME_L) {
+        float top = (float)s;
+        if (!(t <= top)) /* clamp; a NaN also lands on the top level */
+            t = top;
+        float lo = floorf(t);
+        float f = t - lo;
+        *m_lo = (int32_t)lo;
+        *m_hi = (int32_t)lo + 1;
+        *F = (uint32_t)(f * 0x1p32f);
+        return;
+    }
+    if (!(t <= 1.0f))
+        t = 1.0f;
+    float c = ldexpf(1.0f, 1 - s);
+    if (t >= c) {
+        uint32_t tb = float_bits(t);
+        int e = (int)((tb >> 23) & 0xFFu) - 127;
+        uint32_t mant = tb & 0x7FFFFFu;
+        int32_t lo = (int32_t)1 << (e + s - 1);
+        *m_lo = lo;
+        *m_hi = 2 * lo;
+        *F = mant << 9;
+    } else {
+        float f = t * ldexpf(1.0f, s - 1);
+        *m_lo = 0;
+        *m_hi = 1;
+        *F = (uint32_t)(f * 0x1p32f);
+    }
+}
+
+/* One signed code: pick the upper magnitude iff u < F, then apply the sign
+ * bit of x.                                                               */
+int32_t oracle_code(float xv, float pre, float sigma, int zero_norm, int s, int scheme, uint32_t u)
+{
+    int32_t m_lo, m_hi;
+    uint32_t F;
+    oracle_bracket(xv, pre, sigma, zero_norm, s, scheme, &m_lo, &m_hi, &F);
+    int32_t m = (u < F) ? m_hi : m_lo;
+    return (float_bits(xv) >> 31) ? -m : m;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Quantize all n rows given the norm.  Row i is worker worker_base + i.    */
+void oracle_quantize(const void *x, int dtype, int64_t n, int64_t d, float N,
+                     int s, int scheme, uint64_t seed, int64_t worker_base, int32_t *codes)
+{
+    float pre, sigma;
+    double kappa;
+    oracle_scale_params(N, n, s, scheme, &pre, &sigma, &kappa);
+    int zero = (N == 0.0f);
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j < d; ++j) {
+            uint64_t g = (uint64_t)(i * d + j);
+            uint32_t u = oracle_uniform32(seed, (uint64_t)(worker_base + i), (uint64_t)j);
+            codes[g] = oracle_code(load_x(x, dtype, g), pre, sigma, zero, s, scheme, u);
+        }
+}
+
+/* Smallest two's-complement width that holds every sum of n codes:
+ * |sum| <= n*M needs ceil(log2(n*M + 1)) + 1 bits.                         */
+int oracle_min_code_bits(int64_t n, int s, int scheme)
+{
+    int64_t nm = n * oracle_top_code(s, scheme);
+    int bits = 0;
+    while (((int64_t)1 << bits) < nm + 1)
+        ++bits;
+    return bits + 1;
+}
+
+/* Bytes of one packed row: d fields of W bits, padded to 16 bytes.         */
+int64_t oracle_row_bytes(int64_t d, int W)
+{
+    int64_t bits = d * (int64_t)W;
+    return ((bits + 127) / 128) * 16;
+}
+
+/* Little-endian bitstream: bit k of a row is bit k % 8 of byte k / 8;
+ * element j occupies bits [j W, j W + W) in two's complement.             */
+void oracle_pack(const int32_t *codes, int64_t n, int64_t d, int W, uint8_t *out)
+{
+    int64_t rb = oracle_row_bytes(d, W);
+    memset(out, 0, (size_t)(n * rb));
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j < d; ++j) {
+            uint32_t field = (uint32_t)codes[i * d + j];
+            for (int b = 0; b < W; ++b)
+                if ((field >> b) & 1u) {
+                    int64_t k = j * W + b;
+                    out[i * rb + k / 8] |= (uint8_t)(1u << (k % 8));
+                }
+        }
+}
+
+void oracle_unpack(const uint8_t *in, int64_t n, int64_t d, int W, int32_t *codes)
+{
+    int64_t rb = oracle_row_bytes(d, W);
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j < d; ++j) {
+            int64_t v = 0;
+            for (int b = 0; b < W; ++b) {
+                int64_t k = j * W + b;
+                if ((in[i * rb + k / 8] >> (k % 8)) & 1u)
+                    v |= (int64_t)1 << b;
+            }
+            if (v >> (W - 1)) /* sign bit set */
+                v -= (int64_t)1 << W;
+            codes[i * d + j] = (int32_t)v;
+        }
+}
+
+/* Exact integer sum over workers, per coordinate.                          */
+void oracle_sum_codes(const int32_t *codes, int64_t n, int64_t d, int64_t *sums)
+{
+    for (int64_t j = 0; j < d; ++j) {
+        int64_t acc = 0;
+        for (int64_t i = 0; i < n; ++i)
+            acc += codes[i * d + j];
+        sums[j] = acc;
+    }
+}
+
+/* Dequantize once to the mean: mean_j = fp32(sum_j * kappa) (fp64 product). */
+void oracle_dequantize(const int64_t *sums, int64_t n, int64_t d, float N, int s, int scheme,
+                       float *mean)
+{
+    float pre, sigma;
+    double kappa;
+    oracle_scale_params(N, n, s, scheme, &pre, &sigma, &kappa);
+    for (int64_t j = 0; j < d; ++j)
+        mean[j] = (float)((double)sums[j] * kappa);
+}
+
+/* Selected columns of the whole pipeline, given the norm: for each listed
+ * coordinate j, the exact code sum over the n workers and the mean.        */
+void oracle_compress_mean_cols(const void *x, int dtype, int64_t n, int64_t d, float N,
+                               int s, int scheme, uint64_t seed,
+                               const int64_t *cols, int64_t ncols, int64_t *sums, float *mean)
+{
+    float pre, sigma;
+    double kappa;
+    oracle_scale_params(N, n, s, scheme, &pre, &sigma, &kappa);
+    int zero = (N == 0.0f);
+    for (int64_t c = 0; c < ncols; ++c) {
+        int64_t j = cols[c];
+        int64_t acc = 0;
+        for (int64_t i = 0; i < n; ++i) {
+            uint64_t g = (uint64_t)(i * d + j);
+            uint32_t u = oracle_uniform32(seed, (uint64_t)i, (uint64_t)j);
+            acc += oracle_code(load_x(x, dtype, g), pre, sigma, zero, s, scheme, u);
+        }
+        sums[c] = acc;
+        mean[c] = (float)((double)acc * kappa);
+    }
+}
+
+/* Whole pipeline: norm, codes, exact sum, one dequantization.              */
+float oracle_compress_mean(const void *x, int dtype, int64_t n, int64_t d, int s,
+                           float q, float p, int scheme, uint64_t seed,
+                           int64_t *sums, float *mean)
+{
+    double *pw = (double *)malloc((size_t)n * sizeof(double));
+    int64_t *cols = (int64_t *)malloc((size_t)d * sizeof(int64_t));
+    if (!pw || !cols) {
+        free(pw);
+        free(cols);
+        return NAN;
+    }
+    float N = oracle_global_norm(x, dtype, n, d, q, p, pw);
+    for (int64_t j = 0; j < d; ++j)
+        cols[j] = j;
+    oracle_compress_mean_cols(x, dtype, n, d, N, s, scheme, seed, cols, d, sums, mean);
+    free(pw);
+    free(cols);
+    return N;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Ablation: QSGD with LOCAL norms (the baseline Global-QSGD replaces).
+ * Worker i scales by its own N_i = fp32(sqrt(sum_j x_ij^2)) and rounds to
+ * the L_s levels with the same uniforms as above; codes are in [-s, s].
+ * The mean is not an integer sum any more: mean_j = fp32(sum_i code_ij *
+ * kappa_i) with kappa_i = fp64(N_i / (n s)), accumulated in fp64 in worker
+ * order 0..n-1.                                                           */
+void oracle_qsgd_local_mean(const void *x, int dtype, int64_t n, int64_t d, int s, uint64_t seed,
+                            float *norms, int32_t *codes_or_null, float *mean)
+{
+    float *pre = (float *)malloc((size_t)n * sizeof(float));
+    float *sig = (float *)malloc((size_t)n * sizeof(float));
+    double *kap = (double *)malloc((size_t)n * sizeof(double));
+    if (!pre || !sig || !kap) {
+        free(pre); free(sig); free(kap);
+        return;
+    }
+    for (int64_t i = 0; i < n; ++i) {
+        nsum acc = {0.0, 0.0};
+        for (int64_t j = 0; j < d; ++j) {
+            double v = (double)load_x(x, dtype, (uint64_t)(i * d + j));
+            nsum_add(&acc, v * v);
+        }
+        norms[i] = (float)sqrt(acc.s + acc.c);
+        oracle_scale_params(norms[i], 1, s, ORACLE_SCHEME_L, &pre[i], &sig[i], &kap[i]);
+        kap[i] = (double)norms[i] / ((double)n * (double)s);
+    }
+    for (int64_t j = 0; j < d; ++j) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            uint64_t g = (uint64_t)(i * d + j);
+            uint32_t u = oracle_uniform32(seed, (uint64_t)i, (uint64_t)j);
+            int32_t c = oracle_code(load_x(x, dtype, g), pre[i], sig[i], norms[i] == 0.0f, s,
+                                    ORACLE_SCHEME_L, u);
+            if (codes_or_null)
+                codes_or_null[g] = c;
+            acc = acc + (double)c * kap[i];
+        }
+        mean[j] = (float)acc;
+    }
+    free(pre); free(sig); free(kap);
+}
