@@ -1,0 +1,238 @@
+"""Python binding of libgq.so -- Global-QSGD compression on AMD MI355X.
+
+Argument marshalling only: every step of the operator runs in the HIP
+kernels of ``csrc/gq.hip`` behind the C ABI of ``include/gq.h``.  PyTorch
+supplies device memory and the stream.  There is no fallback: without the
+built library, or without a GPU, the compute entry points raise.
+
+The functions keep the C names.  Each takes CUDA (HIP) tensors, allocates
+the outputs it is not given, launches on ``stream`` (default: torch's
+current stream) and returns without synchronizing.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgq.so")
+
+GQ_SCHEME_L = 0
+GQ_SCHEME_E = 1
+GQ_IN_F32 = 0
+GQ_IN_BF16 = 1
+
+STATUS = {0: "GQ_OK", 1: "GQ_ERR_NULL", 2: "GQ_ERR_ARG", 3: "GQ_ERR_UNSUPPORTED",
+          4: "GQ_ERR_CODE_WIDTH", 5: "GQ_ERR_WORKSPACE", 6: "GQ_ERR_ALIGN", 7: "GQ_ERR_DEVICE"}
+
+# exported symbols with their C signatures
+_i32, _i64, _u64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float, ctypes.c_void_p
+SIGNATURES = {
+    "gq_min_code_bits": (_i32, [_i64, _i32, _i32]),
+    "gq_code_row_bytes": (_i64, [_i64, _i32]),
+    "gq_workspace_bytes": (_i64, [_i64, _i64]),
+    "gq_global_norm": (_i32, [_vp, _i32, _i64, _i64, _f32, _f32, _vp, _vp, _i64, _vp]),
+    "gq_quantize": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _vp, _u64, _i64, _i32, _vp, _vp]),
+    "gq_reduce_codes": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp]),
+    "gq_dequantize": (_i32, [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "gq_compress_mean_from_norm": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _u64, _vp, _i32,
+                                          _vp, _vp, _vp]),
+    "gq_compress_mean": (_i32, [_vp, _i32, _i64, _i64, _i32, _f32, _f32, _i32, _u64, _i32, _vp,
+                                _vp, _vp, _vp, _i64, _vp]),
+    "gq_qsgd_local_mean": (_i32, [_vp, _i32, _i64, _i64, _i32, _u64, _vp, _vp, _vp, _i32, _vp,
+                                  _i64, _vp]),
+    "gq_status_str": (ctypes.c_char_p, [_i32]),
+    "gq_last_error": (ctypes.c_char_p, []),
+}
+
+
+class GQError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise GQError(status, lib().gq_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _input(x: torch.Tensor):
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [n, d] tensor")
+    if x.dtype == torch.float32:
+        return GQ_IN_F32
+    if x.dtype == torch.bfloat16:
+        return GQ_IN_BF16
+    raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+
+
+def _scheme(scheme) -> int:
+    if scheme in ("L", GQ_SCHEME_L):
+        return GQ_SCHEME_L
+    if scheme in ("E", GQ_SCHEME_E):
+        return GQ_SCHEME_E
+    raise ValueError(f"unknown scheme {scheme!r}")
+
+
+def _order(v) -> float:
+    return math.inf if (isinstance(v, str) and v == "inf") else float(v)
+
+
+# ---------------------------------------------------------------------------
+# sizes
+
+def gq_min_code_bits(n: int, s: int, scheme) -> int:
+    return int(lib().gq_min_code_bits(n, s, _scheme(scheme)))
+
+
+def gq_code_row_bytes(d: int, code_bits: int) -> int:
+    return int(lib().gq_code_row_bytes(d, code_bits))
+
+
+def gq_workspace_bytes(n: int, d: int) -> int:
+    return int(lib().gq_workspace_bytes(n, d))
+
+
+def _workspace(ws, n, d, device):
+    need = gq_workspace_bytes(n, d)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    return ws
+
+
+# ---------------------------------------------------------------------------
+# the path
+
+def gq_global_norm(x: torch.Tensor, q=2.0, p=2.0, *, norm=None, workspace=None, stream=None):
+    """Global (q,p)-norm of the rows of x; returns a 1-element float32 device tensor."""
+    dt = _input(x)
+    n, d = x.shape
+    norm = torch.empty(1, dtype=torch.float32, device=x.device) if norm is None else norm
+    ws = _workspace(workspace, n, d, x.device)
+    _check(lib().gq_global_norm(_ptr(x), dt, n, d, _order(q), _order(p), _ptr(norm), _ptr(ws),
+                                ws.numel(), _stream(stream)))
+    return norm
+
+
+def gq_quantize(x: torch.Tensor, s: int, scheme, norm: torch.Tensor, seed: int, code_bits: int, *,
+                worker_base: int = 0, codes=None, stream=None):
+    """Packed W-bit codes, uint8 [n, gq_code_row_bytes(d, W)]."""
+    dt = _input(x)
+    n, d = x.shape
+    rb = gq_code_row_bytes(d, code_bits)
+    if codes is None:
+        codes = torch.empty((n, max(rb, 0)), dtype=torch.uint8, device=x.device)
+    _check(lib().gq_quantize(_ptr(x), dt, n, d, s, _scheme(scheme), _ptr(norm), seed, worker_base,
+                             code_bits, _ptr(codes), _stream(stream)))
+    return codes
+
+
+def gq_reduce_codes(codes: torch.Tensor, n: int, d: int, code_bits: int, *, code_sum=None,
+                    stream=None):
+    """Exact sum over the n packed rows; one packed row, uint8 [row_bytes]."""
+    rb = gq_code_row_bytes(d, code_bits)
+    if code_sum is None:
+        code_sum = torch.empty(max(rb, 0), dtype=torch.uint8, device=codes.device)
+    _check(lib().gq_reduce_codes(_ptr(codes), n, d, code_bits, _ptr(code_sum), _stream(stream)))
+    return code_sum
+
+
+def gq_dequantize(code_sum: torch.Tensor, n: int, d: int, s: int, scheme, code_bits: int,
+                  norm: torch.Tensor, *, mean=None, stream=None):
+    """Mean over the n workers from the packed code sums, float32 [d]."""
+    if mean is None:
+        mean = torch.empty(d, dtype=torch.float32, device=code_sum.device)
+    _check(lib().gq_dequantize(_ptr(code_sum), n, d, s, _scheme(scheme), code_bits, _ptr(norm),
+                               _ptr(mean), _stream(stream)))
+    return mean
+
+
+def gq_compress_mean_from_norm(x: torch.Tensor, s: int, scheme, seed: int, norm: torch.Tensor, *,
+                               code_bits: int = 0, want_code_sum: bool = False, mean=None,
+                               code_sum=None, stream=None):
+    """Fused quantize + integer sum + dequantize given the norm: (mean, code_sum or None)."""
+    dt = _input(x)
+    n, d = x.shape
+    if mean is None:
+        mean = torch.empty(d, dtype=torch.float32, device=x.device)
+    if want_code_sum and code_sum is None:
+        code_sum = torch.empty(max(gq_code_row_bytes(d, code_bits), 0), dtype=torch.uint8,
+                               device=x.device)
+    _check(lib().gq_compress_mean_from_norm(_ptr(x), dt, n, d, s, _scheme(scheme), seed,
+                                            _ptr(norm), code_bits, _ptr(mean), _ptr(code_sum),
+                                            _stream(stream)))
+    return mean, code_sum
+
+
+def gq_compress_mean(x: torch.Tensor, s: int, q, p, scheme, seed: int, *, code_bits: int = 0,
+                     want_code_sum: bool = False, mean=None, norm=None, code_sum=None,
+                     workspace=None, stream=None):
+    """The whole path: (mean float32 [d], norm float32 [1], code_sum or None)."""
+    dt = _input(x)
+    n, d = x.shape
+    if mean is None:
+        mean = torch.empty(d, dtype=torch.float32, device=x.device)
+    if norm is None:
+        norm = torch.empty(1, dtype=torch.float32, device=x.device)
+    if want_code_sum and code_sum is None:
+        code_sum = torch.empty(max(gq_code_row_bytes(d, code_bits), 0), dtype=torch.uint8,
+                               device=x.device)
+    ws = _workspace(workspace, n, d, x.device)
+    _check(lib().gq_compress_mean(_ptr(x), dt, n, d, s, _order(q), _order(p), _scheme(scheme), seed,
+                                  code_bits, _ptr(mean), _ptr(norm), _ptr(code_sum), _ptr(ws),
+                                  ws.numel(), _stream(stream)))
+    return mean, norm, code_sum
+
+
+def gq_qsgd_local_mean(x: torch.Tensor, s: int, seed: int, *, code_bits: int = 0,
+                       want_codes: bool = False, mean=None, norms=None, codes=None,
+                       workspace=None, stream=None):
+    """Local-norm QSGD ablation: (mean float32 [d], norms float32 [n], codes or None)."""
+    dt = _input(x)
+    n, d = x.shape
+    if mean is None:
+        mean = torch.empty(d, dtype=torch.float32, device=x.device)
+    if norms is None:
+        norms = torch.empty(n, dtype=torch.float32, device=x.device)
+    if want_codes and codes is None:
+        codes = torch.empty((n, max(gq_code_row_bytes(d, code_bits), 0)), dtype=torch.uint8,
+                            device=x.device)
+    ws = _workspace(workspace, n, d, x.device)
+    _check(lib().gq_qsgd_local_mean(_ptr(x), dt, n, d, s, seed, _ptr(mean), _ptr(norms),
+                                    _ptr(codes), code_bits, _ptr(ws), ws.numel(),
+                                    _stream(stream)))
+    return mean, norms, codes

@@ -1,0 +1,1122 @@
+// gq.hip -- Global-QSGD compression on AMD Instinct MI355X (gfx950, CDNA4).
+//
+// Kernels and C ABI of libgq.so (declarations and the full contract are in
+// include/gq.h).  The operator is Global-Q of "Global-QSGD: Practical
+// Floatless Quantization for Distributed Learning with Theoretical
+// Guarantees": one global (q,p)-norm over all workers (Sec. 2 notation),
+// unbiased random rounding of |x|/N to the standard-dithering levels
+// (s-i)/s or the exponential-dithering levels 2^-k (Sec. 3), integer codes
+// whose sum over workers is exact, one dequantization (Sec. 6).
+//
+// Design (all bandwidth-bound work; nothing here is a dense contraction, so
+// no MFMA):
+//   k_norm_partial   pass 1: streams x once, fp64 sum of squares (or max|x|)
+//                    per (worker, chunk) into a fixed slot -- no atomics, so
+//                    the result bits depend only on (n, d).
+//   k_norm_finalize  one block: fixed-order tree over the partials, then the
+//                    (q,p) combination, sqrt in fp64, one fp32 rounding.
+//   k_compress_mean  pass 2: each thread owns 8 consecutive coordinates (one
+//                    Philox block) and walks the n workers, so the integer sum
+//                    stays in registers; 128-bit loads, one Philox4x32-10 call
+//                    per 8 coordinates (16 random bits each, a second call only
+//                    when the first 16 bits tie the threshold, p ~ 2^-16), and
+//                    the mean is written once.  Tiles are visited in reverse
+//                    of pass 1's order so the data pass 1 touched last is
+//                    re-read first, while it may still sit in the 256 MB
+//                    Infinity Cache.
+//   k_quantize / k_reduce_codes / k_dequantize: the same steps unfused, with
+//                    W-bit codes packed through LDS into coalesced words.
+//   k_local_mean     ablation: per-worker norms (QSGD), fp64 mean.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "gq.h"
+
+namespace {
+
+constexpr int kThreads = 256;               // 4 wave64 per block
+constexpr int kPer = 8;                     // coordinates per thread: one Philox output block
+constexpr int kTile = kThreads * kPer;      // 2048 coordinates per block
+constexpr int64_t kNormTargetBlocks = 8192; // pass-1 blocks: ~32 per CU on 256 CUs
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+
+thread_local char g_err[512];
+
+int32_t fail(int32_t status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+inline int32_t ok()
+{
+    g_err[0] = 0;
+    return GQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side sizes
+
+inline bool order_ok(float v) { return v == 2.0f || (isinf(v) && v > 0.0f); }
+
+inline int64_t top_code(int32_t s, int32_t scheme)
+{
+    return scheme == GQ_SCHEME_L ? (int64_t)s : ((int64_t)1 << (s - 1));
+}
+
+inline bool s_ok(int32_t s, int32_t scheme)
+{
+    if (scheme == GQ_SCHEME_L)
+        return s >= 1 && s <= (1 << 24);
+    if (scheme == GQ_SCHEME_E)
+        return s >= 1 && s <= 31;
+    return false;
+}
+
+int32_t min_bits(int64_t n, int32_t s, int32_t scheme)
+{
+    if (n < 1 || n > ((int64_t)1 << 40) || !s_ok(s, scheme))
+        return -1;
+    const int64_t nm = n * top_code(s, scheme); // < 2^71 is impossible here: n < 2^40, M <= 2^30
+    int bits = 0;
+    while (bits < 62 && ((int64_t)1 << bits) < nm + 1)
+        ++bits;
+    return bits + 1;
+}
+
+__host__ __device__ inline int64_t row_bytes(int64_t d, int32_t W) { return ((d * W + 127) / 128) * 16; }
+
+inline int64_t align256(int64_t b) { return (b + 255) & ~(int64_t)255; }
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Pass-1 geometry: each row is cut into `chunks` ranges of `chunk_len`
+// coordinates (a multiple of the 2048-coordinate tile); one block per
+// (chunk, worker).  Depends on (n, d) only, so the partial-sum tree -- and
+// the norm's bits -- are the same on every call.
+struct NormGeom {
+    int64_t chunks, chunk_len, blocks;
+};
+
+NormGeom norm_geom(int64_t n, int64_t d)
+{
+    NormGeom g{0, kTile, 0};
+    const int64_t tiles = (d + kTile - 1) / kTile;
+    if (tiles == 0)
+        return g;
+    int64_t want = (kNormTargetBlocks + n - 1) / n;
+    if (want < 1)
+        want = 1;
+    if (want > tiles)
+        want = tiles;
+    const int64_t tiles_per_chunk = (tiles + want - 1) / want;
+    g.chunk_len = tiles_per_chunk * kTile;
+    g.chunks = (d + g.chunk_len - 1) / g.chunk_len;
+    g.blocks = g.chunks * n;
+    return g;
+}
+
+// Workspace: [partials n*chunks f64][per-worker n f64][per-worker params n*16 B]
+struct WsLayout {
+    int64_t partials, per_worker, params, total;
+};
+
+WsLayout ws_layout(int64_t n, int64_t d)
+{
+    const NormGeom g = norm_geom(n, d);
+    WsLayout w;
+    w.partials = 0;
+    w.per_worker = align256(8 * n * g.chunks);
+    w.params = w.per_worker + align256(8 * n);
+    w.total = w.params + align256(16 * n);
+    return w;
+}
+
+// ---------------------------------------------------------------------------
+// Device helpers
+
+struct WorkerParams { // per-worker scalars of the local-norm ablation
+    float pre, sigma;
+    double kappa;
+};
+
+struct QParams {
+    float pre;   // 2^64 when N < 2^-64, else 1 (exact pre-scale of |x|)
+    float sigma; // fp32(s / (N pre)) for L, fp32(1 / (N pre)) for E
+    float top;   // clamp of t: s (L) or 1 (E)
+    float cE;    // 2^(1-s): the smallest non-zero E level
+    float p2E;   // 2^(s+31): maps t < 2^(1-s) to the threshold scale
+    double kappa;
+    int s;
+    bool zero;
+    bool prescale;
+};
+
+__device__ __forceinline__ QParams make_qparams(float N, int64_t n, int s, int scheme)
+{
+    QParams q;
+    q.zero = (N == 0.0f);
+    q.prescale = (N < 0x1p-64f);
+    q.pre = q.prescale ? 0x1p64f : 1.0f;
+    const float Np = N * q.pre;
+    q.sigma = (float)((scheme == GQ_SCHEME_L ? (double)s : 1.0) / (double)Np);
+    q.top = (scheme == GQ_SCHEME_L) ? (float)s : 1.0f;
+    q.cE = __uint_as_float((uint32_t)(128 - s) << 23);
+    q.p2E = __uint_as_float((uint32_t)(158 + s) << 23);
+    const double M = (scheme == GQ_SCHEME_L) ? (double)s : (double)((int64_t)1 << (s - 1));
+    q.kappa = (double)N / ((double)n * M);
+    q.s = s;
+    return q;
+}
+
+// Philox4x32-10 (SC'11): per round, two 32x32->64 products of counter words
+// 0 and 2 by the Philox multipliers; high halves are xor-ed with counter
+// words 1 / 3 and the round key, low halves move over; the key advances by
+// the Weyl constants.  The key (the seed) is wave-uniform and lives in SGPRs.
+__device__ __forceinline__ uint4 philox10(uint4 c, uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)c.x * 0xD2511F53u;
+        const uint64_t p1 = (uint64_t)c.z * 0xCD9E8D57u;
+        c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1,
+                       (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+__device__ __forceinline__ uint32_t half16(const uint4 &w, int k)
+{
+    const uint32_t word = (k >> 1) == 0 ? w.x : (k >> 1) == 1 ? w.y : (k >> 1) == 2 ? w.z : w.w;
+    return (k & 1) ? (word >> 16) : (word & 0xFFFFu);
+}
+
+// Deterministic half of the rounding for one coordinate: candidate
+// magnitudes (mlo, mhi) and the 32-bit threshold F (upper iff u < F).
+template <int SCH, bool PRE>
+__device__ __forceinline__ void bracket(float v, const QParams &q, int &mlo, int &mhi, uint32_t &F)
+{
+    float a = fabsf(v);
+    if (PRE)
+        a = a * q.pre;
+    float t = a * q.sigma;
+    if (SCH == GQ_SCHEME_L) {
+        t = (t <= q.top) ? t : q.top; // a NaN lands on the top level
+        const float lo = floorf(t);
+        F = (uint32_t)((t - lo) * 0x1p32f);
+        mlo = (int)lo;
+        mhi = mlo + 1;
+    } else {
+        t = (t <= 1.0f) ? t : 1.0f;
+        const uint32_t tb = __float_as_uint(t);
+        if (t >= q.cE) {
+            // t = 2^e (1 + phi): lower level 2^e -> code 2^(e+s-1), threshold phi 2^32
+            mlo = 1 << ((int)(tb >> 23) - 128 + q.s);
+            mhi = (int)((uint32_t)mlo << 1); // unused when F == 0 (t = 1, s = 31)
+            F = tb << 9;
+        } else {
+            mlo = 0;
+            mhi = 1;
+            F = (uint32_t)(t * q.p2E);
+        }
+    }
+}
+
+// Codes of one 8-coordinate group from draw 0 (high 16 bits of each
+// uniform).  Coordinates whose 16 bits equal the top half of F are marked in
+// `ties`; they took the lower level and are settled by draw 1.
+template <int SCH, bool PRE>
+__device__ __forceinline__ void quant_group(const float (&v)[kPer], const uint4 &A, const QParams &q,
+                                            int (&code)[kPer], uint32_t &ties)
+{
+    ties = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        int mlo, mhi;
+        uint32_t F;
+        bracket<SCH, PRE>(v[k], q, mlo, mhi, F);
+        const uint32_t h = half16(A, k);
+        const uint32_t Fh = F >> 16;
+        const int m = (h < Fh) ? mhi : mlo;
+        ties |= (uint32_t)((h == Fh) & ((F & 0xFFFFu) != 0u)) << k;
+        code[k] = (__float_as_uint(v[k]) >> 31) ? -m : m;
+    }
+}
+
+template <int SCH, bool PRE>
+__device__ __forceinline__ void settle_ties(const float (&v)[kPer], const uint4 &B, const QParams &q,
+                                            int (&code)[kPer], uint32_t ties)
+{
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        if ((ties >> k) & 1u) {
+            int mlo, mhi;
+            uint32_t F;
+            bracket<SCH, PRE>(v[k], q, mlo, mhi, F);
+            if (half16(B, k) < (F & 0xFFFFu))
+                code[k] = (__float_as_uint(v[k]) >> 31) ? -mhi : mhi;
+        }
+    }
+}
+
+// 8 consecutive inputs widened to fp32.  Fast path: the group lies inside
+// the row and the row starts 16-byte aligned (d % 8 == 0): 128-bit loads.
+template <int DT>
+__device__ __forceinline__ void load_group(const void *__restrict__ x, int64_t row_off, int64_t j0,
+                                           int64_t d, bool vec, float (&v)[kPer])
+{
+    if (DT == GQ_IN_F32) {
+        const float *p = (const float *)x + row_off + j0;
+        if (vec) {
+            const float4 a = *(const float4 *)p;
+            const float4 b = *(const float4 *)(p + 4);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+                v[k] = (j0 + k < d) ? p[k] : 0.0f;
+        }
+    } else {
+        const uint16_t *p = (const uint16_t *)x + row_off + j0;
+        if (vec) {
+            const uint4 r = *(const uint4 *)p;
+            v[0] = __uint_as_float(r.x << 16); v[1] = __uint_as_float(r.x & 0xFFFF0000u);
+            v[2] = __uint_as_float(r.y << 16); v[3] = __uint_as_float(r.y & 0xFFFF0000u);
+            v[4] = __uint_as_float(r.z << 16); v[5] = __uint_as_float(r.z & 0xFFFF0000u);
+            v[6] = __uint_as_float(r.w << 16); v[7] = __uint_as_float(r.w & 0xFFFF0000u);
+        } else {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+                v[k] = (j0 + k < d) ? __uint_as_float((uint32_t)p[k] << 16) : 0.0f;
+        }
+    }
+}
+
+// Store 8 W-bit fields per thread (thread-major: coordinate tile*2048 +
+// 8*t + k) into one packed row.  W = 8/16/32: direct vector stores.  Other
+// W: fields go through LDS and each thread assembles whole output words, so
+// global stores stay coalesced.  Every thread of the block must call this.
+// Bytes past the row's end are never written; pad fields are zero.
+__device__ void store_tile_packed(uint32_t *lds, const int (&val)[kPer], int W, uint8_t *row,
+                                  int64_t tile, int64_t rbytes)
+{
+    const int t = threadIdx.x;
+    const int64_t j0 = tile * kTile + (int64_t)t * kPer;
+    if (W == 8) {
+        const int64_t off = j0;
+        if (off < rbytes) {
+            uint2 o;
+            o.x = (val[0] & 0xFF) | (val[1] & 0xFF) << 8 | (val[2] & 0xFF) << 16 | (uint32_t)val[3] << 24;
+            o.y = (val[4] & 0xFF) | (val[5] & 0xFF) << 8 | (val[6] & 0xFF) << 16 | (uint32_t)val[7] << 24;
+            *(uint2 *)(row + off) = o;
+        }
+        return;
+    }
+    if (W == 16) {
+        const int64_t off = 2 * j0;
+        if (off < rbytes) {
+            uint4 o;
+            o.x = (val[0] & 0xFFFF) | (uint32_t)val[1] << 16;
+            o.y = (val[2] & 0xFFFF) | (uint32_t)val[3] << 16;
+            o.z = (val[4] & 0xFFFF) | (uint32_t)val[5] << 16;
+            o.w = (val[6] & 0xFFFF) | (uint32_t)val[7] << 16;
+            *(uint4 *)(row + off) = o;
+        }
+        return;
+    }
+    if (W == 32) {
+        const int64_t off = 4 * j0;
+        if (off < rbytes)
+            *(uint4 *)(row + off) = make_uint4(val[0], val[1], val[2], val[3]);
+        if (off + 16 < rbytes)
+            *(uint4 *)(row + off + 16) = make_uint4(val[4], val[5], val[6], val[7]);
+        return;
+    }
+    const uint32_t mask = (1u << W) - 1u;
+    uint4 *l4 = (uint4 *)lds;
+    l4[2 * t] = make_uint4(val[0] & mask, val[1] & mask, val[2] & mask, val[3] & mask);
+    l4[2 * t + 1] = make_uint4(val[4] & mask, val[5] & mask, val[6] & mask, val[7] & mask);
+    __syncthreads();
+    const int words = 64 * W; // 2048 W bits
+    const int64_t w0 = tile * words;
+    const int64_t rwords = rbytes / 4;
+    uint32_t *rw = (uint32_t *)row;
+    for (int w = t; w < words; w += kThreads) {
+        if (w0 + w >= rwords)
+            break;
+        const int bit0 = w * 32;
+        const int e_last = (bit0 + 31) / W;
+        uint32_t word = 0;
+        for (int e = bit0 / W; e <= e_last; ++e) {
+            const int sh = e * W - bit0; // in (-W, 32)
+            const uint32_t f = lds[e];
+            word |= (sh >= 0) ? (f << sh) : (f >> -sh);
+        }
+        rw[w0 + w] = word;
+    }
+    __syncthreads();
+}
+
+// Inverse of store_tile_packed: 8 sign-extended fields per thread.  Fields
+// past the row's end read as 0.  Every thread of the block must call this.
+__device__ void load_tile_fields(uint32_t *lds, const uint8_t *row, int W, int64_t tile,
+                                 int64_t rbytes, int (&val)[kPer])
+{
+    const int t = threadIdx.x;
+    const int64_t j0 = tile * kTile + (int64_t)t * kPer;
+    if (W == 8) {
+        uint2 r = make_uint2(0, 0);
+        if (j0 < rbytes)
+            r = *(const uint2 *)(row + j0);
+        val[0] = (int8_t)(r.x); val[1] = (int8_t)(r.x >> 8);
+        val[2] = (int8_t)(r.x >> 16); val[3] = (int8_t)(r.x >> 24);
+        val[4] = (int8_t)(r.y); val[5] = (int8_t)(r.y >> 8);
+        val[6] = (int8_t)(r.y >> 16); val[7] = (int8_t)(r.y >> 24);
+        return;
+    }
+    if (W == 16) {
+        uint4 r = make_uint4(0, 0, 0, 0);
+        if (2 * j0 < rbytes)
+            r = *(const uint4 *)(row + 2 * j0);
+        val[0] = (int16_t)(r.x); val[1] = (int16_t)(r.x >> 16);
+        val[2] = (int16_t)(r.y); val[3] = (int16_t)(r.y >> 16);
+        val[4] = (int16_t)(r.z); val[5] = (int16_t)(r.z >> 16);
+        val[6] = (int16_t)(r.w); val[7] = (int16_t)(r.w >> 16);
+        return;
+    }
+    if (W == 32) {
+        uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+        if (4 * j0 < rbytes)
+            a = *(const uint4 *)(row + 4 * j0);
+        if (4 * j0 + 16 < rbytes)
+            b = *(const uint4 *)(row + 4 * j0 + 16);
+        val[0] = (int)a.x; val[1] = (int)a.y; val[2] = (int)a.z; val[3] = (int)a.w;
+        val[4] = (int)b.x; val[5] = (int)b.y; val[6] = (int)b.z; val[7] = (int)b.w;
+        return;
+    }
+    const int words = 64 * W;
+    const int64_t w0 = tile * words;
+    const int64_t rwords = rbytes / 4;
+    const uint32_t *rw = (const uint32_t *)row;
+    for (int w = t; w < words; w += kThreads)
+        lds[w] = (w0 + w < rwords) ? rw[w0 + w] : 0u;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int bit = (t * kPer + k) * W;
+        const int wi = bit >> 5, sh = bit & 31;
+        const uint64_t two = (uint64_t)lds[wi] | ((uint64_t)(wi + 1 < words ? lds[wi + 1] : 0u) << 32);
+        const uint32_t f = (uint32_t)(two >> sh);
+        val[k] = (int)(f << (32 - W)) >> (32 - W);
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+// Block reduction with a fixed tree: butterflies inside each wave, then the
+// four wave results in order.  Result valid in thread 0.
+template <bool MAX>
+__device__ __forceinline__ double block_reduce(double v, double *lds)
+{
+    if (MAX)
+        v = (double)wave_max((float)v);
+    else
+        v = wave_sum(v);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0)
+        lds[wave] = v;
+    __syncthreads();
+    double r = 0.0;
+    if (threadIdx.x == 0) {
+        if (MAX)
+            r = fmax(fmax(lds[0], lds[1]), fmax(lds[2], lds[3]));
+        else
+            r = ((lds[0] + lds[1]) + lds[2]) + lds[3];
+    }
+    __syncthreads();
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: per-(chunk, worker) partial norms.  Block b reads chunk b / n of
+// row b % n, so the last blocks to run read the ends of all rows.
+
+template <int DT, bool QINF>
+__global__ __launch_bounds__(kThreads) void k_norm_partial(const void *__restrict__ x, int64_t n,
+                                                           int64_t d, int64_t chunks,
+                                                           int64_t chunk_len,
+                                                           double *__restrict__ partials)
+{
+    __shared__ double red[4];
+    const int64_t b = blockIdx.x;
+    const int64_t c = b / n, i = b % n;
+    const int64_t jb = c * chunk_len;
+    const int64_t je = (jb + chunk_len < d) ? jb + chunk_len : d;
+    const bool vec_row = (d & 7) == 0;
+    const int64_t row_off = i * d;
+    double s0 = 0.0, s1 = 0.0;
+    float mx = 0.0f;
+    int64_t j = jb + (int64_t)threadIdx.x * kPer;
+    if (vec_row) {
+        // four groups in flight per thread
+        for (; j + 3 * kTile < je; j += 4 * kTile) {
+            float v0[kPer], v1[kPer], v2[kPer], v3[kPer];
+            load_group<DT>(x, row_off, j, d, true, v0);
+            load_group<DT>(x, row_off, j + kTile, d, true, v1);
+            load_group<DT>(x, row_off, j + 2 * kTile, d, true, v2);
+            load_group<DT>(x, row_off, j + 3 * kTile, d, true, v3);
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                if (QINF) {
+                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v0[k]), fabsf(v1[k])),
+                                         fmaxf(fabsf(v2[k]), fabsf(v3[k]))));
+                } else {
+                    s0 += (double)v0[k] * (double)v0[k];
+                    s1 += (double)v1[k] * (double)v1[k];
+                    s0 += (double)v2[k] * (double)v2[k];
+                    s1 += (double)v3[k] * (double)v3[k];
+                }
+            }
+        }
+    }
+    for (; j < je; j += kTile) {
+        float v[kPer];
+        load_group<DT>(x, row_off, j, je, vec_row, v);
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            if (QINF)
+                mx = fmaxf(mx, fabsf(v[k]));
+            else
+                s0 += (double)v[k] * (double)v[k];
+        }
+    }
+    const double r = QINF ? block_reduce<true>((double)mx, red) : block_reduce<false>(s0 + s1, red);
+    if (threadIdx.x == 0)
+        partials[i * chunks + c] = r;
+}
+
+// Pass 1b: one block.  Per worker, a fixed-order reduction of its partials;
+// then the (q,p) combination.  LOCAL: per-worker norms and the per-worker
+// scalars of the local-norm ablation instead of one global norm.
+template <bool QINF, bool PINF, bool LOCAL>
+__global__ __launch_bounds__(kThreads) void k_norm_finalize(const double *__restrict__ partials,
+                                                            int64_t n, int64_t chunks,
+                                                            double *__restrict__ per_worker,
+                                                            float *__restrict__ norm_out, int s,
+                                                            WorkerParams *__restrict__ params)
+{
+    __shared__ double red[4];
+    for (int64_t i = 0; i < n; ++i) {
+        double acc = 0.0;
+        for (int64_t c = threadIdx.x; c < chunks; c += kThreads) {
+            const double v = partials[i * chunks + c];
+            acc = QINF ? fmax(acc, v) : acc + v;
+        }
+        const double r = block_reduce<QINF>(acc, red);
+        if (threadIdx.x == 0)
+            per_worker[i] = r;
+    }
+    __syncthreads();
+    if (threadIdx.x != 0)
+        return;
+    if (LOCAL) {
+        for (int64_t i = 0; i < n; ++i) {
+            const float Ni = (float)sqrt(per_worker[i]);
+            norm_out[i] = Ni;
+            const float pre = (Ni < 0x1p-64f) ? 0x1p64f : 1.0f;
+            WorkerParams w;
+            w.pre = pre;
+            w.sigma = (float)((double)s / (double)(Ni * pre));
+            w.kappa = (double)Ni / ((double)n * (double)s);
+            params[i] = w;
+        }
+        return;
+    }
+    double tot = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        const double w = per_worker[i];
+        if (PINF)
+            tot = fmax(tot, w);
+        else
+            tot += QINF ? w * w : w;
+    }
+    norm_out[0] = (QINF && PINF) ? (float)tot : (float)sqrt(tot);
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2, fused: quantize + exact integer sum over workers + dequantize.
+
+template <int DT, int SCH, bool PRE>
+__device__ __forceinline__ void accumulate_workers(const void *__restrict__ x, int64_t n, int64_t d,
+                                                   int64_t j0, bool vec, const QParams &q,
+                                                   uint32_t k0, uint32_t k1, int (&acc)[kPer])
+{
+    const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
+    for (int64_t i = 0; i < n; ++i) {
+        float v[kPer];
+        load_group<DT>(x, i * d, j0, d, vec, v);
+        const uint4 A = philox10(make_uint4(blo, bhi, (uint32_t)i, 0u), k0, k1);
+        int code[kPer];
+        uint32_t ties;
+        quant_group<SCH, PRE>(v, A, q, code, ties);
+        if (ties) {
+            const uint4 B = philox10(make_uint4(blo, bhi, (uint32_t)i, 1u), k0, k1);
+            settle_ties<SCH, PRE>(v, B, q, code, ties);
+        }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            acc[k] += code[k];
+    }
+}
+
+template <int DT, int SCH>
+__global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restrict__ x, int64_t n,
+                                                            int64_t d, int s, uint64_t seed,
+                                                            const float *__restrict__ norm_dev,
+                                                            float *__restrict__ mean,
+                                                            uint8_t *__restrict__ code_sum, int W)
+{
+    __shared__ uint32_t lds[kTile];
+    const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x; // reverse of pass 1
+    const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
+    const QParams q = make_qparams(*norm_dev, n, s, SCH);
+    int acc[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (!q.zero && j0 < d) {
+        const bool vec = (d & 7) == 0;
+        const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+        if (q.prescale)
+            accumulate_workers<DT, SCH, true>(x, n, d, j0, vec, q, k0, k1, acc);
+        else
+            accumulate_workers<DT, SCH, false>(x, n, d, j0, vec, q, k0, k1, acc);
+    }
+    if (j0 < d) {
+        float m[kPer];
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            m[k] = (float)((double)acc[k] * q.kappa);
+        if (((d & 7) == 0)) {
+            *(float4 *)(mean + j0) = make_float4(m[0], m[1], m[2], m[3]);
+            *(float4 *)(mean + j0 + 4) = make_float4(m[4], m[5], m[6], m[7]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+                if (j0 + k < d)
+                    mean[j0 + k] = m[k];
+        }
+    }
+    if (code_sum)
+        store_tile_packed(lds, acc, W, code_sum, tile, row_bytes(d, W));
+}
+
+// Unfused quantize: block b encodes tile b % tiles of row b / tiles.
+template <int DT, int SCH>
+__global__ __launch_bounds__(kThreads) void k_quantize(const void *__restrict__ x, int64_t n,
+                                                       int64_t d, int s, uint64_t seed,
+                                                       int64_t worker_base,
+                                                       const float *__restrict__ norm_dev,
+                                                       uint8_t *__restrict__ codes, int W,
+                                                       int64_t rbytes, int64_t tiles)
+{
+    __shared__ uint32_t lds[kTile];
+    const int64_t i = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
+    const QParams q = make_qparams(*norm_dev, n, s, SCH);
+    int code[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (!q.zero && j0 < d) {
+        float v[kPer];
+        load_group<DT>(x, i * d, j0, d, (d & 7) == 0, v);
+        const uint64_t wk = (uint64_t)(worker_base + i);
+        const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
+        const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+        const uint4 A = philox10(make_uint4(blo, bhi, (uint32_t)wk, 0u), k0, k1);
+        uint32_t ties;
+        if (q.prescale)
+            quant_group<SCH, true>(v, A, q, code, ties);
+        else
+            quant_group<SCH, false>(v, A, q, code, ties);
+        if (ties) {
+            const uint4 B = philox10(make_uint4(blo, bhi, (uint32_t)wk, 1u), k0, k1);
+            if (q.prescale)
+                settle_ties<SCH, true>(v, B, q, code, ties);
+            else
+                settle_ties<SCH, false>(v, B, q, code, ties);
+        }
+    }
+    store_tile_packed(lds, code, W, codes + i * rbytes, tile, rbytes);
+}
+
+// Unfused integer sum over the n packed rows of one tile.
+__global__ __launch_bounds__(kThreads) void k_reduce_codes(const uint8_t *__restrict__ codes,
+                                                           int64_t n, int W, int64_t rbytes,
+                                                           uint8_t *__restrict__ out)
+{
+    __shared__ uint32_t lds[kTile];
+    const int64_t tile = blockIdx.x;
+    int acc[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int64_t i = 0; i < n; ++i) {
+        int v[kPer];
+        load_tile_fields(lds, codes + i * rbytes, W, tile, rbytes, v);
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            acc[k] += v[k]; // exact when W holds n M; otherwise wraps below
+    }
+    if (W < 32) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            acc[k] = (int)((uint32_t)acc[k] << (32 - W)) >> (32 - W);
+    }
+    store_tile_packed(lds, acc, W, out, tile, rbytes);
+}
+
+// Unfused dequantization of one packed row of code sums.
+template <int SCH>
+__global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t *__restrict__ code_sum,
+                                                         int64_t n, int64_t d, int s, int W,
+                                                         const float *__restrict__ norm_dev,
+                                                         float *__restrict__ mean)
+{
+    __shared__ uint32_t lds[kTile];
+    const int64_t tile = blockIdx.x;
+    const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
+    int v[kPer];
+    load_tile_fields(lds, code_sum, W, tile, row_bytes(d, W), v);
+    const QParams q = make_qparams(*norm_dev, n, s, SCH);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        if (j0 + k < d)
+            mean[j0 + k] = (float)((double)v[k] * q.kappa);
+}
+
+// Ablation: local-norm QSGD.  Worker i uses its own scalars; the mean is an
+// fp64 sum in worker order.  Optional per-worker packed codes.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_local_mean(const void *__restrict__ x, int64_t n,
+                                                         int64_t d, int s, uint64_t seed,
+                                                         const float *__restrict__ norms,
+                                                         const WorkerParams *__restrict__ params,
+                                                         float *__restrict__ mean,
+                                                         uint8_t *__restrict__ codes, int W,
+                                                         int64_t rbytes)
+{
+    __shared__ uint32_t lds[kTile];
+    const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;
+    const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
+    const bool vec = (d & 7) == 0;
+    const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    double acc[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int64_t i = 0; i < n; ++i) {
+        int code[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+        const WorkerParams wp = params[i];
+        if (j0 < d && norms[i] != 0.0f) {
+            QParams q = {};
+            q.pre = wp.pre;
+            q.sigma = wp.sigma;
+            q.top = (float)s;
+            q.s = s;
+            float v[kPer];
+            load_group<DT>(x, i * d, j0, d, vec, v);
+            const uint4 A = philox10(make_uint4(blo, bhi, (uint32_t)i, 0u), k0, k1);
+            uint32_t ties;
+            const bool pre = wp.pre != 1.0f;
+            if (pre)
+                quant_group<GQ_SCHEME_L, true>(v, A, q, code, ties);
+            else
+                quant_group<GQ_SCHEME_L, false>(v, A, q, code, ties);
+            if (ties) {
+                const uint4 B = philox10(make_uint4(blo, bhi, (uint32_t)i, 1u), k0, k1);
+                if (pre)
+                    settle_ties<GQ_SCHEME_L, true>(v, B, q, code, ties);
+                else
+                    settle_ties<GQ_SCHEME_L, false>(v, B, q, code, ties);
+            }
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+                acc[k] = acc[k] + (double)code[k] * wp.kappa;
+        }
+        if (codes)
+            store_tile_packed(lds, code, W, codes + i * rbytes, tile, rbytes);
+    }
+    if (j0 < d) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            if (j0 + k < d)
+                mean[j0 + k] = (float)acc[k];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch helpers
+
+int32_t check_launch(const char *what)
+{
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(GQ_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int32_t validate_x(const void *x, int32_t dtype, int64_t n, int64_t d)
+{
+    if (dtype != GQ_IN_F32 && dtype != GQ_IN_BF16)
+        return fail(GQ_ERR_ARG, "dtype %d is not GQ_IN_F32 or GQ_IN_BF16", dtype);
+    if (n < 1 || n > 0x7FFFFFFF)
+        return fail(GQ_ERR_ARG, "n = %lld must be in [1, 2^31)", (long long)n);
+    if (d < 0)
+        return fail(GQ_ERR_ARG, "d = %lld is negative", (long long)d);
+    if (d > 0 && n > INT64_MAX / 8 / d)
+        return fail(GQ_ERR_ARG, "n * d overflows");
+    if (!x && d > 0)
+        return fail(GQ_ERR_NULL, "x is NULL");
+    if (!aligned16(x))
+        return fail(GQ_ERR_ALIGN, "x is not 16-byte aligned");
+    if ((d + kTile - 1) / kTile > kMaxGrid)
+        return fail(GQ_ERR_UNSUPPORTED, "d = %lld exceeds the launch limit", (long long)d);
+    return GQ_OK;
+}
+
+int32_t validate_scheme(int32_t s, int32_t scheme)
+{
+    if (scheme != GQ_SCHEME_L && scheme != GQ_SCHEME_E)
+        return fail(GQ_ERR_ARG, "scheme %d is not GQ_SCHEME_L or GQ_SCHEME_E", scheme);
+    if (!s_ok(s, scheme))
+        return fail(GQ_ERR_ARG, "s = %d out of range for the scheme", s);
+    return GQ_OK;
+}
+
+int32_t validate_width(int64_t n, int32_t s, int32_t scheme, int32_t W)
+{
+    const int32_t wmin = min_bits(n, s, scheme);
+    if (wmin < 0 || wmin > 32)
+        return fail(GQ_ERR_CODE_WIDTH, "sums of %lld codes need %d > 32 bits", (long long)n, wmin);
+    if (W < wmin || W > 32)
+        return fail(GQ_ERR_CODE_WIDTH, "code_bits %d outside [%d, 32]", W, wmin);
+    return GQ_OK;
+}
+
+int32_t validate_ws(const void *ws, int64_t ws_bytes, int64_t n, int64_t d)
+{
+    const WsLayout L = ws_layout(n, d);
+    if (!ws)
+        return fail(GQ_ERR_NULL, "workspace is NULL");
+    if (!aligned16(ws))
+        return fail(GQ_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (ws_bytes < L.total)
+        return fail(GQ_ERR_WORKSPACE, "workspace of %lld bytes < %lld needed", (long long)ws_bytes,
+                    (long long)L.total);
+    return GQ_OK;
+}
+
+#define GQ_TRY(expr)                  \
+    do {                              \
+        const int32_t st_ = (expr);   \
+        if (st_ != GQ_OK)             \
+            return st_;               \
+    } while (0)
+
+// Enqueue pass 1 (partials + finalize).  Arguments already validated.
+int32_t launch_norm(const void *x, int32_t dtype, int64_t n, int64_t d, bool qinf, bool pinf,
+                    bool local, float *norm_out, void *ws, int s, hipStream_t st)
+{
+    const NormGeom g = norm_geom(n, d);
+    const WsLayout L = ws_layout(n, d);
+    double *partials = (double *)((char *)ws + L.partials);
+    double *per_worker = (double *)((char *)ws + L.per_worker);
+    WorkerParams *params = (WorkerParams *)((char *)ws + L.params);
+    if (g.blocks > 0) {
+        if (g.blocks > kMaxGrid)
+            return fail(GQ_ERR_UNSUPPORTED, "norm grid too large");
+        const dim3 grid((unsigned)g.blocks), block(kThreads);
+        if (dtype == GQ_IN_F32) {
+            if (qinf)
+                k_norm_partial<GQ_IN_F32, true><<<grid, block, 0, st>>>(x, n, d, g.chunks, g.chunk_len, partials);
+            else
+                k_norm_partial<GQ_IN_F32, false><<<grid, block, 0, st>>>(x, n, d, g.chunks, g.chunk_len, partials);
+        } else {
+            if (qinf)
+                k_norm_partial<GQ_IN_BF16, true><<<grid, block, 0, st>>>(x, n, d, g.chunks, g.chunk_len, partials);
+            else
+                k_norm_partial<GQ_IN_BF16, false><<<grid, block, 0, st>>>(x, n, d, g.chunks, g.chunk_len, partials);
+        }
+        GQ_TRY(check_launch("k_norm_partial"));
+    }
+    const dim3 one(1), block(kThreads);
+    if (local)
+        k_norm_finalize<false, false, true><<<one, block, 0, st>>>(partials, n, g.chunks, per_worker, norm_out, s, params);
+    else if (qinf && pinf)
+        k_norm_finalize<true, true, false><<<one, block, 0, st>>>(partials, n, g.chunks, per_worker, norm_out, s, params);
+    else if (qinf)
+        k_norm_finalize<true, false, false><<<one, block, 0, st>>>(partials, n, g.chunks, per_worker, norm_out, s, params);
+    else if (pinf)
+        k_norm_finalize<false, true, false><<<one, block, 0, st>>>(partials, n, g.chunks, per_worker, norm_out, s, params);
+    else
+        k_norm_finalize<false, false, false><<<one, block, 0, st>>>(partials, n, g.chunks, per_worker, norm_out, s, params);
+    return check_launch("k_norm_finalize");
+}
+
+int32_t launch_compress(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                        int32_t scheme, uint64_t seed, const float *norm_dev, int32_t W,
+                        float *mean, void *code_sum, hipStream_t st)
+{
+    const int64_t tiles = (d + kTile - 1) / kTile;
+    if (tiles == 0)
+        return ok();
+    const dim3 grid((unsigned)tiles), block(kThreads);
+    uint8_t *cs = (uint8_t *)code_sum;
+    if (dtype == GQ_IN_F32) {
+        if (scheme == GQ_SCHEME_L)
+            k_compress_mean<GQ_IN_F32, GQ_SCHEME_L><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, mean, cs, W);
+        else
+            k_compress_mean<GQ_IN_F32, GQ_SCHEME_E><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, mean, cs, W);
+    } else {
+        if (scheme == GQ_SCHEME_L)
+            k_compress_mean<GQ_IN_BF16, GQ_SCHEME_L><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, mean, cs, W);
+        else
+            k_compress_mean<GQ_IN_BF16, GQ_SCHEME_E><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, mean, cs, W);
+    }
+    return check_launch("k_compress_mean");
+}
+
+} // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+
+extern "C" {
+
+int32_t gq_min_code_bits(int64_t n, int32_t s, int32_t scheme) { return min_bits(n, s, scheme); }
+
+int64_t gq_code_row_bytes(int64_t d, int32_t code_bits)
+{
+    if (d < 0 || code_bits < 1 || code_bits > 32 || d > INT64_MAX / 64)
+        return -1;
+    return row_bytes(d, code_bits);
+}
+
+int64_t gq_workspace_bytes(int64_t n, int64_t d)
+{
+    if (n < 1 || n > 0x7FFFFFFF || d < 0 || (d > 0 && n > INT64_MAX / 8 / d))
+        return -1;
+    return ws_layout(n, d).total;
+}
+
+const char *gq_status_str(int32_t status)
+{
+    switch (status) {
+    case GQ_OK: return "GQ_OK";
+    case GQ_ERR_NULL: return "GQ_ERR_NULL";
+    case GQ_ERR_ARG: return "GQ_ERR_ARG";
+    case GQ_ERR_UNSUPPORTED: return "GQ_ERR_UNSUPPORTED";
+    case GQ_ERR_CODE_WIDTH: return "GQ_ERR_CODE_WIDTH";
+    case GQ_ERR_WORKSPACE: return "GQ_ERR_WORKSPACE";
+    case GQ_ERR_ALIGN: return "GQ_ERR_ALIGN";
+    case GQ_ERR_DEVICE: return "GQ_ERR_DEVICE";
+    default: return "GQ_ERR_UNKNOWN";
+    }
+}
+
+const char *gq_last_error(void) { return g_err; }
+
+int32_t gq_global_norm(const void *x, int32_t dtype, int64_t n, int64_t d, float q, float p,
+                       float *norm_dev, void *workspace, int64_t workspace_bytes, void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    if (!norm_dev)
+        return fail(GQ_ERR_NULL, "norm_dev is NULL");
+    if (!order_ok(q) || !order_ok(p))
+        return fail(GQ_ERR_UNSUPPORTED, "q and p must be 2 or +inf");
+    GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
+    return launch_norm(x, dtype, n, d, isinf(q), isinf(p), false, norm_dev, workspace, 0,
+                       (hipStream_t)stream);
+}
+
+int32_t gq_quantize(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s, int32_t scheme,
+                    const float *norm_dev, uint64_t seed, int64_t worker_base, int32_t code_bits,
+                    void *codes, void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    GQ_TRY(validate_scheme(s, scheme));
+    if (!norm_dev || (!codes && d > 0))
+        return fail(GQ_ERR_NULL, "norm_dev or codes is NULL");
+    if (worker_base < 0 || worker_base + n > ((int64_t)1 << 32))
+        return fail(GQ_ERR_ARG, "worker indices must lie in [0, 2^32)");
+    GQ_TRY(validate_width(n, s, scheme, code_bits));
+    if (!aligned16(codes))
+        return fail(GQ_ERR_ALIGN, "codes is not 16-byte aligned");
+    const int64_t tiles = (d + kTile - 1) / kTile;
+    if (tiles == 0)
+        return ok();
+    if (tiles * n > kMaxGrid)
+        return fail(GQ_ERR_UNSUPPORTED, "n * tiles exceeds the launch limit");
+    const int64_t rb = row_bytes(d, code_bits);
+    const dim3 grid((unsigned)(tiles * n)), block(kThreads);
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t *c = (uint8_t *)codes;
+    if (dtype == GQ_IN_F32) {
+        if (scheme == GQ_SCHEME_L)
+            k_quantize<GQ_IN_F32, GQ_SCHEME_L><<<grid, block, 0, st>>>(x, n, d, s, seed, worker_base, norm_dev, c, code_bits, rb, tiles);
+        else
+            k_quantize<GQ_IN_F32, GQ_SCHEME_E><<<grid, block, 0, st>>>(x, n, d, s, seed, worker_base, norm_dev, c, code_bits, rb, tiles);
+    } else {
+        if (scheme == GQ_SCHEME_L)
+            k_quantize<GQ_IN_BF16, GQ_SCHEME_L><<<grid, block, 0, st>>>(x, n, d, s, seed, worker_base, norm_dev, c, code_bits, rb, tiles);
+        else
+            k_quantize<GQ_IN_BF16, GQ_SCHEME_E><<<grid, block, 0, st>>>(x, n, d, s, seed, worker_base, norm_dev, c, code_bits, rb, tiles);
+    }
+    return check_launch("k_quantize");
+}
+
+int32_t gq_reduce_codes(const void *codes, int64_t n, int64_t d, int32_t code_bits, void *code_sum,
+                        void *stream)
+{
+    if (n < 1 || n > 0x7FFFFFFF || d < 0)
+        return fail(GQ_ERR_ARG, "n must be >= 1 and d >= 0");
+    if ((!codes || !code_sum) && d > 0)
+        return fail(GQ_ERR_NULL, "codes or code_sum is NULL");
+    if (code_bits < 2 || code_bits > 32)
+        return fail(GQ_ERR_CODE_WIDTH, "code_bits %d outside [2, 32]", code_bits);
+    if (!aligned16(codes) || !aligned16(code_sum))
+        return fail(GQ_ERR_ALIGN, "codes or code_sum is not 16-byte aligned");
+    const int64_t tiles = (d + kTile - 1) / kTile;
+    if (tiles == 0)
+        return ok();
+    if (tiles > kMaxGrid)
+        return fail(GQ_ERR_UNSUPPORTED, "d exceeds the launch limit");
+    k_reduce_codes<<<dim3((unsigned)tiles), dim3(kThreads), 0, (hipStream_t)stream>>>(
+        (const uint8_t *)codes, n, code_bits, row_bytes(d, code_bits), (uint8_t *)code_sum);
+    return check_launch("k_reduce_codes");
+}
+
+int32_t gq_dequantize(const void *code_sum, int64_t n, int64_t d, int32_t s, int32_t scheme,
+                      int32_t code_bits, const float *norm_dev, float *mean, void *stream)
+{
+    if (!norm_dev || ((!code_sum || !mean) && d > 0))
+        return fail(GQ_ERR_NULL, "code_sum, norm_dev or mean is NULL");
+    if (n < 1 || n > 0x7FFFFFFF || d < 0)
+        return fail(GQ_ERR_ARG, "n must be >= 1 and d >= 0");
+    GQ_TRY(validate_scheme(s, scheme));
+    GQ_TRY(validate_width(n, s, scheme, code_bits));
+    if (!aligned16(code_sum) || !aligned16(mean))
+        return fail(GQ_ERR_ALIGN, "code_sum or mean is not 16-byte aligned");
+    const int64_t tiles = (d + kTile - 1) / kTile;
+    if (tiles == 0)
+        return ok();
+    if (tiles > kMaxGrid)
+        return fail(GQ_ERR_UNSUPPORTED, "d exceeds the launch limit");
+    const dim3 grid((unsigned)tiles), block(kThreads);
+    hipStream_t st = (hipStream_t)stream;
+    if (scheme == GQ_SCHEME_L)
+        k_dequantize<GQ_SCHEME_L><<<grid, block, 0, st>>>((const uint8_t *)code_sum, n, d, s, code_bits, norm_dev, mean);
+    else
+        k_dequantize<GQ_SCHEME_E><<<grid, block, 0, st>>>((const uint8_t *)code_sum, n, d, s, code_bits, norm_dev, mean);
+    return check_launch("k_dequantize");
+}
+
+int32_t gq_compress_mean_from_norm(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                                   int32_t scheme, uint64_t seed, const float *norm_dev,
+                                   int32_t code_bits, float *mean, void *code_sum_or_null,
+                                   void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    GQ_TRY(validate_scheme(s, scheme));
+    if (!norm_dev || (!mean && d > 0))
+        return fail(GQ_ERR_NULL, "norm_dev or mean is NULL");
+    if (min_bits(n, s, scheme) > 32)
+        return fail(GQ_ERR_CODE_WIDTH, "sums of %lld codes do not fit 32 bits", (long long)n);
+    if (code_sum_or_null) {
+        GQ_TRY(validate_width(n, s, scheme, code_bits));
+        if (!aligned16(code_sum_or_null))
+            return fail(GQ_ERR_ALIGN, "code_sum is not 16-byte aligned");
+    }
+    if (!aligned16(mean))
+        return fail(GQ_ERR_ALIGN, "mean is not 16-byte aligned");
+    return launch_compress(x, dtype, n, d, s, scheme, seed, norm_dev, code_bits, mean,
+                           code_sum_or_null, (hipStream_t)stream);
+}
+
+int32_t gq_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s, float q,
+                         float p, int32_t scheme, uint64_t seed, int32_t code_bits, float *mean,
+                         float *norm_dev, void *code_sum_or_null, void *workspace,
+                         int64_t workspace_bytes, void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    GQ_TRY(validate_scheme(s, scheme));
+    if (!norm_dev || (!mean && d > 0))
+        return fail(GQ_ERR_NULL, "norm_dev or mean is NULL");
+    if (!order_ok(q) || !order_ok(p))
+        return fail(GQ_ERR_UNSUPPORTED, "q and p must be 2 or +inf");
+    if (min_bits(n, s, scheme) > 32)
+        return fail(GQ_ERR_CODE_WIDTH, "sums of %lld codes do not fit 32 bits", (long long)n);
+    if (code_sum_or_null) {
+        GQ_TRY(validate_width(n, s, scheme, code_bits));
+        if (!aligned16(code_sum_or_null))
+            return fail(GQ_ERR_ALIGN, "code_sum is not 16-byte aligned");
+    }
+    if (!aligned16(mean))
+        return fail(GQ_ERR_ALIGN, "mean is not 16-byte aligned");
+    GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
+    hipStream_t st = (hipStream_t)stream;
+    GQ_TRY(launch_norm(x, dtype, n, d, isinf(q), isinf(p), false, norm_dev, workspace, 0, st));
+    return launch_compress(x, dtype, n, d, s, scheme, seed, norm_dev, code_bits, mean,
+                           code_sum_or_null, st);
+}
+
+int32_t gq_qsgd_local_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                           uint64_t seed, float *mean, float *norms_dev, void *codes_or_null,
+                           int32_t code_bits, void *workspace, int64_t workspace_bytes,
+                           void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    GQ_TRY(validate_scheme(s, GQ_SCHEME_L));
+    if (!norms_dev || (!mean && d > 0))
+        return fail(GQ_ERR_NULL, "mean or norms_dev is NULL");
+    if (codes_or_null) {
+        GQ_TRY(validate_width(1, s, GQ_SCHEME_L, code_bits));
+        if (!aligned16(codes_or_null))
+            return fail(GQ_ERR_ALIGN, "codes is not 16-byte aligned");
+    }
+    if (!aligned16(mean))
+        return fail(GQ_ERR_ALIGN, "mean is not 16-byte aligned");
+    GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
+    hipStream_t st = (hipStream_t)stream;
+    GQ_TRY(launch_norm(x, dtype, n, d, false, false, true, norms_dev, workspace, s, st));
+    const int64_t tiles = (d + kTile - 1) / kTile;
+    if (tiles == 0)
+        return ok();
+    const WsLayout L = ws_layout(n, d);
+    const WorkerParams *params = (const WorkerParams *)((const char *)workspace + L.params);
+    const int64_t rb = codes_or_null ? row_bytes(d, code_bits) : 0;
+    const dim3 grid((unsigned)tiles), block(kThreads);
+    if (dtype == GQ_IN_F32)
+        k_local_mean<GQ_IN_F32><<<grid, block, 0, st>>>(x, n, d, s, seed, norms_dev, params, mean, (uint8_t *)codes_or_null, code_bits, rb);
+    else
+        k_local_mean<GQ_IN_BF16><<<grid, block, 0, st>>>(x, n, d, s, seed, norms_dev, params, mean, (uint8_t *)codes_or_null, code_bits, rb);
+    return check_launch("k_local_mean");
+}
+
+} // extern "C"

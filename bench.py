@@ -1,0 +1,224 @@
+"""Benchmark of the fused Global-QSGD compress + integer sum + dequantize path.
+
+One step = one gq_compress_mean call over one batch of n simulated workers'
+gradient shards already resident in HBM: the global (q,p)-norm pass, then
+the fused quantize / exact integer sum / dequantize pass.  The default
+workload is the ResNet-50-sized bucket: standard dithering, s = 127,
+q = 2, p = inf, n = 8 workers x d = 25,557,032 fp32 coordinates.
+
+Prints one JSON line.  `value` is input GB/s (n d bytes-per-element / step
+time); `roofline` describes the dominant kernel (k_compress_mean) timed per
+launch with HIP events on the stream it runs on; `cpu_baseline` is the CPU
+oracle timed on a bounded prefix of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+DOMINANT = "k_compress_mean"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, help="workload key in workloads.WORKLOADS")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--unfused", action="store_true", help="also time the four-call unfused path")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "allreduce_compatible_gradient_amd", "csrc", "gq.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload_name: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload_name)
+    if not rec or rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def event_pairs(torch, k):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(k)]
+
+
+def cpu_baseline(w, target_s: float):
+    """The oracle as it is (one thread, scalar C) on the first d' coordinates of every worker."""
+    import oracle
+    import workloads as wl
+    scheme = oracle.SCHEME_L if w.scheme == "L" else oracle.SCHEME_E
+    d0 = 1 << 12
+    x = wl.generate(w, d=d0)
+    t0 = time.perf_counter()
+    oracle.compress_mean(x, w.s, w.q, w.p, scheme, w.seed)
+    per_elem = (time.perf_counter() - t0) / (w.n * d0)
+    d1 = int(min(w.d, max(d0, target_s / per_elem / w.n)))
+    x = wl.generate(w, d=d1)
+    t0 = time.perf_counter()
+    oracle.compress_mean(x, w.s, w.q, w.p, scheme, w.seed)
+    dt = time.perf_counter() - t0
+    gbs = w.n * d1 * w.elem_bytes / dt / 1e9
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {d1} of {w.d} coordinates of all {w.n} workers "
+                      f"({w.n * d1} elements, {dt:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the n workers are "
+              "simulated as rows of one device buffer and no collective is part of this build",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import allreduce_compatible_gradient_amd as gq
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 5}))
+        return
+
+    w = wl.WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    x = wl.generate(w, threads=min(16, os.cpu_count() or 1))
+    xd = torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).to(dev)
+    if w.dtype == "bf16":
+        xd = xd.view(torch.bfloat16)
+    del x
+    gen_s = time.perf_counter() - t0
+    n, d = w.n, w.d
+    mean = torch.empty(d, dtype=torch.float32, device=dev)
+    norm = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(gq.gq_workspace_bytes(n, d), dtype=torch.uint8, device=dev)
+
+    def step():
+        gq.gq_compress_mean(xd, w.s, w.q, w.p, w.scheme, w.seed, mean=mean, norm=norm,
+                            workspace=ws, stream=stream)
+
+    # ---- the timed steps (value)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # ---- the dominant kernel alone, one event pair per launch on the same stream
+    kpairs = event_pairs(torch, args.steps)
+    npairs = event_pairs(torch, args.steps)
+    for i in range(args.steps):
+        npairs[i][0].record(stream)
+        gq.gq_global_norm(xd, w.q, w.p, norm=norm, workspace=ws, stream=stream)
+        npairs[i][1].record(stream)
+        kpairs[i][0].record(stream)
+        gq.gq_compress_mean_from_norm(xd, w.s, w.scheme, w.seed, norm, mean=mean, stream=stream)
+        kpairs[i][1].record(stream)
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in kpairs]))
+    n_ms = float(np.mean([a.elapsed_time(b) for a, b in npairs]))
+
+    in_bytes = n * d * w.elem_bytes
+    k_alg = in_bytes + 4 * d                      # one read of x, one write of the mean
+    fused_alg = 2 * in_bytes + 4 * d              # both passes
+    value = in_bytes / (ms * 1e-3) / 1e9
+    achieved = k_alg / (k_ms * 1e-3) / 1e9
+    W = gq.gq_min_code_bits(n, w.s, w.scheme)
+    out = {
+        "metric": "fused Global-QSGD compress+int-sum+dequant GB/s (fp32 in) and % HBM peak",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "scheme": f"Global-{w.scheme}_s", "s": w.s,
+                   "q": w.q if w.q != float("inf") else "inf",
+                   "p": w.p if w.p != float("inf") else "inf",
+                   "n_workers": n, "d": d, "input_dtype": w.dtype, "code_bits": w.code_bits,
+                   "min_code_bits": W, "values": w.values},
+        "hbm_frac_fused": round(fused_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernels_ms": {"norm_pass": round(n_ms, 6), DOMINANT: round(k_ms, 6)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for(w.name), "kernel": DOMINANT,
+                     "alg_bytes_per_launch": k_alg},
+        "bits_per_element": w.code_bits,
+        "input_gen_s": round(gen_s, 2),
+    }
+    if args.unfused:
+        codes = torch.empty((n, gq.gq_code_row_bytes(d, w.code_bits)), dtype=torch.uint8,
+                            device=dev)
+        csum = torch.empty(gq.gq_code_row_bytes(d, w.code_bits), dtype=torch.uint8, device=dev)
+
+        def ustep():
+            gq.gq_global_norm(xd, w.q, w.p, norm=norm, workspace=ws, stream=stream)
+            gq.gq_quantize(xd, w.s, w.scheme, norm, w.seed, w.code_bits, codes=codes,
+                           stream=stream)
+            gq.gq_reduce_codes(codes, n, d, w.code_bits, code_sum=csum, stream=stream)
+            gq.gq_dequantize(csum, n, d, w.s, w.scheme, w.code_bits, norm, mean=mean,
+                             stream=stream)
+        for _ in range(3):
+            ustep()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            ustep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ums = e0.elapsed_time(e1) / args.steps
+        out["unfused"] = {"ms_per_step": round(ums, 6),
+                          "input_GBs": round(in_bytes / (ums * 1e-3) / 1e9, 3)}
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

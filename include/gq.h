@@ -1,0 +1,170 @@
+/*
+ * gq.h -- Global-QSGD gradient compression on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libgq.so.  The operator is the Allreduce-compatible quantizer of
+ * "Global-QSGD: Practical Floatless Quantization for Distributed Learning
+ * with Theoretical Guarantees" (Xin, Canini, Richtarik, Horvath):
+ *   - Sec. 2 (notation) defines the (q,p)-norm of the concatenation
+ *     x = [x_1 .. x_n] of the n workers' vectors;
+ *   - Sec. 3 (Global-Q) divides every coordinate by that ONE global norm,
+ *     instead of each worker's local norm, and rounds it at random, without
+ *     bias, to a level grid: standard dithering Global-L_s (levels (s-i)/s)
+ *     or exponential dithering Global-E_s (levels 0 and 2^-k);
+ *   - Sec. 6 (implementation) runs quantization, an integer Allreduce and
+ *     one dequantization per gradient bucket.
+ * Here the n workers are the n rows of one device buffer x[n][d], and the
+ * Allreduce is an exact integer sum over those rows.
+ *
+ * Conventions shared by every entry point
+ *   - x is row-major [n][d]; row i is worker i.  dtype GQ_IN_F32 (float) or
+ *     GQ_IN_BF16 (bfloat16, widened exactly to float).
+ *   - q, p are 2.0f or +INFINITY (the (q,p)-norm: q inside a worker, p over
+ *     the n per-worker norms).
+ *   - s: number of level intervals.  L: 1 <= s <= 2^24; the integer code of
+ *     a coordinate is in [-s, s].  E: 1 <= s <= 31; levels 2^-k (k < s)
+ *     are coded as the integers 2^(s-1-k), so codes are in [-2^(s-1), 2^(s-1)].
+ *     M denotes the top code (s for L, 2^(s-1) for E).
+ *   - code_bits W: two's-complement width of packed codes and code sums;
+ *     gq_min_code_bits(n, s, scheme) <= W <= 32 so that any sum of n codes
+ *     is exact in W bits.
+ *   - Packed layout: each row is a little-endian bitstream; coordinate j
+ *     occupies bits [j W, j W + W); rows are gq_code_row_bytes(d, W) bytes
+ *     apart (16-byte multiples); pad bits are zero.  W = 8, 16, 32 is
+ *     exactly an int8 / int16 / int32 array.
+ *   - Randomness: Philox4x32-10 (Salmon et al., SC'11), key = seed, counter
+ *     (lo32(j/8), hi32(j/8), worker, draw).  Coordinate j of worker w uses the
+ *     16-bit half (j%8)%2 of word (j%8)/2 of draw 0 as the high half of a
+ *     32-bit uniform u and the same half of draw 1 as its low half; the
+ *     upper level is taken iff u < F, F = floor(frac * 2^32).
+ *   - Memory: every pointer is a DEVICE pointer owned by the caller.  x,
+ *     mean and packed code buffers must be 16-byte aligned.  With d == 0
+ *     the per-coordinate buffers (x, codes, sums, mean) may be NULL.  The library
+ *     allocates nothing and keeps no state between calls.
+ *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Calls only
+ *     enqueue kernels and never synchronize; results are ready when the
+ *     stream reaches them.  Scalars computed on the device (the norm) stay
+ *     there and later calls read them there.
+ *   - Errors: every argument check runs before any HIP call, and a failing
+ *     check returns its status with nothing enqueued.  GQ_ERR_DEVICE means a
+ *     launch failed (hipGetLastError); gq_last_error() describes the most
+ *     recent failure of the calling thread.  Non-finite inputs give
+ *     unspecified but in-range codes (|code| <= M) and never fault.
+ */
+#ifndef GQ_H
+#define GQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { GQ_SCHEME_L = 0, GQ_SCHEME_E = 1 };
+enum { GQ_IN_F32 = 0, GQ_IN_BF16 = 1 };
+
+enum {
+    GQ_OK = 0,
+    GQ_ERR_NULL = 1,        /* a required pointer is NULL */
+    GQ_ERR_ARG = 2,         /* n, d, s, dtype or scheme out of range */
+    GQ_ERR_UNSUPPORTED = 3, /* q or p not in {2, inf}; sizes beyond the launch limits */
+    GQ_ERR_CODE_WIDTH = 4,  /* code_bits outside [gq_min_code_bits, 32] */
+    GQ_ERR_WORKSPACE = 5,   /* workspace smaller than gq_workspace_bytes */
+    GQ_ERR_ALIGN = 6,       /* a buffer is not 16-byte aligned */
+    GQ_ERR_DEVICE = 7       /* a HIP launch failed */
+};
+
+/* Smallest code width that holds every sum of n codes of the scheme:
+ * ceil(log2(n M + 1)) + 1.  Returns -1 for invalid (n, s, scheme).        */
+int32_t gq_min_code_bits(int64_t n, int32_t s, int32_t scheme);
+
+/* Bytes of one packed row of d W-bit fields: 16 * ceil(d W / 128).
+ * Returns -1 for d < 0 or W outside [1, 32].                               */
+int64_t gq_code_row_bytes(int64_t d, int32_t code_bits);
+
+/* Device workspace needed by gq_global_norm, gq_compress_mean and
+ * gq_qsgd_local_mean for an [n][d] input (per-block partial norms and the
+ * per-worker norms).  Returns -1 for invalid sizes.                        */
+int64_t gq_workspace_bytes(int64_t n, int64_t d);
+
+/* Global (q,p)-norm of the concatenation (Sec. 2 notation):
+ *   q = 2: S_i = sum_j x_ij^2 in fp64 (each square exact); q = inf:
+ *   m_i = max_j |x_ij|.  p = 2: N = fp32(sqrt(sum_i S_i)) (q = 2) or
+ *   fp32(sqrt(sum_i m_i^2)) (q = inf); p = inf: N = fp32(sqrt(max_i S_i))
+ *   or max_i m_i.  Writes N to norm_dev[0] (one float, device).
+ * The reduction tree is fixed by (n, d), so repeated calls give identical
+ * bits.  d == 0 gives N = 0.                                               */
+int32_t gq_global_norm(const void *x, int32_t dtype, int64_t n, int64_t d, float q, float p,
+                       float *norm_dev, void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Quantization (Sec. 3, Global-Q with the L or E levels), given the global
+ * norm N in norm_dev[0]:
+ *   pre = 2^64 if N < 2^-64 else 1 (exact);  L: sigma = fp32(s / (N pre)),
+ *   E: sigma = fp32(1 / (N pre)), both divided in fp64;
+ *   t = fp32(fp32(|x| pre) sigma) clamped to s (L) or 1 (E);
+ *   L: magnitude floor(t) or floor(t)+1, F = floor((t - floor t) 2^32);
+ *   E: t = 2^e (1+phi) >= 2^(1-s): magnitude 2^(e+s-1) or twice it,
+ *      F = phi 2^32; t < 2^(1-s): magnitude 0 or 1, F = floor(t 2^(s-1) 2^32);
+ *   code = (u < F ? upper : lower), negated when the sign bit of x is set.
+ * N == 0 gives all-zero codes.  Row i uses worker index worker_base + i in
+ * the Philox counter, so shards quantized on different devices with their
+ * global row index reproduce one big quantization.
+ * codes: n rows of gq_code_row_bytes(d, W) bytes.  W must hold a sum of n
+ * codes (gq_min_code_bits(n, s, scheme) <= W <= 32).                       */
+int32_t gq_quantize(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s, int32_t scheme,
+                    const float *norm_dev, uint64_t seed, int64_t worker_base, int32_t code_bits,
+                    void *codes, void *stream);
+
+/* The integer Allreduce of Sec. 6 on one device: code_sum[j] = sum_i
+ * code[i][j], exact, written as one packed row of W-bit fields.  The sum
+ * is exact whenever the codes came from gq_quantize with the same n and W
+ * (W >= gq_min_code_bits); otherwise it wraps modulo 2^W.                  */
+int32_t gq_reduce_codes(const void *codes, int64_t n, int64_t d, int32_t code_bits,
+                        void *code_sum, void *stream);
+
+/* Dequantization to the mean (Sec. 6): mean[j] = fp32(code_sum[j] kappa),
+ * kappa = fp64(N / (n M)), product in fp64.  mean: d floats, device.       */
+int32_t gq_dequantize(const void *code_sum, int64_t n, int64_t d, int32_t s, int32_t scheme,
+                      int32_t code_bits, const float *norm_dev, float *mean, void *stream);
+
+/* Fused quantize + exact integer sum + dequantize in one streaming pass,
+ * given N in norm_dev[0]: equals gq_quantize, gq_reduce_codes and
+ * gq_dequantize in sequence, without materializing the codes.  If
+ * code_sum_or_null is not NULL it also receives the packed W-bit code sums
+ * (then W must satisfy the width rule; otherwise code_bits is ignored).    */
+int32_t gq_compress_mean_from_norm(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                                   int32_t scheme, uint64_t seed, const float *norm_dev,
+                                   int32_t code_bits, float *mean, void *code_sum_or_null,
+                                   void *stream);
+
+/* The whole path: gq_global_norm, then gq_compress_mean_from_norm.
+ * Writes N to norm_dev[0] and the dequantized mean to mean[0..d).          */
+int32_t gq_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s, float q,
+                         float p, int32_t scheme, uint64_t seed, int32_t code_bits, float *mean,
+                         float *norm_dev, void *code_sum_or_null, void *workspace,
+                         int64_t workspace_bytes, void *stream);
+
+/* Ablation: QSGD with LOCAL norms, the scheme Global-QSGD replaces (Sec. 3:
+ * each worker normalizes by its own norm).  Worker i uses
+ * N_i = fp32(sqrt(sum_j x_ij^2)) and the L_s rules above with N_i; codes
+ * are in [-s, s] and are not summable across workers.
+ * mean[j] = fp32(sum_i fp64(code_ij kappa_i)), kappa_i = fp64(N_i / (n s)),
+ * accumulated in fp64 in worker order.  norms_dev: n floats.  If
+ * codes_or_null is not NULL it receives the per-worker packed codes at
+ * code_bits (gq_min_code_bits(1, s, GQ_SCHEME_L) <= W <= 32).             */
+int32_t gq_qsgd_local_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                           uint64_t seed, float *mean, float *norms_dev, void *codes_or_null,
+                           int32_t code_bits, void *workspace, int64_t workspace_bytes,
+                           void *stream);
+
+/* Name of a status code (static string).                                  */
+const char *gq_status_str(int32_t status);
+
+/* Description of the last failed call on this thread ("" if none).        */
+const char *gq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQ_H */

@@ -60,6 +60,8 @@ def lib():
         L.oracle_uniform32.restype = ctypes.c_uint32
         L.oracle_global_norm.argtypes = [_vp, _int, _i64, _i64, _f32, _f32, _vp]
         L.oracle_global_norm.restype = _f32
+        L.oracle_norm_from_partials.argtypes = [_vp, _i64, _f32, _f32]
+        L.oracle_norm_from_partials.restype = _f32
         L.oracle_top_code.argtypes = [_int, _int]
         L.oracle_top_code.restype = _i64
         L.oracle_scale_params.argtypes = [_f32, _i64, _int, _int, _vp, _vp, _vp]
@@ -80,6 +82,9 @@ def lib():
         L.oracle_compress_mean.argtypes = [_vp, _int, _i64, _i64, _int, _f32, _f32, _int, _u64,
                                            _vp, _vp]
         L.oracle_compress_mean.restype = _f32
+        L.oracle_local_norms.argtypes = [_vp, _int, _i64, _i64, _vp]
+        L.oracle_qsgd_local_cols.argtypes = [_vp, _int, _i64, _i64, _int, _u64, _vp, _vp, _i64,
+                                             _vp, _vp]
         L.oracle_qsgd_local_mean.argtypes = [_vp, _int, _i64, _i64, _int, _u64, _vp, _vp, _vp]
         _lib = L
     return _lib
@@ -140,6 +145,28 @@ def global_norm(x: np.ndarray, q, p):
     n, d = x.shape
     pw = np.zeros(n, dtype=np.float64)
     N = lib().oracle_global_norm(_ptr(x), _x_dtype(x), n, d, _order(q), _order(p), _ptr(pw))
+    return np.float32(N), pw
+
+
+def global_norm_rows(x: np.ndarray, q, p, threads: int = 1):
+    """global_norm computed one row at a time (rows in parallel threads), then combined.
+
+    Same arithmetic as global_norm: each row's partial is its own oracle call."""
+    from concurrent.futures import ThreadPoolExecutor
+    x = _rows(x)
+    n = x.shape[0]
+    pw = np.zeros(n, dtype=np.float64)
+
+    def one(i):
+        pw[i] = global_norm(x[i:i + 1], q, p)[1][0]
+
+    if threads > 1:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, range(n)))
+    else:
+        for i in range(n):
+            one(i)
+    N = lib().oracle_norm_from_partials(_ptr(pw), n, _order(q), _order(p))
     return np.float32(N), pw
 
 
@@ -265,3 +292,40 @@ def qsgd_local_mean(x: np.ndarray, s: int, seed: int):
     lib().oracle_qsgd_local_mean(_ptr(x), _x_dtype(x), n, d, s, seed, _ptr(norms), _ptr(codes),
                                  _ptr(mean))
     return norms, codes, mean
+
+
+def local_norms(x: np.ndarray, threads: int = 1) -> np.ndarray:
+    """Per-worker l2 norms of the ablation, fp32 [n] (rows in parallel threads)."""
+    from concurrent.futures import ThreadPoolExecutor
+    x = _rows(x)
+    n, d = x.shape
+    norms = np.zeros(n, dtype=np.float32)
+
+    def one(i):
+        r = np.ascontiguousarray(x[i:i + 1])
+        out = np.zeros(1, dtype=np.float32)
+        lib().oracle_local_norms(_ptr(r), _x_dtype(r), 1, d, _ptr(out))
+        norms[i] = out[0]
+
+    if threads > 1:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, range(n)))
+    else:
+        for i in range(n):
+            one(i)
+    return norms
+
+
+def qsgd_local_cols(x: np.ndarray, norms: np.ndarray, s: int, seed: int, cols):
+    """Selected coordinates of the ablation given the norms: (codes int32 [n, k], mean [k])."""
+    x = _rows(x)
+    n, d = x.shape
+    norms = np.ascontiguousarray(norms, dtype=np.float32)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if cols.size and (cols.min() < 0 or cols.max() >= d):
+        raise IndexError("column out of range")
+    codes = np.zeros((n, cols.size), dtype=np.int32)
+    mean = np.zeros(cols.size, dtype=np.float32)
+    lib().oracle_qsgd_local_cols(_ptr(x), _x_dtype(x), n, d, s, seed, _ptr(norms), _ptr(cols),
+                                 cols.size, _ptr(codes), _ptr(mean))
+    return codes, mean

@@ -140,10 +140,28 @@ static void nsum_add(nsum *a, double v)
 
 static int is_inf_order(float v) { return isinf(v) && v > 0; }
 
+/* Combination over workers of the per-worker values (sum of squares for
+ * q = 2, max |x| for q = inf) with the outer order p.                    */
+float oracle_norm_from_partials(const double *per_worker, int64_t n, float q, float p)
+{
+    int q_inf = is_inf_order(q), p_inf = is_inf_order(p);
+    if (p_inf) {
+        double m = 0.0;
+        for (int64_t i = 0; i < n; ++i)
+            if (per_worker[i] > m)
+                m = per_worker[i];
+        return q_inf ? (float)m : (float)sqrt(m);
+    }
+    nsum tot = {0.0, 0.0};
+    for (int64_t i = 0; i < n; ++i)
+        nsum_add(&tot, q_inf ? per_worker[i] * per_worker[i] : per_worker[i]);
+    return (float)sqrt(tot.s + tot.c);
+}
+
 float oracle_global_norm(const void *x, int dtype, int64_t n, int64_t d,
                          float q, float p, double *per_worker)
 {
-    int q_inf = is_inf_order(q), p_inf = is_inf_order(p);
+    int q_inf = is_inf_order(q);
     for (int64_t i = 0; i < n; ++i) {
         if (q_inf) {
             float m = 0.0f;
@@ -162,18 +180,7 @@ float oracle_global_norm(const void *x, int dtype, int64_t n, int64_t d,
             per_worker[i] = acc.s + acc.c;
         }
     }
-    /* combine over workers */
-    if (p_inf) {
-        double m = 0.0;
-        for (int64_t i = 0; i < n; ++i)
-            if (per_worker[i] > m)
-                m = per_worker[i];
-        return q_inf ? (float)m : (float)sqrt(m);
-    }
-    nsum tot = {0.0, 0.0};
-    for (int64_t i = 0; i < n; ++i)
-        nsum_add(&tot, q_inf ? per_worker[i] * per_worker[i] : per_worker[i]);
-    return (float)sqrt(tot.s + tot.c);
+    return oracle_norm_from_partials(per_worker, n, q, p);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -238,7 +245,7 @@ void oracle_bracket(float xv, float pre, float sigma, int zero_norm, int s, int 
         uint32_t mant = tb & 0x7FFFFFu;
         int32_t lo = (int32_t)1 << (e + s - 1);
         *m_lo = lo;
-        *m_hi = 2 * lo;
+        *m_hi = (int32_t)(2u * (uint32_t)lo); /* unused when F == 0 (t = 1, s = 31) */
         *F = mant << 9;
     } else {
         float f = t * ldexpf(1.0f, s - 1);
@@ -401,16 +408,8 @@ float oracle_compress_mean(const void *x, int dtype, int64_t n, int64_t d, int s
  * The mean is not an integer sum any more: mean_j = fp32(sum_i code_ij *
  * kappa_i) with kappa_i = fp64(N_i / (n s)), accumulated in fp64 in worker
  * order 0..n-1.                                                           */
-void oracle_qsgd_local_mean(const void *x, int dtype, int64_t n, int64_t d, int s, uint64_t seed,
-                            float *norms, int32_t *codes_or_null, float *mean)
+void oracle_local_norms(const void *x, int dtype, int64_t n, int64_t d, float *norms)
 {
-    float *pre = (float *)malloc((size_t)n * sizeof(float));
-    float *sig = (float *)malloc((size_t)n * sizeof(float));
-    double *kap = (double *)malloc((size_t)n * sizeof(double));
-    if (!pre || !sig || !kap) {
-        free(pre); free(sig); free(kap);
-        return;
-    }
     for (int64_t i = 0; i < n; ++i) {
         nsum acc = {0.0, 0.0};
         for (int64_t j = 0; j < d; ++j) {
@@ -418,21 +417,45 @@ void oracle_qsgd_local_mean(const void *x, int dtype, int64_t n, int64_t d, int 
             nsum_add(&acc, v * v);
         }
         norms[i] = (float)sqrt(acc.s + acc.c);
-        oracle_scale_params(norms[i], 1, s, ORACLE_SCHEME_L, &pre[i], &sig[i], &kap[i]);
-        kap[i] = (double)norms[i] / ((double)n * (double)s);
     }
-    for (int64_t j = 0; j < d; ++j) {
+}
+
+/* Listed coordinates of the ablation, given the per-worker norms; codes_or_null
+ * (n x ncols, row-major) receives the per-worker codes of those coordinates. */
+void oracle_qsgd_local_cols(const void *x, int dtype, int64_t n, int64_t d, int s, uint64_t seed,
+                            const float *norms, const int64_t *cols, int64_t ncols,
+                            int32_t *codes_or_null, float *mean)
+{
+    for (int64_t c = 0; c < ncols; ++c) {
+        int64_t j = cols[c];
         double acc = 0.0;
         for (int64_t i = 0; i < n; ++i) {
+            float pre, sigma;
+            double kappa;
+            oracle_scale_params(norms[i], 1, s, ORACLE_SCHEME_L, &pre, &sigma, &kappa);
+            kappa = (double)norms[i] / ((double)n * (double)s);
             uint64_t g = (uint64_t)(i * d + j);
             uint32_t u = oracle_uniform32(seed, (uint64_t)i, (uint64_t)j);
-            int32_t c = oracle_code(load_x(x, dtype, g), pre[i], sig[i], norms[i] == 0.0f, s,
-                                    ORACLE_SCHEME_L, u);
+            int32_t code = oracle_code(load_x(x, dtype, g), pre, sigma, norms[i] == 0.0f, s,
+                                       ORACLE_SCHEME_L, u);
             if (codes_or_null)
-                codes_or_null[g] = c;
-            acc = acc + (double)c * kap[i];
+                codes_or_null[i * ncols + c] = code;
+            acc = acc + (double)code * kappa;
         }
-        mean[j] = (float)acc;
+        mean[c] = (float)acc;
     }
-    free(pre); free(sig); free(kap);
+}
+
+void oracle_qsgd_local_mean(const void *x, int dtype, int64_t n, int64_t d, int s, uint64_t seed,
+                            float *norms, int32_t *codes_or_null, float *mean)
+{
+    int64_t *cols = (int64_t *)malloc((size_t)(d > 0 ? d : 1) * sizeof(int64_t));
+    if (!cols)
+        return;
+    oracle_local_norms(x, dtype, n, d, norms);
+    for (int64_t j = 0; j < d; ++j)
+        cols[j] = j;
+    /* with every column listed in order, the [n][ncols] codes are the [n][d] codes */
+    oracle_qsgd_local_cols(x, dtype, n, d, s, seed, norms, cols, d, codes_or_null, mean);
+    free(cols);
 }

@@ -1,0 +1,129 @@
+"""The C ABI on the CPU: the library loads, exports what include/gq.h
+declares, and rejects bad arguments before touching the device."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import allreduce_compatible_gradient_amd as gq
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "gq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gq_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = gq.lib()
+    names = _declared()
+    assert "gq_compress_mean" in names and len(names) >= 12
+    for name in names:
+        assert hasattr(L, name), name
+        assert name in gq.SIGNATURES, name
+
+
+def test_status_strings():
+    L = gq.lib()
+    for code, name in gq.STATUS.items():
+        assert L.gq_status_str(code).decode() == name
+
+
+def test_size_helpers_match_the_oracle():
+    for n in (1, 2, 4, 8, 16, 64, 1000):
+        for s in (1, 3, 7, 15, 127):
+            assert gq.gq_min_code_bits(n, s, "L") == oracle.min_code_bits(n, s, oracle.SCHEME_L)
+        for s in (1, 4, 8, 12):
+            assert gq.gq_min_code_bits(n, s, "E") == oracle.min_code_bits(n, s, oracle.SCHEME_E)
+    for d in (0, 1, 7, 8, 65536, 25_557_032):
+        for W in (2, 6, 8, 9, 11, 13, 16, 31, 32):
+            assert gq.gq_code_row_bytes(d, W) == oracle.row_bytes(d, W)
+    assert gq.gq_min_code_bits(0, 3, "L") == -1
+    assert gq.gq_min_code_bits(2, 0, "L") == -1
+    assert gq.gq_min_code_bits(2, 32, "E") == -1
+    assert gq.gq_code_row_bytes(10, 33) == -1
+    assert gq.gq_workspace_bytes(8, 25_557_032) > 0
+    assert gq.gq_workspace_bytes(0, 5) == -1
+
+
+# Fake device pointers: every call below fails validation before any HIP call.
+A = ctypes.c_void_p(0x10000)   # 16-byte aligned
+U = ctypes.c_void_p(0x10004)   # misaligned
+NUL = None
+WS = gq.gq_workspace_bytes(4, 1000)
+
+
+def _err(status):
+    return gq.STATUS[status]
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((NUL, 0, 4, 1000, 2.0, 2.0, A, A, WS, NUL), 1),      # x NULL
+    ((A, 0, 4, 1000, 2.0, 2.0, NUL, A, WS, NUL), 1),      # norm NULL
+    ((A, 5, 4, 1000, 2.0, 2.0, A, A, WS, NUL), 2),        # dtype
+    ((A, 0, 0, 1000, 2.0, 2.0, A, A, WS, NUL), 2),        # n = 0
+    ((A, 0, 4, -1, 2.0, 2.0, A, A, WS, NUL), 2),          # d < 0
+    ((A, 0, 1 << 30, 1 << 40, 2.0, 2.0, A, A, WS, NUL), 2),  # n d overflow
+    ((A, 0, 4, 1000, 3.0, 2.0, A, A, WS, NUL), 3),        # q = 3
+    ((A, 0, 4, 1000, 2.0, 1.0, A, A, WS, NUL), 3),        # p = 1
+    ((A, 0, 4, 1000, 2.0, -math.inf, A, A, WS, NUL), 3),  # p = -inf
+    ((U, 0, 4, 1000, 2.0, 2.0, A, A, WS, NUL), 6),        # x misaligned
+    ((A, 0, 4, 1000, 2.0, 2.0, A, A, WS - 1, NUL), 5),    # workspace too small
+    ((A, 0, 4, 1000, 2.0, 2.0, A, NUL, WS, NUL), 1),      # workspace NULL
+])
+def test_global_norm_rejects(args, expect):
+    assert gq.lib().gq_global_norm(*args) == expect
+    assert gq.lib().gq_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A, 0, 4, 100, 7, 0, A, 1, 0, 8, A, NUL), 0xFF),     # valid: not called (sentinel)
+    ((A, 0, 4, 100, 0, 0, A, 1, 0, 8, A, NUL), 2),        # s = 0
+    ((A, 0, 4, 100, 7, 2, A, 1, 0, 8, A, NUL), 2),        # scheme 2
+    ((A, 0, 4, 100, 32, 1, A, 1, 0, 32, A, NUL), 2),      # E with s = 32
+    ((A, 0, 4, 100, 7, 0, A, 1, 0, 5, A, NUL), 4),        # W below W_min = 6
+    ((A, 0, 4, 100, 7, 0, A, 1, 0, 33, A, NUL), 4),       # W above 32
+    ((A, 0, 1 << 28, 100, 127, 0, A, 1, 0, 32, A, NUL), 4),  # n s needs > 32 bits
+    ((A, 0, 4, 100, 7, 0, NUL, 1, 0, 8, A, NUL), 1),      # norm NULL
+    ((A, 0, 4, 100, 7, 0, A, 1, 0, 8, NUL, NUL), 1),      # codes NULL
+    ((A, 0, 4, 100, 7, 0, A, 1, 0, 8, U, NUL), 6),        # codes misaligned
+    ((A, 0, 4, 100, 7, 0, A, 1, -1, 8, A, NUL), 2),       # worker_base < 0
+    ((A, 0, 4, 100, 7, 0, A, 1, (1 << 32) - 2, 8, A, NUL), 2),  # workers past 2^32
+])
+def test_quantize_rejects(args, expect):
+    if expect == 0xFF:
+        pytest.skip("valid arguments launch a kernel")
+    assert gq.lib().gq_quantize(*args) == expect
+
+
+def test_other_entry_points_reject():
+    L = gq.lib()
+    assert L.gq_reduce_codes(NUL, 4, 100, 8, A, NUL) == 1
+    assert L.gq_reduce_codes(A, 0, 100, 8, A, NUL) == 2
+    assert L.gq_reduce_codes(A, 4, 100, 1, A, NUL) == 4
+    assert L.gq_reduce_codes(U, 4, 100, 8, A, NUL) == 6
+    assert L.gq_dequantize(A, 4, 100, 7, 0, 5, A, A, NUL) == 4
+    assert L.gq_dequantize(A, 4, 100, 7, 0, 8, NUL, A, NUL) == 1
+    assert L.gq_dequantize(A, 4, 100, 7, 0, 8, A, U, NUL) == 6
+    assert L.gq_compress_mean_from_norm(A, 0, 4, 100, 7, 0, 1, A, 8, U, NUL, NUL) == 6
+    assert L.gq_compress_mean_from_norm(A, 0, 4, 100, 7, 0, 1, A, 5, A, A, NUL) == 4
+    assert L.gq_compress_mean_from_norm(A, 0, 4, 100, 7, 0, 1, NUL, 8, A, NUL, NUL) == 1
+    ws = gq.gq_workspace_bytes(4, 100)
+    assert L.gq_compress_mean(A, 0, 4, 100, 7, 2.0, 5.0, 0, 1, 8, A, A, NUL, A, ws, NUL) == 3
+    assert L.gq_compress_mean(A, 0, 4, 100, 7, 2.0, 2.0, 0, 1, 8, A, A, NUL, A, ws - 1, NUL) == 5
+    assert L.gq_compress_mean(A, 1, 4, 100, 0, 2.0, 2.0, 0, 1, 8, A, A, NUL, A, ws, NUL) == 2
+    assert L.gq_qsgd_local_mean(A, 0, 4, 100, 3, 1, A, A, A, 2, A, ws, NUL) == 4
+    assert L.gq_qsgd_local_mean(A, 0, 4, 100, 3, 1, NUL, A, NUL, 0, A, ws, NUL) == 1
+
+
+def test_binding_fails_loudly_without_a_gpu():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(ValueError):
+        gq.gq_global_norm(torch.zeros(2, 8), 2, 2)

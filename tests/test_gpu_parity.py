@@ -1,0 +1,290 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI.
+
+Bar: integer codes and code sums bit-exact; the norm within 1e-6 relative
+(the fp64 sums are taken in different orders; the fp32 norm then agrees to
+the bit unless the exact value sits within ~1e-15 of an fp32 rounding
+boundary) and, because every code and mean depends on the norm's bits, the
+dequantized means are compared bit-exactly too.  Inputs come from the
+seeded generators of workloads.py and only the oracle computes expected
+values.
+"""
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import allreduce_compatible_gradient_amd as gq  # noqa: E402
+import oracle  # noqa: E402
+import workloads as wl  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+INF = math.inf
+SCH = {"L": oracle.SCHEME_L, "E": oracle.SCHEME_E}
+DEV = "cuda:0"
+
+
+def log(msg):
+    print(f"[gpu-parity {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gq.lib()
+
+
+def to_dev(x: np.ndarray) -> torch.Tensor:
+    if x.dtype == np.uint16:  # bf16 bit patterns
+        return torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(x).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def check_norm(gN, N):
+    gN = np.float32(gN)
+    assert abs(float(gN) - float(N)) <= 1e-6 * abs(float(N)) or gN == N, (gN, N)
+    assert gN == N, f"norm differs in the last bits: {gN!r} vs {N!r}"
+
+
+def M_of(s, scheme):
+    return s if scheme == "L" else 1 << (s - 1)
+
+
+# ---------------------------------------------------------------------------
+# Small shapes: several tiles, ragged tails, every scheme, norm and dtype
+
+SHAPES = [(1, 1), (3, 17), (4, 2048), (4, 2049), (2, 6000), (5, 4104), (7, 10007), (16, 24)]
+CASES = [("L", 7, 2.0, 2.0), ("L", 127, 2.0, INF), ("E", 8, 2.0, 2.0), ("E", 5, INF, INF),
+         ("L", 3, INF, 2.0), ("E", 12, 2.0, INF)]
+
+
+@pytest.mark.parametrize("n,d", SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("scheme,s,q,p", CASES)
+def test_fused_and_unfused_match_oracle(n, d, dtype, scheme, s, q, p):
+    seed = 1000 * n + d
+    x = wl.random_rows(n, d, seed=seed, dtype=dtype, scale=0.3)
+    W = gq.gq_min_code_bits(n, s, scheme)
+    N, sums, mean = oracle.compress_mean(x, s, q, p, SCH[scheme], seed)
+    xd = to_dev(x)
+    # fused path
+    gmean, gnorm, gsum = gq.gq_compress_mean(xd, s, q, p, scheme, seed, code_bits=W,
+                                             want_code_sum=True)
+    check_norm(host(gnorm)[0], N)
+    assert np.array_equal(host(gsum), oracle.pack(sums.astype(np.int32), W)[0])
+    assert np.array_equal(host(gmean), mean)
+    # unfused path: norm, codes, integer sum, dequantize
+    norm = gq.gq_global_norm(xd, q, p)
+    check_norm(host(norm)[0], N)
+    codes = gq.gq_quantize(xd, s, scheme, norm, seed, W)
+    ocodes = oracle.quantize(x, N, s, SCH[scheme], seed)
+    assert np.array_equal(host(codes), oracle.pack(ocodes, W))
+    # the sum and dequantization kernels take the oracle's packed codes as input
+    packed = torch.from_numpy(oracle.pack(ocodes, W)).to(DEV)
+    csum = gq.gq_reduce_codes(packed, n, d, W)
+    assert np.array_equal(host(csum), oracle.pack(sums.astype(np.int32), W)[0])
+    dmean = gq.gq_dequantize(torch.from_numpy(oracle.pack(sums.astype(np.int32), W)[0]).to(DEV),
+                             n, d, s, scheme, W, norm)
+    assert np.array_equal(host(dmean), mean)
+
+
+@pytest.mark.parametrize("scheme,s,n", [("L", 3, 4), ("E", 4, 3), ("L", 100, 2)])
+def test_every_code_width(scheme, s, n):
+    d = 5000
+    x = wl.random_rows(n, d, seed=s, scale=2.0)
+    N, sums, _ = oracle.compress_mean(x, s, 2, 2, SCH[scheme], 3)
+    ocodes = oracle.quantize(x, N, s, SCH[scheme], 3)
+    xd = to_dev(x)
+    norm = gq.gq_global_norm(xd, 2, 2)
+    for W in range(gq.gq_min_code_bits(n, s, scheme), 33):
+        codes = gq.gq_quantize(xd, s, scheme, norm, 3, W)
+        assert np.array_equal(host(codes), oracle.pack(ocodes, W)), W
+        csum = gq.gq_reduce_codes(codes, n, d, W)
+        assert np.array_equal(host(csum), oracle.pack(sums.astype(np.int32), W)[0]), W
+        _, _, fsum = gq.gq_compress_mean(xd, s, 2, 2, scheme, 3, code_bits=W, want_code_sum=True)
+        assert np.array_equal(host(fsum), host(csum)), W
+
+
+def test_worker_base_shards_reproduce_the_whole():
+    n, d, s = 6, 3000, 9
+    x = wl.random_rows(n, d, seed=5)
+    N, _ = oracle.global_norm(x, 2, 2)
+    W = gq.gq_min_code_bits(n, s, "L")
+    whole = oracle.pack(oracle.quantize(x, N, s, SCH["L"], 77), W)
+    xd = to_dev(x)
+    norm = gq.gq_global_norm(xd, 2, 2)
+    for r in range(n):  # each "rank" quantizes its own row with its global index
+        part = gq.gq_quantize(xd[r:r + 1].contiguous(), s, "L", norm, 77, W, worker_base=r)
+        assert np.array_equal(host(part)[0], whole[r])
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+
+def test_zero_input_and_empty_rows():
+    x = np.zeros((3, 4100), np.float32)
+    x[1, 7] = -0.0
+    xd = to_dev(x)
+    for scheme, s in (("L", 5), ("E", 6)):
+        W = gq.gq_min_code_bits(3, s, scheme)
+        mean, norm, csum = gq.gq_compress_mean(xd, s, 2, 2, scheme, 1, code_bits=W,
+                                               want_code_sum=True)
+        assert host(norm)[0] == 0 and not host(mean).any() and not host(csum).any()
+        codes = gq.gq_quantize(xd, s, scheme, norm, 1, W)
+        assert not host(codes).any()
+    # d == 0: the norm is 0 and nothing else is touched
+    e = torch.empty((2, 0), dtype=torch.float32, device=DEV)
+    mean, norm, _ = gq.gq_compress_mean(e, 3, 2, 2, "L", 0)
+    assert host(norm)[0] == 0 and mean.numel() == 0
+
+
+def test_subnormal_inputs_use_the_exact_prescale():
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((3, 3000)) * 1e-41).astype(np.float32)  # all subnormal
+    assert np.all(np.abs(x[x != 0]) < np.finfo(np.float32).tiny)
+    for scheme, s, q, p in (("L", 7, 2, 2), ("E", 9, INF, INF), ("L", 2, 2, INF)):
+        N, sums, mean = oracle.compress_mean(x, s, q, p, SCH[scheme], 4)
+        assert N < 2.0 ** -64
+        W = gq.gq_min_code_bits(3, s, scheme)
+        gmean, gnorm, gsum = gq.gq_compress_mean(to_dev(x), s, q, p, scheme, 4, code_bits=W,
+                                                 want_code_sum=True)
+        check_norm(host(gnorm)[0], N)
+        assert np.array_equal(host(gsum), oracle.pack(sums.astype(np.int32), W)[0])
+        assert np.array_equal(host(gmean), mean)
+
+
+def test_exact_levels_and_max_element():
+    # q = p = inf with max |x| = 8: x = k exactly gives code k (L, s = 8)
+    x = np.tile(np.arange(-8, 9, dtype=np.float32), (2, 64))
+    n, d = x.shape
+    xd = to_dev(x)
+    W = gq.gq_min_code_bits(n, 8, "L")
+    for seed in range(3):
+        mean, norm, csum = gq.gq_compress_mean(xd, 8, INF, INF, "L", seed, code_bits=W,
+                                               want_code_sum=True)
+        assert host(norm)[0] == 8.0
+        expect = (x.astype(np.int64).sum(axis=0)).astype(np.int32)
+        assert np.array_equal(host(csum), oracle.pack(expect, W)[0])
+        assert np.array_equal(host(mean), x.mean(axis=0))
+
+
+def test_non_finite_inputs_stay_on_the_grid():
+    x = wl.random_rows(4, 4096, seed=9)
+    x[0, 5] = np.nan
+    x[1, 100] = np.inf
+    x[2, 2000] = -np.inf
+    for scheme, s in (("L", 7), ("E", 6)):
+        W = gq.gq_min_code_bits(4, s, scheme)
+        xd = to_dev(x)
+        norm = gq.gq_global_norm(xd, INF, INF)
+        codes = gq.gq_quantize(xd, s, scheme, norm, 1, W)
+        c = oracle.unpack(host(codes), 4, 4096, W)
+        assert np.abs(c).max() <= M_of(s, scheme)
+
+
+def test_repeated_calls_are_bit_identical():
+    w = wl.WORKLOADS[1]
+    x = wl.generate(w)
+    xd = to_dev(x)
+    outs = [gq.gq_compress_mean(xd, w.s, w.q, w.p, w.scheme, w.seed, code_bits=8,
+                                want_code_sum=True) for _ in range(3)]
+    ref = [host(t) for t in outs[0]]
+    for o in outs[1:]:
+        for a, b in zip(ref, o):
+            assert np.array_equal(a, host(b))
+
+
+# ---------------------------------------------------------------------------
+# Local-norm QSGD ablation
+
+@pytest.mark.parametrize("n,d,dtype", [(1, 100, "f32"), (4, 4099, "f32"), (8, 16384, "bf16")])
+def test_local_qsgd_matches_oracle(n, d, dtype):
+    s = 3
+    x = wl.random_rows(n, d, seed=n + d, dtype=dtype)
+    norms, codes, mean = oracle.qsgd_local_mean(x, s, 12)
+    W = gq.gq_min_code_bits(1, s, "L")
+    gmean, gnorms, gcodes = gq.gq_qsgd_local_mean(to_dev(x), s, 12, code_bits=W, want_codes=True)
+    gn = host(gnorms)
+    for i in range(n):
+        check_norm(gn[i], norms[i])
+    assert np.array_equal(host(gcodes), oracle.pack(codes, W))
+    assert np.array_equal(host(gmean), mean)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, in the launch configuration the benchmark times:
+# the norm over every input, the code sums and means at sampled coordinates
+# (all tile boundaries near both ends plus random ones), and at every
+# coordinate the properties |sum| <= n M and mean == fp32(sum kappa).
+
+def _sample_cols(d, rng, k=20000):
+    edge = np.concatenate([np.arange(0, min(d, 4100)), np.arange(max(0, d - 4100), d)])
+    return np.unique(np.concatenate([edge, rng.integers(0, d, size=k)]))
+
+
+def _fields(buf: np.ndarray, d: int, W: int) -> np.ndarray:
+    if W in (8, 16, 32):
+        return buf.view({8: np.int8, 16: np.int16, 32: np.int32}[W])[:d].astype(np.int64)
+    return oracle.unpack(buf, 1, d, W)[0].astype(np.int64)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("key", [1, 2, 3, 4, 5])
+def test_workload_full_size(key):
+    w = wl.WORKLOADS[key]
+    threads = min(16, os.cpu_count() or 1)
+    log(f"workload {key} {w.name}: generating {w.input_bytes / 1e9:.2f} GB")
+    x = wl.generate(w, threads=threads)
+    log("oracle norm")
+    N, _ = oracle.global_norm_rows(x, w.q, w.p, threads=threads)
+    log("device copy")
+    xd = to_dev(x)
+    W = w.code_bits
+    mean_b, norm_b, _ = gq.gq_compress_mean(xd, w.s, w.q, w.p, w.scheme, w.seed)  # benchmarked call
+    mean, norm, csum = gq.gq_compress_mean(xd, w.s, w.q, w.p, w.scheme, w.seed, code_bits=W,
+                                           want_code_sum=True)
+    check_norm(host(norm)[0], N)
+    gmean = host(mean)
+    assert np.array_equal(gmean, host(mean_b))
+    sums = _fields(host(csum), w.d, W)
+    log("sampled oracle columns")
+    rng = np.random.default_rng(key)
+    cols = _sample_cols(w.d, rng)
+    osums, omean = oracle.compress_mean_cols(x, N, w.s, SCH[w.scheme], w.seed, cols)
+    assert np.array_equal(sums[cols], osums)
+    assert np.array_equal(gmean[cols], omean)
+    # properties at every coordinate
+    M = M_of(w.s, w.scheme)
+    assert np.abs(sums).max() <= w.n * M
+    kappa = float(N) / (w.n * M)
+    assert np.array_equal(gmean, (sums.astype(np.float64) * kappa).astype(np.float32))
+    if key == 2:
+        # the unfused four-call path at full size agrees with the fused one
+        codes = gq.gq_quantize(xd, w.s, w.scheme, norm, w.seed, W)
+        csum2 = gq.gq_reduce_codes(codes, w.n, w.d, W)
+        mean2 = gq.gq_dequantize(csum2, w.n, w.d, w.s, w.scheme, W, norm)
+        assert np.array_equal(host(csum2), host(csum))
+        assert np.array_equal(host(mean2), gmean)
+        del codes
+    if key == 5:
+        # the local-norm ablation at full size: norms of every row, sampled columns
+        log("local-norm ablation")
+        lmean, lnorms, _ = gq.gq_qsgd_local_mean(xd, w.s, w.seed)
+        onorms = oracle.local_norms(x, threads=threads)
+        assert np.array_equal(host(lnorms), onorms)
+        _, exp = oracle.qsgd_local_cols(x, onorms, w.s, w.seed, cols)
+        assert np.array_equal(host(lmean)[cols], exp)
+    del xd, x
+    torch.cuda.empty_cache()
+    log(f"workload {key} ok")
+

@@ -536,3 +536,20 @@ def test_local_qsgd_unbiased_monte_carlo():
     truth = x.astype(np.float64).mean(axis=0)
     se = means.std(axis=0) / math.sqrt(means.shape[0])
     assert np.all(np.abs(means.mean(axis=0) - truth) < 5 * se + 1e-7)
+
+
+def test_row_parallel_norm_equals_whole_norm():
+    x = wl.random_rows(6, 999, seed=44)
+    for q, p in [(2, 2), (2, INF), (INF, INF), (INF, 2)]:
+        a = oracle.global_norm(x, q, p)
+        b = oracle.global_norm_rows(x, q, p, threads=3)
+        assert a[0] == b[0] and np.array_equal(a[1], b[1])
+
+
+def test_local_ablation_pieces_compose():
+    x = wl.random_rows(5, 301, seed=45)
+    norms, codes, mean = oracle.qsgd_local_mean(x, 4, seed=2)
+    assert np.array_equal(oracle.local_norms(x, threads=2), norms)
+    cols = np.array([0, 17, 300, 150])
+    c2, m2 = oracle.qsgd_local_cols(x, norms, 4, 2, cols)
+    assert np.array_equal(c2, codes[:, cols]) and np.array_equal(m2, mean[cols])
