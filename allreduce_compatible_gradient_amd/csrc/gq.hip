@@ -13,17 +13,19 @@
 //   k_norm_partial   pass 1: streams x once, fp64 sum of squares (or max|x|)
 //                    per (worker, chunk) into a fixed slot -- no atomics, so
 //                    the result bits depend only on (n, d).
-//   k_norm_finalize  one block: fixed-order tree over the partials, then the
-//                    (q,p) combination, sqrt in fp64, one fp32 rounding.
+//   k_norm_finalize  one 1024-thread block: every thread loads ~8 partials
+//                    at once, fixed-order segmented tree per worker, then the
+//                    (q,p) combination over workers, sqrt in fp64, one fp32
+//                    rounding.
 //   k_compress_mean  pass 2: each thread owns 8 consecutive coordinates (one
 //                    Philox block) and walks the n workers, so the integer sum
 //                    stays in registers; 128-bit loads, one Philox4x32-10 call
 //                    per 8 coordinates (16 random bits each, a second call only
 //                    when the first 16 bits tie the threshold, p ~ 2^-16), and
-//                    the mean is written once.  Tiles are visited in reverse
-//                    of pass 1's order so the data pass 1 touched last is
-//                    re-read first, while it may still sit in the 256 MB
-//                    Infinity Cache.
+//                    the mean is written once.  One block per 2048-coordinate
+//                    tile (short-lived blocks streaming 2 KB per wave read
+//                    HBM faster than grid-stride loops on this part), tiles in
+//                    reverse of pass 1's order.
 //   k_quantize / k_reduce_codes / k_dequantize: the same steps unfused, with
 //                    W-bit codes packed through LDS into coalesced words.
 //   k_local_mean     ablation: per-worker norms (QSGD), fp64 mean.
@@ -153,6 +155,7 @@ struct QParams {
     float top;   // clamp of t: s (L) or 1 (E)
     float cE;    // 2^(1-s): the smallest non-zero E level
     float p2E;   // 2^(s+31): maps t < 2^(1-s) to the threshold scale
+    float twoE;  // 2^(s-1): integer code of the level 1
     double kappa;
     int s;
     bool zero;
@@ -170,6 +173,7 @@ __device__ __forceinline__ QParams make_qparams(float N, int64_t n, int s, int s
     q.top = (scheme == GQ_SCHEME_L) ? (float)s : 1.0f;
     q.cE = __uint_as_float((uint32_t)(128 - s) << 23);
     q.p2E = __uint_as_float((uint32_t)(158 + s) << 23);
+    q.twoE = __uint_as_float((uint32_t)(126 + s) << 23);
     const double M = (scheme == GQ_SCHEME_L) ? (double)s : (double)((int64_t)1 << (s - 1));
     q.kappa = (double)N / ((double)n * M);
     q.s = s;
@@ -186,8 +190,11 @@ __device__ __forceinline__ uint4 philox10(uint4 c, uint32_t k0, uint32_t k1)
     for (int r = 0; r < 10; ++r) {
         const uint64_t p0 = (uint64_t)c.x * 0xD2511F53u;
         const uint64_t p1 = (uint64_t)c.z * 0xCD9E8D57u;
-        c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1,
-                       (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+        // v_bitop3_b32 with truth table 0x96 is a three-input xor
+        c = make_uint4(__builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c.y, k0, 0x96),
+                       (uint32_t)p1,
+                       __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c.w, k1, 0x96),
+                       (uint32_t)p0);
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
@@ -200,71 +207,76 @@ __device__ __forceinline__ uint32_t half16(const uint4 &w, int k)
     return (k & 1) ? (word >> 16) : (word & 0xFFFFu);
 }
 
-// Deterministic half of the rounding for one coordinate: candidate
-// magnitudes (mlo, mhi) and the 32-bit threshold F (upper iff u < F).
+// Deterministic half of the rounding for one coordinate, in fp32 exactly as
+// the contract states: the lower candidate magnitude lo (an integer held
+// exactly in a float), the step to the upper one, and the 32-bit threshold
+// F (upper iff u < F).  Returns F >> 16 through Fh; F itself is only formed
+// on the rare path that needs its low half.
 template <int SCH, bool PRE>
-__device__ __forceinline__ void bracket(float v, const QParams &q, int &mlo, int &mhi, uint32_t &F)
+__device__ __forceinline__ void bracket(float v, const QParams &q, float &lo, float &step,
+                                        uint32_t &Fh, uint32_t *F_full)
 {
     float a = fabsf(v);
     if (PRE)
         a = a * q.pre;
-    float t = a * q.sigma;
     if (SCH == GQ_SCHEME_L) {
-        t = (t <= q.top) ? t : q.top; // a NaN lands on the top level
-        const float lo = floorf(t);
-        F = (uint32_t)((t - lo) * 0x1p32f);
-        mlo = (int)lo;
-        mhi = mlo + 1;
+        const float t = fminf(a * q.sigma, q.top); // v_min: a NaN lands on the top level
+        lo = floorf(t);
+        const float f = t - lo; // exact
+        step = 1.0f;
+        Fh = (uint32_t)(f * 0x1p16f); // floor(f 2^16) = F >> 16
+        if (F_full)
+            *F_full = (uint32_t)(f * 0x1p32f);
     } else {
-        t = (t <= 1.0f) ? t : 1.0f;
+        // Both cases are formed and one is selected (no divergent branch):
+        //   t >= 2^(1-s), t = 2^e (1 + phi): lower level 2^e -> code 2^(e+s-1),
+        //     step to 2^(e+1) equal to it, F = phi 2^32 (the fraction bits);
+        //   t <  2^(1-s): codes 0 or 1, F = floor(t 2^(s-1) 2^32).
+        const float t = fminf(a * q.sigma, 1.0f);
         const uint32_t tb = __float_as_uint(t);
-        if (t >= q.cE) {
-            // t = 2^e (1 + phi): lower level 2^e -> code 2^(e+s-1), threshold phi 2^32
-            mlo = 1 << ((int)(tb >> 23) - 128 + q.s);
-            mhi = (int)((uint32_t)mlo << 1); // unused when F == 0 (t = 1, s = 31)
-            F = tb << 9;
-        } else {
-            mlo = 0;
-            mhi = 1;
-            F = (uint32_t)(t * q.p2E);
-        }
+        const bool big = t >= q.cE;
+        const float lo_big = __uint_as_float(tb & 0xFF800000u) * q.twoE;
+        const float y = t * q.p2E; // exact; < 2^32 when t < 2^(1-s)
+        lo = big ? lo_big : 0.0f;
+        step = big ? lo_big : 1.0f;
+        Fh = big ? ((tb >> 7) & 0xFFFFu) : (uint32_t)(y * 0x1p-16f);
+        if (F_full)
+            *F_full = big ? (tb << 9) : (uint32_t)y;
     }
 }
 
-// Codes of one 8-coordinate group from draw 0 (high 16 bits of each
-// uniform).  Coordinates whose 16 bits equal the top half of F are marked in
-// `ties`; they took the lower level and are settled by draw 1.
+// Magnitudes of one 8-coordinate group from draw 0: the high 16 bits h of
+// each uniform decide unless h == F >> 16; such coordinates keep the lower
+// level here and `tie` is raised for the rare second draw.
 template <int SCH, bool PRE>
 __device__ __forceinline__ void quant_group(const float (&v)[kPer], const uint4 &A, const QParams &q,
-                                            int (&code)[kPer], uint32_t &ties)
+                                            float (&m)[kPer], bool &tie)
 {
-    ties = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-        int mlo, mhi;
-        uint32_t F;
-        bracket<SCH, PRE>(v[k], q, mlo, mhi, F);
+        float lo, step;
+        uint32_t Fh;
+        bracket<SCH, PRE>(v[k], q, lo, step, Fh, nullptr);
         const uint32_t h = half16(A, k);
-        const uint32_t Fh = F >> 16;
-        const int m = (h < Fh) ? mhi : mlo;
-        ties |= (uint32_t)((h == Fh) & ((F & 0xFFFFu) != 0u)) << k;
-        code[k] = (__float_as_uint(v[k]) >> 31) ? -m : m;
+        m[k] = (h < Fh) ? lo + step : lo;
+        tie |= (h == Fh);
     }
 }
 
+// The rare path: for each coordinate whose 16 bits tied, draw 1 supplies the
+// low 16 bits of its uniform; adds the step to the magnitude when the full
+// 32-bit uniform is below F.
 template <int SCH, bool PRE>
-__device__ __forceinline__ void settle_ties(const float (&v)[kPer], const uint4 &B, const QParams &q,
-                                            int (&code)[kPer], uint32_t ties)
+__device__ __forceinline__ void settle_ties(const float (&v)[kPer], const uint4 &A, const uint4 &B,
+                                            const QParams &q, float (&m)[kPer])
 {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-        if ((ties >> k) & 1u) {
-            int mlo, mhi;
-            uint32_t F;
-            bracket<SCH, PRE>(v[k], q, mlo, mhi, F);
-            if (half16(B, k) < (F & 0xFFFFu))
-                code[k] = (__float_as_uint(v[k]) >> 31) ? -mhi : mhi;
-        }
+        float lo, step;
+        uint32_t Fh, F;
+        bracket<SCH, PRE>(v[k], q, lo, step, Fh, &F);
+        if ((half16(A, k) == Fh) && (half16(B, k) < (F & 0xFFFFu)))
+            m[k] += step;
     }
 }
 
@@ -520,32 +532,78 @@ __global__ __launch_bounds__(kThreads) void k_norm_partial(const void *__restric
         partials[i * chunks + c] = r;
 }
 
-// Pass 1b: one block.  Per worker, a fixed-order reduction of its partials;
-// then the (q,p) combination.  LOCAL: per-worker norms and the per-worker
+// Pass 1b: one block of kFinThreads.  Worker i's partials are summed by a
+// segment of `seg` consecutive threads (a power of two, seg * workers per
+// pass = kFinThreads); each thread adds its partials c = lane, lane + seg,
+// ... in order, eight loads in flight, then the segment reduces with a fixed
+// butterfly (and, for segments wider than a wave, the wave results in
+// order through LDS).  The per-worker values are then combined over workers
+// by a block-wide fixed tree.  LOCAL: per-worker norms and the per-worker
 // scalars of the local-norm ablation instead of one global norm.
-template <bool QINF, bool PINF, bool LOCAL>
-__global__ __launch_bounds__(kThreads) void k_norm_finalize(const double *__restrict__ partials,
-                                                            int64_t n, int64_t chunks,
-                                                            double *__restrict__ per_worker,
-                                                            float *__restrict__ norm_out, int s,
-                                                            WorkerParams *__restrict__ params)
+constexpr int kFinThreads = 1024;
+
+template <bool MAX>
+__device__ __forceinline__ double combine(double a, double b) { return MAX ? fmax(a, b) : a + b; }
+
+template <bool MAX>
+__device__ __forceinline__ double butterfly(double v, int width)
 {
-    __shared__ double red[4];
-    for (int64_t i = 0; i < n; ++i) {
+    for (int off = width >> 1; off > 0; off >>= 1)
+        v = combine<MAX>(v, __shfl_xor(v, off));
+    return v;
+}
+
+template <bool QINF, bool PINF, bool LOCAL>
+__global__ __launch_bounds__(kFinThreads) void k_norm_finalize(const double *__restrict__ partials,
+                                                               int64_t n, int64_t chunks,
+                                                               double *__restrict__ per_worker,
+                                                               float *__restrict__ norm_out, int s,
+                                                               WorkerParams *__restrict__ params)
+{
+    __shared__ double red[kFinThreads / 64];
+    const int t = threadIdx.x, lane64 = t & 63, wave = t >> 6;
+    int seg = kFinThreads;
+    while (seg > 1 && (int64_t)seg * n > kFinThreads)
+        seg >>= 1;
+    const int rows_per_pass = kFinThreads / seg;
+    for (int64_t r0 = 0; r0 < n; r0 += rows_per_pass) {
+        const int64_t i = r0 + t / seg;
+        const int lane = t % seg;
         double acc = 0.0;
-        for (int64_t c = threadIdx.x; c < chunks; c += kThreads) {
-            const double v = partials[i * chunks + c];
-            acc = QINF ? fmax(acc, v) : acc + v;
+        if (i < n) {
+            const double *p = partials + i * chunks;
+            int64_t c = lane;
+            for (; c + 7 * (int64_t)seg < chunks; c += 8 * (int64_t)seg) {
+                double v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    v[u] = p[c + u * (int64_t)seg];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    acc = combine<QINF>(acc, v[u]);
+            }
+            for (; c < chunks; c += seg)
+                acc = combine<QINF>(acc, p[c]);
         }
-        const double r = block_reduce<QINF>(acc, red);
-        if (threadIdx.x == 0)
-            per_worker[i] = r;
+        acc = butterfly<QINF>(acc, seg < 64 ? seg : 64);
+        if (seg > 64) {
+            if (lane64 == 0)
+                red[wave] = acc;
+            __syncthreads();
+            if (lane == 0) {
+                double r = red[wave];
+                for (int w = 1; w < seg / 64; ++w)
+                    r = combine<QINF>(r, red[wave + w]);
+                acc = r;
+            }
+            __syncthreads();
+        }
+        if (lane == 0 && i < n)
+            per_worker[i] = acc;
     }
     __syncthreads();
-    if (threadIdx.x != 0)
-        return;
     if (LOCAL) {
-        for (int64_t i = 0; i < n; ++i) {
+        for (int64_t i = t; i < n; i += kFinThreads) {
             const float Ni = (float)sqrt(per_worker[i]);
             norm_out[i] = Ni;
             const float pre = (Ni < 0x1p-64f) ? 0x1p64f : 1.0f;
@@ -557,44 +615,61 @@ __global__ __launch_bounds__(kThreads) void k_norm_finalize(const double *__rest
         }
         return;
     }
-    double tot = 0.0;
-    for (int64_t i = 0; i < n; ++i) {
+    // combine over workers: strided in-order partial per thread, then a fixed tree
+    double acc = 0.0;
+    for (int64_t i = t; i < n; i += kFinThreads) {
         const double w = per_worker[i];
-        if (PINF)
-            tot = fmax(tot, w);
-        else
-            tot += QINF ? w * w : w;
+        acc = combine<PINF>(acc, (QINF && !PINF) ? w * w : w);
     }
-    norm_out[0] = (QINF && PINF) ? (float)tot : (float)sqrt(tot);
+    acc = butterfly<PINF>(acc, 64);
+    if (lane64 == 0)
+        red[wave] = acc;
+    __syncthreads();
+    if (t == 0) {
+        double tot = red[0];
+        for (int w = 1; w < kFinThreads / 64; ++w)
+            tot = combine<PINF>(tot, red[w]);
+        norm_out[0] = (QINF && PINF) ? (float)tot : (float)sqrt(tot);
+    }
 }
 
 // ---------------------------------------------------------------------------
 // Pass 2, fused: quantize + exact integer sum over workers + dequantize.
 
-template <int DT, int SCH, bool PRE>
+// Walk the n workers for one 8-coordinate group, adding the signed codes.
+// FACC: the sum is kept in fp32, exact because every partial sum is an
+// integer of magnitude <= n M <= 2^24; the sign is applied by an fma with
+// +-1.  Otherwise int32.  (Prefetching the next worker's inputs into
+// registers was measured to give nothing for fp32 and to cost 3% for bf16.)
+template <int DT, int SCH, bool PRE, bool FACC>
 __device__ __forceinline__ void accumulate_workers(const void *__restrict__ x, int64_t n, int64_t d,
                                                    int64_t j0, bool vec, const QParams &q,
-                                                   uint32_t k0, uint32_t k1, int (&acc)[kPer])
+                                                   uint32_t k0, uint32_t k1, float (&accf)[kPer],
+                                                   int (&acci)[kPer])
 {
     const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
     for (int64_t i = 0; i < n; ++i) {
         float v[kPer];
         load_group<DT>(x, i * d, j0, d, vec, v);
         const uint4 A = philox10(make_uint4(blo, bhi, (uint32_t)i, 0u), k0, k1);
-        int code[kPer];
-        uint32_t ties;
-        quant_group<SCH, PRE>(v, A, q, code, ties);
-        if (ties) {
+        float m[kPer];
+        bool tie = false;
+        quant_group<SCH, PRE>(v, A, q, m, tie);
+        if (tie) {
             const uint4 B = philox10(make_uint4(blo, bhi, (uint32_t)i, 1u), k0, k1);
-            settle_ties<SCH, PRE>(v, B, q, code, ties);
+            settle_ties<SCH, PRE>(v, A, B, q, m);
         }
 #pragma unroll
-        for (int k = 0; k < kPer; ++k)
-            acc[k] += code[k];
+        for (int k = 0; k < kPer; ++k) {
+            if (FACC)
+                accf[k] = fmaf(copysignf(1.0f, v[k]), m[k], accf[k]);
+            else
+                acci[k] += (int)copysignf(m[k], v[k]);
+        }
     }
 }
 
-template <int DT, int SCH>
+template <int DT, int SCH, bool FACC>
 __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restrict__ x, int64_t n,
                                                             int64_t d, int s, uint64_t seed,
                                                             const float *__restrict__ norm_dev,
@@ -602,17 +677,26 @@ __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restri
                                                             uint8_t *__restrict__ code_sum, int W)
 {
     __shared__ uint32_t lds[kTile];
-    const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x; // reverse of pass 1
+    // Reverse of pass 1's order: pass 1's blocks finish on the last chunks of
+    // every row, so starting pass 2 there re-reads data the memory-side cache
+    // still holds (measured: -7% time on an 0.8 GB input, neutral on 7-16 GB).
+    const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;
     const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
     const QParams q = make_qparams(*norm_dev, n, s, SCH);
+    float accf[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
     int acc[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (!q.zero && j0 < d) {
         const bool vec = (d & 7) == 0;
         const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
         if (q.prescale)
-            accumulate_workers<DT, SCH, true>(x, n, d, j0, vec, q, k0, k1, acc);
+            accumulate_workers<DT, SCH, true, FACC>(x, n, d, j0, vec, q, k0, k1, accf, acc);
         else
-            accumulate_workers<DT, SCH, false>(x, n, d, j0, vec, q, k0, k1, acc);
+            accumulate_workers<DT, SCH, false, FACC>(x, n, d, j0, vec, q, k0, k1, accf, acc);
+        if (FACC) {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+                acc[k] = (int)accf[k];
+        }
     }
     if (j0 < d) {
         float m[kPer];
@@ -654,18 +738,22 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void *__restrict__ 
         const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
         const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
         const uint4 A = philox10(make_uint4(blo, bhi, (uint32_t)wk, 0u), k0, k1);
-        uint32_t ties;
+        float m[kPer];
+        bool tie = false;
         if (q.prescale)
-            quant_group<SCH, true>(v, A, q, code, ties);
+            quant_group<SCH, true>(v, A, q, m, tie);
         else
-            quant_group<SCH, false>(v, A, q, code, ties);
-        if (ties) {
+            quant_group<SCH, false>(v, A, q, m, tie);
+        if (tie) {
             const uint4 B = philox10(make_uint4(blo, bhi, (uint32_t)wk, 1u), k0, k1);
             if (q.prescale)
-                settle_ties<SCH, true>(v, B, q, code, ties);
+                settle_ties<SCH, true>(v, A, B, q, m);
             else
-                settle_ties<SCH, false>(v, B, q, code, ties);
+                settle_ties<SCH, false>(v, A, B, q, m);
         }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            code[k] = (int)copysignf(m[k], v[k]);
     }
     store_tile_packed(lds, code, W, codes + i * rbytes, tile, rbytes);
 }
@@ -724,7 +812,7 @@ __global__ __launch_bounds__(kThreads) void k_local_mean(const void *__restrict_
                                                          int64_t rbytes)
 {
     __shared__ uint32_t lds[kTile];
-    const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;
+    const int64_t tile = blockIdx.x;
     const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
     const bool vec = (d & 7) == 0;
     const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
@@ -742,22 +830,25 @@ __global__ __launch_bounds__(kThreads) void k_local_mean(const void *__restrict_
             float v[kPer];
             load_group<DT>(x, i * d, j0, d, vec, v);
             const uint4 A = philox10(make_uint4(blo, bhi, (uint32_t)i, 0u), k0, k1);
-            uint32_t ties;
+            float m[kPer];
+            bool tie = false;
             const bool pre = wp.pre != 1.0f;
             if (pre)
-                quant_group<GQ_SCHEME_L, true>(v, A, q, code, ties);
+                quant_group<GQ_SCHEME_L, true>(v, A, q, m, tie);
             else
-                quant_group<GQ_SCHEME_L, false>(v, A, q, code, ties);
-            if (ties) {
+                quant_group<GQ_SCHEME_L, false>(v, A, q, m, tie);
+            if (tie) {
                 const uint4 B = philox10(make_uint4(blo, bhi, (uint32_t)i, 1u), k0, k1);
                 if (pre)
-                    settle_ties<GQ_SCHEME_L, true>(v, B, q, code, ties);
+                    settle_ties<GQ_SCHEME_L, true>(v, A, B, q, m);
                 else
-                    settle_ties<GQ_SCHEME_L, false>(v, B, q, code, ties);
+                    settle_ties<GQ_SCHEME_L, false>(v, A, B, q, m);
             }
 #pragma unroll
-            for (int k = 0; k < kPer; ++k)
+            for (int k = 0; k < kPer; ++k) {
+                code[k] = (int)copysignf(m[k], v[k]);
                 acc[k] = acc[k] + (double)code[k] * wp.kappa;
+            }
         }
         if (codes)
             store_tile_packed(lds, code, W, codes + i * rbytes, tile, rbytes);
@@ -865,7 +956,7 @@ int32_t launch_norm(const void *x, int32_t dtype, int64_t n, int64_t d, bool qin
         }
         GQ_TRY(check_launch("k_norm_partial"));
     }
-    const dim3 one(1), block(kThreads);
+    const dim3 one(1), block(kFinThreads);
     if (local)
         k_norm_finalize<false, false, true><<<one, block, 0, st>>>(partials, n, g.chunks, per_worker, norm_out, s, params);
     else if (qinf && pinf)
@@ -888,17 +979,23 @@ int32_t launch_compress(const void *x, int32_t dtype, int64_t n, int64_t d, int3
         return ok();
     const dim3 grid((unsigned)tiles), block(kThreads);
     uint8_t *cs = (uint8_t *)code_sum;
-    if (dtype == GQ_IN_F32) {
-        if (scheme == GQ_SCHEME_L)
-            k_compress_mean<GQ_IN_F32, GQ_SCHEME_L><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, mean, cs, W);
-        else
-            k_compress_mean<GQ_IN_F32, GQ_SCHEME_E><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, mean, cs, W);
-    } else {
-        if (scheme == GQ_SCHEME_L)
-            k_compress_mean<GQ_IN_BF16, GQ_SCHEME_L><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, mean, cs, W);
-        else
-            k_compress_mean<GQ_IN_BF16, GQ_SCHEME_E><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, mean, cs, W);
-    }
+    // fp32 accumulation is exact while every partial sum stays within 2^24
+    const bool facc = n * top_code(s, scheme) <= ((int64_t)1 << 24);
+#define GQ_COMPRESS(DT, SCH, FA) \
+    k_compress_mean<DT, SCH, FA><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, mean, cs, W)
+#define GQ_COMPRESS_DT(DT)                                                        \
+    do {                                                                          \
+        if (scheme == GQ_SCHEME_L)                                                \
+            facc ? GQ_COMPRESS(DT, GQ_SCHEME_L, true) : GQ_COMPRESS(DT, GQ_SCHEME_L, false); \
+        else                                                                      \
+            facc ? GQ_COMPRESS(DT, GQ_SCHEME_E, true) : GQ_COMPRESS(DT, GQ_SCHEME_E, false); \
+    } while (0)
+    if (dtype == GQ_IN_F32)
+        GQ_COMPRESS_DT(GQ_IN_F32);
+    else
+        GQ_COMPRESS_DT(GQ_IN_BF16);
+#undef GQ_COMPRESS_DT
+#undef GQ_COMPRESS
     return check_launch("k_compress_mean");
 }
 

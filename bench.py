@@ -71,7 +71,7 @@ def cpu_baseline(w, target_s: float):
     import oracle
     import workloads as wl
     scheme = oracle.SCHEME_L if w.scheme == "L" else oracle.SCHEME_E
-    d0 = 1 << 12
+    d0 = min(w.d, 1 << 16)
     x = wl.generate(w, d=d0)
     t0 = time.perf_counter()
     oracle.compress_mean(x, w.s, w.q, w.p, scheme, w.seed)

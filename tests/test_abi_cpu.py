@@ -82,7 +82,6 @@ def test_global_norm_rejects(args, expect):
 
 
 @pytest.mark.parametrize("args,expect", [
-    ((A, 0, 4, 100, 7, 0, A, 1, 0, 8, A, NUL), 0xFF),     # valid: not called (sentinel)
     ((A, 0, 4, 100, 0, 0, A, 1, 0, 8, A, NUL), 2),        # s = 0
     ((A, 0, 4, 100, 7, 2, A, 1, 0, 8, A, NUL), 2),        # scheme 2
     ((A, 0, 4, 100, 32, 1, A, 1, 0, 32, A, NUL), 2),      # E with s = 32
@@ -96,8 +95,6 @@ def test_global_norm_rejects(args, expect):
     ((A, 0, 4, 100, 7, 0, A, 1, (1 << 32) - 2, 8, A, NUL), 2),  # workers past 2^32
 ])
 def test_quantize_rejects(args, expect):
-    if expect == 0xFF:
-        pytest.skip("valid arguments launch a kernel")
     assert gq.lib().gq_quantize(*args) == expect
 
 
