@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
     ap.add_argument("--unfused", action="store_true", help="also time the four-call unfused path")
+    ap.add_argument("--ablation", action="store_true",
+                    help="also time local-norm QSGD on the same input (default on workload 5)")
     return ap.parse_args()
 
 
@@ -85,6 +87,52 @@ def cpu_baseline(w, target_s: float):
     return {"value": round(gbs, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first {d1} of {w.d} coordinates of all {w.n} workers "
                       f"({w.n * d1} elements, {dt:.1f} s)"}
+
+
+def ablation(gq, torch, w, xd, stream, steps, global_ms, gmean, gnorm, ws):
+    """Global-L_s against per-worker local-norm QSGD on the same input: time,
+    bits sent per element, and the relative error of the dequantized mean."""
+    n, d = w.n, w.d
+    lmean = torch.empty(d, dtype=torch.float32, device=xd.device)
+    norms = torch.empty(n, dtype=torch.float32, device=xd.device)
+
+    def lstep():
+        gq.gq_qsgd_local_mean(xd, w.s, w.seed, mean=lmean, norms=norms, workspace=ws,
+                              stream=stream)
+    for _ in range(3):
+        lstep()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        lstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    lms = e0.elapsed_time(e1) / steps
+    # accuracy against the exact mean (fp64 reference; a reporting aid, not the path)
+    gq.gq_compress_mean(xd, w.s, w.q, w.p, w.scheme, w.seed, mean=gmean, norm=gnorm,
+                        workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    ref = torch.zeros(d, dtype=torch.float64, device=xd.device)
+    for i in range(n):
+        ref += xd[i].double()
+    ref /= n
+    den = float((ref * ref).sum())
+
+    def rel(m):
+        return float(((m.double() - ref) ** 2).sum()) / den
+    in_bytes = n * d * w.elem_bytes
+    wl_bits = gq.gq_min_code_bits(1, w.s, "L")  # per-worker local codes: [-s, s]
+    return {
+        "global": {"ms_per_step": round(global_ms, 6),
+                   "input_GBs": round(in_bytes / (global_ms * 1e-3) / 1e9, 3),
+                   "code_bits": w.code_bits, "bits_per_element": w.code_bits,
+                   "rel_sq_error_of_mean": rel(gmean), "allreduce_compatible": True},
+        "local_qsgd": {"ms_per_step": round(lms, 6),
+                       "input_GBs": round(in_bytes / (lms * 1e-3) / 1e9, 3),
+                       "code_bits": wl_bits, "bits_per_element": wl_bits + 32.0 / d,
+                       "rel_sq_error_of_mean": rel(lmean), "allreduce_compatible": False},
+    }
 
 
 def main():
@@ -215,6 +263,8 @@ def main():
         ums = e0.elapsed_time(e1) / args.steps
         out["unfused"] = {"ms_per_step": round(ums, 6),
                           "input_GBs": round(in_bytes / (ums * 1e-3) / 1e9, 3)}
+    if args.ablation or w.key == 5:
+        out["ablation"] = ablation(gq, torch, w, xd, stream, args.steps, ms, mean, norm, ws)
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -82,6 +82,18 @@ def lib():
         L.oracle_compress_mean.argtypes = [_vp, _int, _i64, _i64, _int, _f32, _f32, _int, _u64,
                                            _vp, _vp]
         L.oracle_compress_mean.restype = _f32
+        L.oracle_uniform32_ctr.argtypes = [_u64, ctypes.c_uint32, ctypes.c_uint32, _u64]
+        L.oracle_uniform32_ctr.restype = ctypes.c_uint32
+        L.oracle_e8_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e8_value.restype = ctypes.c_double
+        L.oracle_e8_round.argtypes = [ctypes.c_double, ctypes.c_uint32]
+        L.oracle_e8_round.restype = ctypes.c_uint8
+        L.oracle_e8_quantize.argtypes = [_vp, _int, _i64, _i64, _f32, _u64, _i64, _vp]
+        L.oracle_e8_reduce_pair.argtypes = [_vp, _vp, _i64, _u64, ctypes.c_uint32, ctypes.c_uint32,
+                                            _vp]
+        L.oracle_e8_tree.argtypes = [_vp, _i64, _i64, _u64, _vp, _vp]
+        L.oracle_e8_tree.restype = _int
+        L.oracle_e8_dequantize.argtypes = [_vp, _i64, _f32, _vp]
         L.oracle_local_norms.argtypes = [_vp, _int, _i64, _i64, _vp]
         L.oracle_qsgd_local_cols.argtypes = [_vp, _int, _i64, _i64, _int, _u64, _vp, _vp, _i64,
                                              _vp, _vp]
@@ -329,3 +341,60 @@ def qsgd_local_cols(x: np.ndarray, norms: np.ndarray, s: int, seed: int, cols):
     lib().oracle_qsgd_local_cols(_ptr(x), _x_dtype(x), n, d, s, seed, _ptr(norms), _ptr(cols),
                                  cols.size, _ptr(codes), _ptr(mean))
     return codes, mean
+
+
+# ---------------------------------------------------------------------------
+# The pages' 8-bit exponential-dithering wire format and its tree reduction
+
+
+def uniform32_ctr(seed: int, c2: int, c3pair: int, j: int) -> int:
+    return int(lib().oracle_uniform32_ctr(seed, c2, c3pair, j))
+
+
+def e8_value(c: int) -> float:
+    return float(lib().oracle_e8_value(c))
+
+
+def e8_round(v: float, u: int) -> int:
+    return int(lib().oracle_e8_round(float(v), u))
+
+
+def e8_quantize(x: np.ndarray, N, seed: int, worker_base: int = 0) -> np.ndarray:
+    x = _rows(x)
+    n, d = x.shape
+    codes = np.zeros((n, d), dtype=np.uint8)
+    lib().oracle_e8_quantize(_ptr(x), _x_dtype(x), n, d, float(N), seed, worker_base, _ptr(codes))
+    return codes
+
+
+def e8_reduce_pair(a: np.ndarray, b: np.ndarray, seed: int, level: int, node: int) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    out = np.zeros(a.size, dtype=np.uint8)
+    lib().oracle_e8_reduce_pair(_ptr(a), _ptr(b), a.size, seed, level, node, _ptr(out))
+    return out
+
+
+def e8_tree(codes: np.ndarray, seed: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    n, d = codes.shape
+    root = np.zeros(d, dtype=np.uint8)
+    scratch = np.zeros(n * d, dtype=np.uint8)
+    if lib().oracle_e8_tree(_ptr(codes), n, d, seed, _ptr(root), _ptr(scratch)) != 0:
+        raise ValueError("the tree needs a power-of-two number of rows")
+    return root
+
+
+def e8_dequantize(root: np.ndarray, N) -> np.ndarray:
+    root = np.ascontiguousarray(root, dtype=np.uint8)
+    mean = np.zeros(root.size, dtype=np.float32)
+    lib().oracle_e8_dequantize(_ptr(root), root.size, float(N), _ptr(mean))
+    return mean
+
+
+def e8_compress_mean(x: np.ndarray, q, p, seed: int):
+    """Norm, 8-bit codes, tree reduction with re-rounding, dequantization: (N, root, mean)."""
+    N, _ = global_norm(x, q, p)
+    codes = e8_quantize(x, N, seed)
+    root = e8_tree(codes, seed)
+    return N, root, e8_dequantize(root, N)

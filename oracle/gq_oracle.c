@@ -459,3 +459,134 @@ void oracle_qsgd_local_mean(const void *x, int dtype, int64_t n, int64_t d, int 
     oracle_qsgd_local_cols(x, dtype, n, d, s, seed, norms, cols, d, codes_or_null, mean);
     free(cols);
 }
+
+/* ------------------------------------------------------------------------ */
+/* The pages' own wire format for exponential dithering (Sec. 4 worked
+ * example, Sec. 6 custom reduction): 8-bit codes, bit 7 the sign, bits 0..6
+ * a level index.  Index 0 is the level 0; index k in [1, 127] is the level
+ * 2^(1-k), so the levels are {0} and 2^-m for m = 0..126 (s = 127).
+ * A tree Allreduce combines two children into their average, rounded again
+ * at random, without bias, onto the same grid ("extra variance due to
+ * stochastic rounding during AllReduce").  Readings: the average (not the
+ * sum) keeps every node inside [-1, 1]; the pair is added in fp64; n is a
+ * power of two; the draws of tree level l >= 1, node m use Philox counter
+ * words (lo32(j/8), hi32(j/8), m, 2 l + draw), so level 0 is the
+ * quantization layout above.                                               */
+
+/* Uniform of element j from counter words 2 and 3 = (c2, 2 c3pair + draw). */
+uint32_t oracle_uniform32_ctr(uint64_t seed, uint32_t c2, uint32_t c3pair, uint64_t j)
+{
+    uint64_t b = j / 8;
+    unsigned e = (unsigned)(j % 8);
+    uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
+    uint32_t ca[4] = {(uint32_t)(b & 0xFFFFFFFFu), (uint32_t)(b >> 32), c2, 2u * c3pair};
+    uint32_t cb[4] = {(uint32_t)(b & 0xFFFFFFFFu), (uint32_t)(b >> 32), c2, 2u * c3pair + 1u};
+    uint32_t A[4], B[4];
+    oracle_philox4x32_10(ca, key, A);
+    oracle_philox4x32_10(cb, key, B);
+    unsigned shift = 16u * (e % 2u);
+    return (((A[e / 2] >> shift) & 0xFFFFu) << 16) | ((B[e / 2] >> shift) & 0xFFFFu);
+}
+
+/* Value of a code in units of the global norm.                             */
+double oracle_e8_value(uint8_t c)
+{
+    int idx = c & 0x7F;
+    if (idx == 0)
+        return 0.0;
+    double v = ldexp(1.0, 1 - idx);
+    return (c & 0x80) ? -v : v;
+}
+
+/* Round r = |v| <= 1 (fp64) at random onto the grid, sign from v: the upper
+ * neighbour with probability F / 2^32.
+ *   r >= 2^-126, r = 2^e (1 + phi): neighbours 2^e and 2^(e+1),
+ *     F = floor(phi 2^32) (the top 32 of phi's 52 fraction bits);
+ *   0 < r < 2^-126: neighbours 0 and 2^-126, F = floor(r 2^126 2^32).      */
+uint8_t oracle_e8_round(double v, uint32_t u)
+{
+    double r = fabs(v);
+    if (!(r <= 1.0))
+        r = 1.0; /* clamp; NaN lands on the top level */
+    if (r == 0.0)
+        return 0;
+    uint8_t sign = (v < 0.0) ? 0x80 : 0x00;
+    if (r >= 0x1p-126) {
+        int e;
+        double m = frexp(r, &e); /* r = m 2^e, m in [0.5, 1) */
+        e -= 1;                  /* r = 2^e (1 + phi), phi = 2 m - 1 */
+        double phi = 2.0 * m - 1.0;
+        uint32_t F = (uint32_t)(phi * 0x1p32);
+        int up = u < F;
+        int idx = 1 - (e + up); /* level 2^(e+up) */
+        return (uint8_t)(sign | idx);
+    }
+    uint32_t F = (uint32_t)((r * 0x1p126) * 0x1p32);
+    return (uint8_t)(u < F ? (sign | 127) : 0);
+}
+
+/* Quantize n rows to 8-bit codes given the norm (Global-E_s, s = 127):
+ * t = min(fp32(|x| pre sigma), 1) with sigma = fp32(1 / (N pre)), then the
+ * random rounding above with the level-0 uniforms of worker worker_base + i. */
+void oracle_e8_quantize(const void *x, int dtype, int64_t n, int64_t d, float N, uint64_t seed,
+                        int64_t worker_base, uint8_t *codes)
+{
+    float pre, sigma;
+    double kappa;
+    oracle_scale_params(N, n, 127, ORACLE_SCHEME_E, &pre, &sigma, &kappa);
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j < d; ++j) {
+            uint64_t g = (uint64_t)(i * d + j);
+            if (N == 0.0f) {
+                codes[g] = 0;
+                continue;
+            }
+            float xv = load_x(x, dtype, g);
+            float t = (fabsf(xv) * pre) * sigma;
+            if (!(t <= 1.0f))
+                t = 1.0f;
+            uint32_t u = oracle_uniform32_ctr(seed, (uint32_t)(worker_base + i), 0, (uint64_t)j);
+            uint8_t c = oracle_e8_round((double)t, u);
+            if ((float_bits(xv) >> 31) && c)
+                c |= 0x80;
+            else
+                c &= 0x7F;
+            codes[g] = c;
+        }
+}
+
+/* The custom reduction of two code vectors at tree level `level`, node `node`. */
+void oracle_e8_reduce_pair(const uint8_t *a, const uint8_t *b, int64_t d, uint64_t seed,
+                           uint32_t level, uint32_t node, uint8_t *out)
+{
+    for (int64_t j = 0; j < d; ++j) {
+        double v = 0.5 * (oracle_e8_value(a[j]) + oracle_e8_value(b[j]));
+        out[j] = oracle_e8_round(v, oracle_uniform32_ctr(seed, node, level, (uint64_t)j));
+    }
+}
+
+/* The whole tree over n = 2^L rows of codes (row-major [n][d]): level l
+ * combines nodes 2m and 2m+1 of level l-1 into node m.  scratch: n*d bytes. */
+int oracle_e8_tree(const uint8_t *codes, int64_t n, int64_t d, uint64_t seed, uint8_t *root,
+                   uint8_t *scratch)
+{
+    if (n < 1 || (n & (n - 1)) != 0)
+        return -1;
+    memcpy(scratch, codes, (size_t)(n * d));
+    int64_t nodes = n;
+    for (uint32_t level = 1; nodes > 1; ++level) {
+        for (int64_t m = 0; m < nodes / 2; ++m)
+            oracle_e8_reduce_pair(scratch + (2 * m) * d, scratch + (2 * m + 1) * d, d, seed, level,
+                                  (uint32_t)m, scratch + m * d);
+        nodes /= 2;
+    }
+    memcpy(root, scratch, (size_t)d);
+    return 0;
+}
+
+/* Dequantize the root: mean_j = fp32(N value_j) (fp64 product).            */
+void oracle_e8_dequantize(const uint8_t *root, int64_t d, float N, float *mean)
+{
+    for (int64_t j = 0; j < d; ++j)
+        mean[j] = (float)((double)N * oracle_e8_value(root[j]));
+}
