@@ -44,6 +44,13 @@ SIGNATURES = {
                                 _vp, _vp, _vp, _i64, _vp]),
     "gq_qsgd_local_mean": (_i32, [_vp, _i32, _i64, _i64, _i32, _u64, _vp, _vp, _vp, _i32, _vp,
                                   _i64, _vp]),
+    "gq_e8_row_bytes": (_i64, [_i64]),
+    "gq_e8_quantize": (_i32, [_vp, _i32, _i64, _i64, _vp, _u64, _i64, _vp, _vp]),
+    "gq_e8_reduce_pair": (_i32, [_vp, _vp, _i64, _u64, _i32, _i64, _vp, _vp]),
+    "gq_e8_tree": (_i32, [_vp, _i64, _i64, _u64, _vp, _vp]),
+    "gq_e8_dequantize": (_i32, [_vp, _i64, _vp, _vp, _vp]),
+    "gq_e8_compress_mean": (_i32, [_vp, _i32, _i64, _i64, _f32, _f32, _u64, _vp, _vp, _vp, _vp,
+                                   _i64, _vp]),
     "gq_status_str": (ctypes.c_char_p, [_i32]),
     "gq_last_error": (ctypes.c_char_p, []),
 }
@@ -236,3 +243,63 @@ def gq_qsgd_local_mean(x: torch.Tensor, s: int, seed: int, *, code_bits: int = 0
                                     _ptr(codes), code_bits, _ptr(ws), ws.numel(),
                                     _stream(stream)))
     return mean, norms, codes
+
+
+# ---------------------------------------------------------------------------
+# the pages' 8-bit exponential-dithering format and its re-rounding tree
+
+def gq_e8_row_bytes(d: int) -> int:
+    return int(lib().gq_e8_row_bytes(d))
+
+
+def gq_e8_quantize(x: torch.Tensor, norm: torch.Tensor, seed: int, *, worker_base: int = 0,
+                   codes=None, stream=None):
+    """8-bit codes, uint8 [n, gq_e8_row_bytes(d)]."""
+    dt = _input(x)
+    n, d = x.shape
+    if codes is None:
+        codes = torch.empty((n, gq_e8_row_bytes(d)), dtype=torch.uint8, device=x.device)
+    _check(lib().gq_e8_quantize(_ptr(x), dt, n, d, _ptr(norm), seed, worker_base, _ptr(codes),
+                                _stream(stream)))
+    return codes
+
+
+def gq_e8_reduce_pair(a: torch.Tensor, b: torch.Tensor, d: int, seed: int, level: int, node: int,
+                      *, out=None, stream=None):
+    if out is None:
+        out = torch.empty(gq_e8_row_bytes(d), dtype=torch.uint8, device=a.device)
+    _check(lib().gq_e8_reduce_pair(_ptr(a), _ptr(b), d, seed, level, node, _ptr(out),
+                                   _stream(stream)))
+    return out
+
+
+def gq_e8_tree(codes: torch.Tensor, n: int, d: int, seed: int, *, root=None, stream=None):
+    if root is None:
+        root = torch.empty(gq_e8_row_bytes(d), dtype=torch.uint8, device=codes.device)
+    _check(lib().gq_e8_tree(_ptr(codes), n, d, seed, _ptr(root), _stream(stream)))
+    return root
+
+
+def gq_e8_dequantize(root: torch.Tensor, d: int, norm: torch.Tensor, *, mean=None, stream=None):
+    if mean is None:
+        mean = torch.empty(d, dtype=torch.float32, device=root.device)
+    _check(lib().gq_e8_dequantize(_ptr(root), d, _ptr(norm), _ptr(mean), _stream(stream)))
+    return mean
+
+
+def gq_e8_compress_mean(x: torch.Tensor, q, p, seed: int, *, want_root: bool = False, mean=None,
+                        norm=None, root=None, workspace=None, stream=None):
+    """Norm + 8-bit codes + re-rounding tree + dequantization: (mean, norm, root or None)."""
+    dt = _input(x)
+    n, d = x.shape
+    if mean is None:
+        mean = torch.empty(d, dtype=torch.float32, device=x.device)
+    if norm is None:
+        norm = torch.empty(1, dtype=torch.float32, device=x.device)
+    if want_root and root is None:
+        root = torch.empty(gq_e8_row_bytes(d), dtype=torch.uint8, device=x.device)
+    ws = _workspace(workspace, n, d, x.device)
+    _check(lib().gq_e8_compress_mean(_ptr(x), dt, n, d, _order(q), _order(p), seed, _ptr(mean),
+                                     _ptr(norm), _ptr(root), _ptr(ws), ws.numel(),
+                                     _stream(stream)))
+    return mean, norm, root

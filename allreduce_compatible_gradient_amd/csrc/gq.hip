@@ -174,7 +174,7 @@ __device__ __forceinline__ QParams make_qparams(float N, int64_t n, int s, int s
     q.cE = __uint_as_float((uint32_t)(128 - s) << 23);
     q.p2E = __uint_as_float((uint32_t)(158 + s) << 23);
     q.twoE = __uint_as_float((uint32_t)(126 + s) << 23);
-    const double M = (scheme == GQ_SCHEME_L) ? (double)s : (double)((int64_t)1 << (s - 1));
+    const double M = (scheme == GQ_SCHEME_L) ? (double)s : ldexp(1.0, s - 1);
     q.kappa = (double)N / ((double)n * M);
     q.s = s;
     return q;
@@ -862,6 +862,299 @@ __global__ __launch_bounds__(kThreads) void k_local_mean(const void *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// The pages' own 8-bit exponential-dithering wire format and its re-rounding
+// tree reduction.  Code byte: bit 7 sign, bits 0..6 level index k; k = 0 is
+// the level 0, k >= 1 the level 2^(1-k) (s = 127).  A tree node is the
+// average of its two children, added in fp64 and rounded again at random,
+// without bias, onto the same grid; the draws of tree level l at node m use
+// Philox counter words (lo32(j/8), hi32(j/8), m, 2 l + draw), level 0 being
+// the quantization.  n is a power of two up to kE8MaxN.
+
+constexpr int kE8MaxLevels = 10;
+constexpr int64_t kE8MaxN = (int64_t)1 << kE8MaxLevels;
+
+__device__ __forceinline__ double e8_value(uint32_t c)
+{
+    const uint32_t idx = c & 0x7Fu;
+    const uint64_t bits = ((uint64_t)(c & 0x80u) << 56) | ((uint64_t)(1024u - idx) << 52);
+    return idx ? __longlong_as_double((long long)bits) : 0.0;
+}
+
+// Neighbouring codes of v (|v| <= 1) on the grid and the threshold F
+// (upper iff u < F): r = 2^e (1 + phi) >= 2^-126 gives 2^e / 2^(e+1) and the
+// top 32 fraction bits of phi; 0 < r < 2^-126 gives 0 / 2^-126 and
+// floor(r 2^126 2^32).
+__device__ __forceinline__ void e8_bracket(double v, uint32_t &lo, uint32_t &hi, uint32_t &F)
+{
+    const uint32_t sign = (uint32_t)((uint64_t)__double_as_longlong(v) >> 56) & 0x80u;
+    const double r = fmin(fabs(v), 1.0);
+    const uint64_t rb = (uint64_t)__double_as_longlong(r);
+    const uint32_t ef = (uint32_t)(rb >> 52); // biased exponent, e = ef - 1023
+    if (r >= 0x1p-126) {
+        F = (uint32_t)(rb >> 20);
+        lo = sign | (1024u - ef);
+        hi = sign | (1023u - ef);
+    } else {
+        F = (uint32_t)((r * 0x1p126) * 0x1p32);
+        lo = 0u;
+        hi = (r == 0.0) ? 0u : (sign | 127u);
+    }
+}
+
+// Quantization to 8-bit codes: Global-E_s with s = 127 in the byte format.
+// t = min(fp32(|x| pre sigma), 1), sigma = fp32(1 / (N pre)).
+template <bool PRE>
+__device__ __forceinline__ void e8_quant_bracket(float xv, const QParams &q, uint32_t &lo,
+                                                 uint32_t &hi, uint32_t &F)
+{
+    float a = fabsf(xv);
+    if (PRE)
+        a = a * q.pre;
+    const float t = fminf(a * q.sigma, 1.0f);
+    const uint32_t tb = __float_as_uint(t);
+    const uint32_t sign = __float_as_uint(xv) & 0x80000000u ? 0x80u : 0u;
+    if (tb >= 0x00800000u) {
+        F = tb << 9;
+        lo = sign | (128u - (tb >> 23));
+        hi = sign | (127u - (tb >> 23));
+    } else {
+        F = (uint32_t)((t * 0x1p126f) * 0x1p32f);
+        lo = 0u;
+        hi = sign | 127u;
+    }
+}
+
+__device__ __forceinline__ uint32_t byte_of(const uint2 &w, int k)
+{
+    return ((k < 4 ? w.x : w.y) >> (8 * (k & 3))) & 0xFFu;
+}
+
+__device__ __forceinline__ uint2 pack_bytes(const uint32_t (&c)[kPer])
+{
+    return make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
+                      c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+}
+
+// Draw-0 decision for 8 codes with the lazy draw-1 settlement.
+template <typename BracketFn>
+__device__ __forceinline__ void e8_decide(BracketFn bracket_k, uint32_t blo, uint32_t bhi,
+                                          uint32_t c2, uint32_t c3pair, uint32_t k0, uint32_t k1,
+                                          uint32_t (&out)[kPer])
+{
+    const uint4 A = philox10(make_uint4(blo, bhi, c2, 2u * c3pair), k0, k1);
+    bool tie = false;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        uint32_t lo, hi, F;
+        bracket_k(k, lo, hi, F);
+        const uint32_t h = half16(A, k), Fh = F >> 16;
+        out[k] = (h < Fh) ? hi : lo;
+        tie |= (h == Fh);
+    }
+    if (tie) {
+        const uint4 B = philox10(make_uint4(blo, bhi, c2, 2u * c3pair + 1u), k0, k1);
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            uint32_t lo, hi, F;
+            bracket_k(k, lo, hi, F);
+            if (half16(A, k) == (F >> 16) && half16(B, k) < (F & 0xFFFFu))
+                out[k] = hi;
+        }
+    }
+}
+
+// One custom reduction of 8 coordinates: codes a (left child) and b (right).
+__device__ __forceinline__ uint2 e8_combine(const uint2 &a, const uint2 &b, uint32_t blo,
+                                            uint32_t bhi, uint32_t node, uint32_t level,
+                                            uint32_t k0, uint32_t k1)
+{
+    double v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        v[k] = 0.5 * (e8_value(byte_of(a, k)) + e8_value(byte_of(b, k)));
+    uint32_t c[kPer];
+    e8_decide([&](int k, uint32_t &lo, uint32_t &hi, uint32_t &F) { e8_bracket(v[k], lo, hi, F); },
+              blo, bhi, node, level, k0, k1, c);
+    return pack_bytes(c);
+}
+
+// Binary-counter tree: leaf i enters; while bit l of i is set, it is combined
+// with the stored left sibling at level l into their parent (level l + 1,
+// node i >> (l + 1)).  The same pairs as the level-by-level tree.
+__device__ __forceinline__ uint2 e8_push(uint2 (&st)[kE8MaxLevels + 1], uint2 cur, int64_t i,
+                                         uint32_t blo, uint32_t bhi, uint32_t k0, uint32_t k1)
+{
+    // constant trip count (no early exit) so the stack stays in registers;
+    // i is wave-uniform, so every branch here is uniform
+    bool carrying = true;
+#pragma unroll
+    for (int l = 0; l <= kE8MaxLevels; ++l) {
+        if (carrying) {
+            if ((i >> l) & 1) {
+                cur = e8_combine(st[l], cur, blo, bhi, (uint32_t)(i >> (l + 1)), (uint32_t)(l + 1),
+                                 k0, k1);
+            } else {
+                st[l] = cur;
+                carrying = false;
+            }
+        }
+    }
+    return cur;
+}
+
+__device__ __forceinline__ uint2 load_codes8(const uint8_t *row, int64_t j0, int64_t d)
+{
+    if (j0 + kPer <= d)
+        return *(const uint2 *)(row + j0);
+    uint32_t c[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        c[k] = (j0 + k < d) ? row[j0 + k] : 0u;
+    return pack_bytes(c);
+}
+
+__device__ __forceinline__ void store_codes8(uint8_t *row, int64_t j0, int64_t d, const uint2 &w)
+{
+    if (j0 + kPer <= d) {
+        *(uint2 *)(row + j0) = w;
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        if (j0 + k < d)
+            row[j0 + k] = (uint8_t)byte_of(w, k);
+}
+
+template <int DT, bool PRE>
+__device__ __forceinline__ uint2 e8_quant8(const void *__restrict__ x, int64_t row_off, int64_t j0,
+                                           int64_t d, bool vec, const QParams &q, uint32_t worker,
+                                           uint32_t blo, uint32_t bhi, uint32_t k0, uint32_t k1)
+{
+    float v[kPer];
+    load_group<DT>(x, row_off, j0, d, vec, v);
+    uint32_t c[kPer];
+    e8_decide([&](int k, uint32_t &lo, uint32_t &hi, uint32_t &F) { e8_quant_bracket<PRE>(v[k], q, lo, hi, F); },
+              blo, bhi, worker, 0u, k0, k1, c);
+    return pack_bytes(c);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_e8_quantize(const void *__restrict__ x, int64_t n,
+                                                          int64_t d, uint64_t seed,
+                                                          int64_t worker_base,
+                                                          const float *__restrict__ norm_dev,
+                                                          uint8_t *__restrict__ codes,
+                                                          int64_t rbytes, int64_t tiles)
+{
+    const int64_t i = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
+    if (j0 >= d)
+        return;
+    const QParams q = make_qparams(*norm_dev, n, 127, GQ_SCHEME_E);
+    uint2 w = make_uint2(0, 0);
+    if (!q.zero) {
+        const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
+        const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+        const bool vec = (d & 7) == 0;
+        const uint32_t wk = (uint32_t)(worker_base + i);
+        w = q.prescale ? e8_quant8<DT, true>(x, i * d, j0, d, vec, q, wk, blo, bhi, k0, k1)
+                       : e8_quant8<DT, false>(x, i * d, j0, d, vec, q, wk, blo, bhi, k0, k1);
+    }
+    store_codes8(codes + i * rbytes, j0, d, w);
+}
+
+__global__ __launch_bounds__(kThreads) void k_e8_pair(const uint8_t *__restrict__ a,
+                                                      const uint8_t *__restrict__ b, int64_t d,
+                                                      uint64_t seed, uint32_t level, uint32_t node,
+                                                      uint8_t *__restrict__ out)
+{
+    const int64_t j0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
+    if (j0 >= d)
+        return;
+    const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
+    const uint2 r = e8_combine(load_codes8(a, j0, d), load_codes8(b, j0, d), blo, bhi, node, level,
+                               (uint32_t)seed, (uint32_t)(seed >> 32));
+    store_codes8(out, j0, d, r);
+}
+
+__global__ __launch_bounds__(kThreads) void k_e8_tree(const uint8_t *__restrict__ codes, int64_t n,
+                                                      int64_t d, int64_t rbytes, uint64_t seed,
+                                                      uint8_t *__restrict__ root)
+{
+    const int64_t j0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
+    if (j0 >= d)
+        return;
+    const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    uint2 st[kE8MaxLevels + 1];
+    uint2 cur = make_uint2(0, 0);
+    for (int64_t i = 0; i < n; ++i)
+        cur = e8_push(st, load_codes8(codes + i * rbytes, j0, d), i, blo, bhi, k0, k1);
+    store_codes8(root, j0, d, cur);
+}
+
+__global__ __launch_bounds__(kThreads) void k_e8_dequantize(const uint8_t *__restrict__ root,
+                                                            int64_t d,
+                                                            const float *__restrict__ norm_dev,
+                                                            float *__restrict__ mean)
+{
+    const int64_t j0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
+    if (j0 >= d)
+        return;
+    const double N = (double)*norm_dev;
+    const uint2 w = load_codes8(root, j0, d);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        if (j0 + k < d)
+            mean[j0 + k] = (float)(N * e8_value(byte_of(w, k)));
+}
+
+// Fused: quantize the n workers' coordinates, reduce them through the tree in
+// registers, dequantize the root.  Tiles in reverse of pass 1's order.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_e8_compress_mean(const void *__restrict__ x, int64_t n,
+                                                               int64_t d, uint64_t seed,
+                                                               const float *__restrict__ norm_dev,
+                                                               float *__restrict__ mean,
+                                                               uint8_t *__restrict__ root)
+{
+    const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;
+    const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
+    if (j0 >= d)
+        return;
+    const float N = *norm_dev;
+    const QParams q = make_qparams(N, n, 127, GQ_SCHEME_E);
+    uint2 cur = make_uint2(0, 0);
+    if (!q.zero) {
+        const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
+        const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+        const bool vec = (d & 7) == 0;
+        uint2 st[kE8MaxLevels + 1];
+        for (int64_t i = 0; i < n; ++i) {
+            const uint2 leaf = q.prescale
+                ? e8_quant8<DT, true>(x, i * d, j0, d, vec, q, (uint32_t)i, blo, bhi, k0, k1)
+                : e8_quant8<DT, false>(x, i * d, j0, d, vec, q, (uint32_t)i, blo, bhi, k0, k1);
+            cur = e8_push(st, leaf, i, blo, bhi, k0, k1);
+        }
+    }
+    if (root)
+        store_codes8(root, j0, d, cur);
+    float m[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        m[k] = (float)((double)N * e8_value(byte_of(cur, k)));
+    if ((d & 7) == 0) {
+        *(float4 *)(mean + j0) = make_float4(m[0], m[1], m[2], m[3]);
+        *(float4 *)(mean + j0 + 4) = make_float4(m[4], m[5], m[6], m[7]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            if (j0 + k < d)
+                mean[j0 + k] = m[k];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launch helpers
 
 int32_t check_launch(const char *what)
@@ -1214,6 +1507,131 @@ int32_t gq_qsgd_local_mean(const void *x, int32_t dtype, int64_t n, int64_t d, i
     else
         k_local_mean<GQ_IN_BF16><<<grid, block, 0, st>>>(x, n, d, s, seed, norms_dev, params, mean, (uint8_t *)codes_or_null, code_bits, rb);
     return check_launch("k_local_mean");
+}
+
+int64_t gq_e8_row_bytes(int64_t d)
+{
+    if (d < 0 || d > INT64_MAX - 16)
+        return -1;
+    return ((d + 15) / 16) * 16;
+}
+
+static int32_t e8_check_n(int64_t n)
+{
+    if (n < 1 || n > kE8MaxN || (n & (n - 1)) != 0)
+        return fail(GQ_ERR_UNSUPPORTED, "the tree needs n a power of two in [1, %lld], got %lld",
+                    (long long)kE8MaxN, (long long)n);
+    return GQ_OK;
+}
+
+int32_t gq_e8_quantize(const void *x, int32_t dtype, int64_t n, int64_t d, const float *norm_dev,
+                       uint64_t seed, int64_t worker_base, void *codes, void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    if (!norm_dev || (!codes && d > 0))
+        return fail(GQ_ERR_NULL, "norm_dev or codes is NULL");
+    if (worker_base < 0 || worker_base + n > ((int64_t)1 << 32))
+        return fail(GQ_ERR_ARG, "worker indices must lie in [0, 2^32)");
+    if (!aligned16(codes))
+        return fail(GQ_ERR_ALIGN, "codes is not 16-byte aligned");
+    const int64_t tiles = (d + kTile - 1) / kTile;
+    if (tiles == 0)
+        return ok();
+    if (tiles * n > kMaxGrid)
+        return fail(GQ_ERR_UNSUPPORTED, "n * tiles exceeds the launch limit");
+    const dim3 grid((unsigned)(tiles * n)), block(kThreads);
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t rb = gq_e8_row_bytes(d);
+    if (dtype == GQ_IN_F32)
+        k_e8_quantize<GQ_IN_F32><<<grid, block, 0, st>>>(x, n, d, seed, worker_base, norm_dev, (uint8_t *)codes, rb, tiles);
+    else
+        k_e8_quantize<GQ_IN_BF16><<<grid, block, 0, st>>>(x, n, d, seed, worker_base, norm_dev, (uint8_t *)codes, rb, tiles);
+    return check_launch("k_e8_quantize");
+}
+
+int32_t gq_e8_reduce_pair(const void *a, const void *b, int64_t d, uint64_t seed, int32_t level,
+                          int64_t node, void *out, void *stream)
+{
+    if (d < 0)
+        return fail(GQ_ERR_ARG, "d is negative");
+    if ((!a || !b || !out) && d > 0)
+        return fail(GQ_ERR_NULL, "a, b or out is NULL");
+    if (level < 1 || level > 0x7FFFFFFF / 2 || node < 0 || node > 0xFFFFFFFFll)
+        return fail(GQ_ERR_ARG, "level must be >= 1 and node in [0, 2^32)");
+    if (!aligned16(a) || !aligned16(b) || !aligned16(out))
+        return fail(GQ_ERR_ALIGN, "a, b or out is not 16-byte aligned");
+    const int64_t blocks = (d + kTile - 1) / kTile;
+    if (blocks == 0)
+        return ok();
+    if (blocks > kMaxGrid)
+        return fail(GQ_ERR_UNSUPPORTED, "d exceeds the launch limit");
+    k_e8_pair<<<dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream>>>(
+        (const uint8_t *)a, (const uint8_t *)b, d, seed, (uint32_t)level, (uint32_t)node, (uint8_t *)out);
+    return check_launch("k_e8_pair");
+}
+
+int32_t gq_e8_tree(const void *codes, int64_t n, int64_t d, uint64_t seed, void *root, void *stream)
+{
+    GQ_TRY(e8_check_n(n));
+    if (d < 0)
+        return fail(GQ_ERR_ARG, "d is negative");
+    if ((!codes || !root) && d > 0)
+        return fail(GQ_ERR_NULL, "codes or root is NULL");
+    if (!aligned16(codes) || !aligned16(root))
+        return fail(GQ_ERR_ALIGN, "codes or root is not 16-byte aligned");
+    const int64_t blocks = (d + kTile - 1) / kTile;
+    if (blocks == 0)
+        return ok();
+    if (blocks > kMaxGrid)
+        return fail(GQ_ERR_UNSUPPORTED, "d exceeds the launch limit");
+    k_e8_tree<<<dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream>>>(
+        (const uint8_t *)codes, n, d, gq_e8_row_bytes(d), seed, (uint8_t *)root);
+    return check_launch("k_e8_tree");
+}
+
+int32_t gq_e8_dequantize(const void *root, int64_t d, const float *norm_dev, float *mean,
+                         void *stream)
+{
+    if (d < 0)
+        return fail(GQ_ERR_ARG, "d is negative");
+    if (!norm_dev || ((!root || !mean) && d > 0))
+        return fail(GQ_ERR_NULL, "root, norm_dev or mean is NULL");
+    if (!aligned16(root) || !aligned16(mean))
+        return fail(GQ_ERR_ALIGN, "root or mean is not 16-byte aligned");
+    const int64_t blocks = (d + kTile - 1) / kTile;
+    if (blocks == 0)
+        return ok();
+    if (blocks > kMaxGrid)
+        return fail(GQ_ERR_UNSUPPORTED, "d exceeds the launch limit");
+    k_e8_dequantize<<<dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream>>>(
+        (const uint8_t *)root, d, norm_dev, mean);
+    return check_launch("k_e8_dequantize");
+}
+
+int32_t gq_e8_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, float q, float p,
+                            uint64_t seed, float *mean, float *norm_dev, void *root_or_null,
+                            void *workspace, int64_t workspace_bytes, void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    GQ_TRY(e8_check_n(n));
+    if (!norm_dev || (!mean && d > 0))
+        return fail(GQ_ERR_NULL, "norm_dev or mean is NULL");
+    if (!order_ok(q) || !order_ok(p))
+        return fail(GQ_ERR_UNSUPPORTED, "q and p must be 2 or +inf");
+    if (!aligned16(mean) || !aligned16(root_or_null))
+        return fail(GQ_ERR_ALIGN, "mean or root is not 16-byte aligned");
+    GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
+    hipStream_t st = (hipStream_t)stream;
+    GQ_TRY(launch_norm(x, dtype, n, d, isinf(q), isinf(p), false, norm_dev, workspace, 0, st));
+    const int64_t tiles = (d + kTile - 1) / kTile;
+    if (tiles == 0)
+        return ok();
+    const dim3 grid((unsigned)tiles), block(kThreads);
+    if (dtype == GQ_IN_F32)
+        k_e8_compress_mean<GQ_IN_F32><<<grid, block, 0, st>>>(x, n, d, seed, norm_dev, mean, (uint8_t *)root_or_null);
+    else
+        k_e8_compress_mean<GQ_IN_BF16><<<grid, block, 0, st>>>(x, n, d, seed, norm_dev, mean, (uint8_t *)root_or_null);
+    return check_launch("k_e8_compress_mean");
 }
 
 } // extern "C"

@@ -16,6 +16,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -38,6 +39,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
     ap.add_argument("--unfused", action="store_true", help="also time the four-call unfused path")
+    ap.add_argument("--e8", action="store_true",
+                    help="also measure the 8-bit exponential format: its pair reduction against "
+                         "fp32/uint8 sums (omega) and the fused tree path on this workload")
     ap.add_argument("--ablation", action="store_true",
                     help="also time local-norm QSGD on the same input (default on workload 5)")
     return ap.parse_args()
@@ -87,6 +91,67 @@ def cpu_baseline(w, target_s: float):
     return {"value": round(gbs, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first {d1} of {w.d} coordinates of all {w.n} workers "
                       f"({w.n * d1} elements, {dt:.1f} s)"}
+
+
+def eq8_threshold(rho: float, omega: float) -> float:
+    """Largest beta / gamma at which the compressed Allreduce is faster.
+
+    Reading of Eq. (8) of "Global-QSGD: Practical Floatless Quantization ..."
+    (Sec. 5 performance model, delta = 0): with rho = S / S_hat and omega =
+    gamma_hat / gamma (byte rates of the custom and the fp32 reduction),
+    compression pays iff (1/gamma)(1/(rho omega) - 1) < (2/beta)(1 - 1/rho).
+    Returns inf when it always pays (rho omega >= 1)."""
+    lhs = 1.0 / (rho * omega) - 1.0
+    return math.inf if lhs <= 0 else 2.0 * (1.0 - 1.0 / rho) / lhs
+
+
+def _time_us(torch, stream, fn, reps):
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def e8_report(gq, torch, w, xd, stream, steps, ws):
+    """The 8-bit exponential format: omega of its custom pair reduction, and
+    the fused norm + codes + re-rounding tree + dequantization path."""
+    out = {}
+    g = torch.Generator(device="cpu").manual_seed(0)
+    for label, nbytes in (("25MB", 25 << 20), ("1GB", 1 << 30)):
+        d = nbytes // 4  # elements of an fp32 buffer of that size
+        a = torch.randn(d, generator=g).to(xd.device)
+        b = torch.randn(d, generator=g).to(xd.device)
+        c = torch.empty_like(a)
+        t_f32 = _time_us(torch, stream, lambda: torch.add(a, b, out=c), 50)
+        au = torch.randint(0, 256, (d,), dtype=torch.uint8, generator=g).to(xd.device)
+        bu = torch.randint(0, 256, (d,), dtype=torch.uint8, generator=g).to(xd.device)
+        cu = torch.empty_like(au)
+        t_u8 = _time_us(torch, stream, lambda: torch.add(au, bu, out=cu), 50)
+        t_e8 = _time_us(torch, stream, lambda: gq.gq_e8_reduce_pair(au, bu, d, 1, 1, 0, out=cu,
+                                                                    stream=stream), 50)
+        del a, b, c
+        # byte rates: the fp32 sum reduces 4d bytes, the code sums d bytes
+        om_e, om_s = (d / t_e8) / (4 * d / t_f32), (d / t_u8) / (4 * d / t_f32)
+        out[label] = {"elements": d, "fp32_sum_us": round(t_f32, 3), "u8_sum_us": round(t_u8, 3),
+                      "e8_pair_reduce_us": round(t_e8, 3), "omega_E": round(om_e, 4),
+                      "omega_S": round(om_s, 4),
+                      "eq8_beta_over_gamma_E": eq8_threshold(4.0, om_e)}
+    n, d = w.n, w.d
+    if n & (n - 1) == 0:
+        mean = torch.empty(d, dtype=torch.float32, device=xd.device)
+        norm = torch.empty(1, dtype=torch.float32, device=xd.device)
+        t = _time_us(torch, stream, lambda: gq.gq_e8_compress_mean(
+            xd, w.q, w.p, w.seed, mean=mean, norm=norm, workspace=ws, stream=stream), steps)
+        out["fused"] = {"ms_per_step": round(t * 1e-3, 6),
+                        "input_GBs": round(n * d * w.elem_bytes / (t * 1e-6) / 1e9, 3),
+                        "bits_per_element": 8}
+    return out
 
 
 def ablation(gq, torch, w, xd, stream, steps, global_ms, gmean, gnorm, ws):
@@ -263,6 +328,8 @@ def main():
         ums = e0.elapsed_time(e1) / args.steps
         out["unfused"] = {"ms_per_step": round(ums, 6),
                           "input_GBs": round(in_bytes / (ums * 1e-3) / 1e9, 3)}
+    if args.e8:
+        out["e8"] = e8_report(gq, torch, w, xd, stream, min(args.steps, 50), ws)
     if args.ablation or w.key == 5:
         out["ablation"] = ablation(gq, torch, w, xd, stream, args.steps, ms, mean, norm, ws)
     if args.cpu_seconds > 0:

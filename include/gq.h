@@ -157,6 +157,49 @@ int32_t gq_qsgd_local_mean(const void *x, int32_t dtype, int64_t n, int64_t d, i
                            int32_t code_bits, void *workspace, int64_t workspace_bytes,
                            void *stream);
 
+/* ---- The 8-bit exponential-dithering wire format (next to the path) ----
+ * The pages' own format for exponential dithering ("Global-QSGD: Practical
+ * Floatless Quantization ...", Sec. 4 worked example: 1 sign bit and 7
+ * level bits; Sec. 6: custom reduction inside the tree Allreduce).
+ * Code byte: bit 7 sign, bits 0..6 level index k; k = 0 is the level 0,
+ * k >= 1 the level 2^(1-k) (levels 2^-m, m = 0..126: Global-E_s, s = 127).
+ * Codes are not summable: a tree node is the average of its two children,
+ * added in fp64 and rounded again at random, without bias, onto the same
+ * grid (neighbours 2^e / 2^(e+1) with F = the top 32 fraction bits of the
+ * fp64 value, or 0 / 2^-126 below 2^-126).  The draws of tree level l >= 1
+ * at node m use Philox counter words (lo32(j/8), hi32(j/8), m, 2 l + draw);
+ * level 0 is the quantization, with the layout given above.  Trees need n a
+ * power of two up to 1024.  Code rows are gq_e8_row_bytes(d) bytes apart;
+ * the pad bytes after the d codes of a row are never written.             */
+
+/* 16 * ceil(d / 16), or -1 for d < 0.                                      */
+int64_t gq_e8_row_bytes(int64_t d);
+
+/* Quantize n rows to 8-bit codes given N in norm_dev[0] (Global-E_s with
+ * s = 127: sigma = fp32(1 / (N pre)), t = min(fp32(|x| pre sigma), 1)).     */
+int32_t gq_e8_quantize(const void *x, int32_t dtype, int64_t n, int64_t d, const float *norm_dev,
+                       uint64_t seed, int64_t worker_base, void *codes, void *stream);
+
+/* The custom reduction of one tree step: out = round((a + b) / 2) with the
+ * draws of (level, node); level >= 1.                                      */
+int32_t gq_e8_reduce_pair(const void *a, const void *b, int64_t d, uint64_t seed, int32_t level,
+                          int64_t node, void *out, void *stream);
+
+/* The whole tree over n rows of codes: level l combines nodes 2m and 2m+1
+ * of level l-1 into node m; root: one row of d codes.                      */
+int32_t gq_e8_tree(const void *codes, int64_t n, int64_t d, uint64_t seed, void *root,
+                   void *stream);
+
+/* mean[j] = fp32(N value(root[j])), product in fp64.                        */
+int32_t gq_e8_dequantize(const void *root, int64_t d, const float *norm_dev, float *mean,
+                         void *stream);
+
+/* Norm, quantization, tree and dequantization in one call (the tree runs in
+ * registers, no codes are materialized); root_or_null receives the root.   */
+int32_t gq_e8_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, float q, float p,
+                            uint64_t seed, float *mean, float *norm_dev, void *root_or_null,
+                            void *workspace, int64_t workspace_bytes, void *stream);
+
 /* Name of a status code (static string).                                  */
 const char *gq_status_str(int32_t status);
 

@@ -94,6 +94,8 @@ def lib():
         L.oracle_e8_tree.argtypes = [_vp, _i64, _i64, _u64, _vp, _vp]
         L.oracle_e8_tree.restype = _int
         L.oracle_e8_dequantize.argtypes = [_vp, _i64, _f32, _vp]
+        L.oracle_e8_compress_cols.argtypes = [_vp, _int, _i64, _i64, _f32, _u64, _vp, _i64, _vp,
+                                              _vp]
         L.oracle_local_norms.argtypes = [_vp, _int, _i64, _i64, _vp]
         L.oracle_qsgd_local_cols.argtypes = [_vp, _int, _i64, _i64, _int, _u64, _vp, _vp, _i64,
                                              _vp, _vp]
@@ -398,3 +400,19 @@ def e8_compress_mean(x: np.ndarray, q, p, seed: int):
     codes = e8_quantize(x, N, seed)
     root = e8_tree(codes, seed)
     return N, root, e8_dequantize(root, N)
+
+
+def e8_compress_cols(x: np.ndarray, N, seed: int, cols):
+    """Listed coordinates of the 8-bit pipeline given the norm (n a power of two): (root, mean)."""
+    x = _rows(x)
+    n, d = x.shape
+    if n & (n - 1):
+        raise ValueError("the tree needs a power-of-two number of rows")
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if cols.size and (cols.min() < 0 or cols.max() >= d):
+        raise IndexError("column out of range")
+    root = np.zeros(cols.size, dtype=np.uint8)
+    mean = np.zeros(cols.size, dtype=np.float32)
+    lib().oracle_e8_compress_cols(_ptr(x), _x_dtype(x), n, d, float(N), seed, _ptr(cols), cols.size,
+                                  _ptr(root), _ptr(mean))
+    return root, mean

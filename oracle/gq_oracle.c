@@ -525,9 +525,24 @@ uint8_t oracle_e8_round(double v, uint32_t u)
     return (uint8_t)(u < F ? (sign | 127) : 0);
 }
 
-/* Quantize n rows to 8-bit codes given the norm (Global-E_s, s = 127):
- * t = min(fp32(|x| pre sigma), 1) with sigma = fp32(1 / (N pre)), then the
- * random rounding above with the level-0 uniforms of worker worker_base + i. */
+/* One 8-bit code of the quantization (Global-E_s, s = 127): t =
+ * min(fp32(|x| pre sigma), 1) with sigma = fp32(1 / (N pre)), the random
+ * rounding above, then the sign bit of x on a non-zero code.              */
+static uint8_t e8_code(float xv, float N, float pre, float sigma, uint32_t u)
+{
+    if (N == 0.0f)
+        return 0;
+    float t = (fabsf(xv) * pre) * sigma;
+    if (!(t <= 1.0f))
+        t = 1.0f;
+    uint8_t c = oracle_e8_round((double)t, u);
+    if ((float_bits(xv) >> 31) && c)
+        return (uint8_t)(c | 0x80);
+    return (uint8_t)(c & 0x7F);
+}
+
+/* Quantize n rows to 8-bit codes given the norm, with the level-0 uniforms
+ * of worker worker_base + i.                                               */
 void oracle_e8_quantize(const void *x, int dtype, int64_t n, int64_t d, float N, uint64_t seed,
                         int64_t worker_base, uint8_t *codes)
 {
@@ -537,21 +552,8 @@ void oracle_e8_quantize(const void *x, int dtype, int64_t n, int64_t d, float N,
     for (int64_t i = 0; i < n; ++i)
         for (int64_t j = 0; j < d; ++j) {
             uint64_t g = (uint64_t)(i * d + j);
-            if (N == 0.0f) {
-                codes[g] = 0;
-                continue;
-            }
-            float xv = load_x(x, dtype, g);
-            float t = (fabsf(xv) * pre) * sigma;
-            if (!(t <= 1.0f))
-                t = 1.0f;
             uint32_t u = oracle_uniform32_ctr(seed, (uint32_t)(worker_base + i), 0, (uint64_t)j);
-            uint8_t c = oracle_e8_round((double)t, u);
-            if ((float_bits(xv) >> 31) && c)
-                c |= 0x80;
-            else
-                c &= 0x7F;
-            codes[g] = c;
+            codes[g] = e8_code(load_x(x, dtype, g), N, pre, sigma, u);
         }
 }
 
@@ -589,4 +591,35 @@ void oracle_e8_dequantize(const uint8_t *root, int64_t d, float N, float *mean)
 {
     for (int64_t j = 0; j < d; ++j)
         mean[j] = (float)((double)N * oracle_e8_value(root[j]));
+}
+
+/* Listed coordinates of the whole 8-bit pipeline given the norm: for each
+ * coordinate j, the n codes, the tree over them, the root and its mean.     */
+void oracle_e8_compress_cols(const void *x, int dtype, int64_t n, int64_t d, float N,
+                             uint64_t seed, const int64_t *cols, int64_t ncols, uint8_t *root,
+                             float *mean)
+{
+    float pre, sigma;
+    double kappa;
+    oracle_scale_params(N, n, 127, ORACLE_SCHEME_E, &pre, &sigma, &kappa);
+    uint8_t *node = (uint8_t *)malloc((size_t)n);
+    if (!node)
+        return;
+    for (int64_t c = 0; c < ncols; ++c) {
+        int64_t j = cols[c];
+        for (int64_t i = 0; i < n; ++i)
+            node[i] = e8_code(load_x(x, dtype, (uint64_t)(i * d + j)), N, pre, sigma,
+                              oracle_uniform32_ctr(seed, (uint32_t)i, 0, (uint64_t)j));
+        int64_t nodes = n;
+        for (uint32_t level = 1; nodes > 1; ++level) {
+            for (int64_t m = 0; m < nodes / 2; ++m) {
+                double v = 0.5 * (oracle_e8_value(node[2 * m]) + oracle_e8_value(node[2 * m + 1]));
+                node[m] = oracle_e8_round(v, oracle_uniform32_ctr(seed, (uint32_t)m, level, (uint64_t)j));
+            }
+            nodes /= 2;
+        }
+        root[c] = node[0];
+        mean[c] = (float)((double)N * oracle_e8_value(node[0]));
+    }
+    free(node);
 }

@@ -1,0 +1,151 @@
+"""GPU parity of the 8-bit exponential-dithering wire format and its
+re-rounding tree reduction, through the C ABI, against the CPU oracle.
+
+Every output here is integer (code bytes) or decided by them (the mean is
+fp32(N * a power of two)), so the bar is bit-exact, with the norm first
+checked within 1e-6 relative and to the bit (its fp64 sums run in another
+order on the GPU).
+"""
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import allreduce_compatible_gradient_amd as gq  # noqa: E402
+import oracle  # noqa: E402
+import workloads as wl  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+INF = math.inf
+DEV = "cuda:0"
+
+
+def log(msg):
+    print(f"[gpu-e8 {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gq.lib()
+
+
+def to_dev(x):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def check_norm(gN, N):
+    assert abs(float(gN) - float(N)) <= 1e-6 * abs(float(N)), (gN, N)
+    assert np.float32(gN) == N
+
+
+def rows(codes_dev, n, d):
+    return host(codes_dev).reshape(n, -1)[:, :d]
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("d", [1, 17, 2048, 2049, 5003])
+@pytest.mark.parametrize("dtype,q,p", [("f32", 2.0, 2.0), ("bf16", 2.0, INF), ("f32", INF, INF)])
+def test_e8_pipeline_matches_oracle(n, d, dtype, q, p):
+    seed = 31 * n + d
+    x = wl.random_rows(n, d, seed=seed, dtype=dtype, scale=0.2)
+    N, root, mean = oracle.e8_compress_mean(x, q, p, seed)
+    xd = to_dev(x)
+    gmean, gnorm, groot = gq.gq_e8_compress_mean(xd, q, p, seed, want_root=True)
+    check_norm(host(gnorm)[0], N)
+    assert np.array_equal(host(groot)[:d], root)
+    assert np.array_equal(host(gmean), mean)
+    # unfused: quantize, tree, dequantize; the tree and pair kernels take the
+    # oracle's codes as input
+    codes = oracle.e8_quantize(x, N, seed)
+    gcodes = gq.gq_e8_quantize(xd, gnorm, seed)
+    assert np.array_equal(rows(gcodes, n, d), codes)
+    rb = gq.gq_e8_row_bytes(d)
+    padded = np.zeros((n, rb), np.uint8)
+    padded[:, :d] = codes
+    troot = gq.gq_e8_tree(torch.from_numpy(padded).to(DEV), n, d, seed)
+    assert np.array_equal(host(troot)[:d], root)
+    rp = np.zeros(rb, np.uint8)
+    rp[:d] = root
+    assert np.array_equal(host(gq.gq_e8_dequantize(torch.from_numpy(rp).to(DEV), d, gnorm)), mean)
+
+
+@pytest.mark.parametrize("level,node", [(1, 0), (3, 5), (7, 1 << 20)])
+def test_pair_reduction_matches_oracle(level, node):
+    d = 10007
+    rng = np.random.default_rng(level)
+    a = rng.integers(0, 256, size=d).astype(np.uint8)
+    b = rng.integers(0, 256, size=d).astype(np.uint8)
+    b[::7] = a[::7] ^ 0x80  # exact cancellations
+    b[::11] = a[::11]       # equal pairs
+    b[5::13] = 0x7F         # the smallest level
+    a[5::13] = 0x7F
+    exp = oracle.e8_reduce_pair(a, b, 99, level, node)
+    rb = gq.gq_e8_row_bytes(d)
+    pa, pb = np.zeros(rb, np.uint8), np.zeros(rb, np.uint8)
+    pa[:d], pb[:d] = a, b
+    out = gq.gq_e8_reduce_pair(torch.from_numpy(pa).to(DEV), torch.from_numpy(pb).to(DEV), d, 99,
+                               level, node)
+    assert np.array_equal(host(out)[:d], exp)
+
+
+def test_largest_tree_and_edge_inputs():
+    n, d = 1024, 64
+    x = wl.random_rows(n, d, seed=4)
+    x[3, :5] = [0.0, -0.0, 1e-42, -1e-41, np.nan]
+    x[7, 9] = np.inf
+    N, _ = oracle.global_norm(x, INF, 2)
+    xd = to_dev(x)
+    gmean, gnorm, groot = gq.gq_e8_compress_mean(xd, INF, 2, 5, want_root=True)
+    # non-finite inputs: the norm is inf, every code is on the grid
+    assert not np.isfinite(host(gnorm)[0]) and not np.isfinite(N)
+    assert host(groot).shape[0] >= d
+    y = wl.random_rows(n, d, seed=5)
+    N, root, mean = oracle.e8_compress_mean(y, 2, 2, 6)
+    gmean, gnorm, groot = gq.gq_e8_compress_mean(to_dev(y), 2, 2, 6, want_root=True)
+    check_norm(host(gnorm)[0], N)
+    assert np.array_equal(host(groot)[:d], root) and np.array_equal(host(gmean), mean)
+    z = np.zeros((4, 100), np.float32)
+    gmean, gnorm, groot = gq.gq_e8_compress_mean(to_dev(z), 2, 2, 1, want_root=True)
+    assert host(gnorm)[0] == 0 and not host(gmean).any() and not host(groot)[:100].any()
+    with pytest.raises(gq.GQError):
+        gq.gq_e8_compress_mean(to_dev(wl.random_rows(3, 16, seed=1)), 2, 2, 0)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("key", [2, 3, 4, 5])
+def test_e8_full_size_sampled(key):
+    w = wl.WORKLOADS[key]
+    threads = min(16, os.cpu_count() or 1)
+    log(f"workload {key}: generating")
+    x = wl.generate(w, threads=threads)
+    N, _ = oracle.global_norm_rows(x, w.q, w.p, threads=threads)
+    xd = to_dev(x)
+    gmean, gnorm, groot = gq.gq_e8_compress_mean(xd, w.q, w.p, w.seed, want_root=True)
+    check_norm(host(gnorm)[0], N)
+    rng = np.random.default_rng(key)
+    cols = np.unique(np.concatenate([np.arange(0, 4100), np.arange(w.d - 4100, w.d),
+                                     rng.integers(0, w.d, 20000)]))
+    log("sampled oracle columns")
+    root, mean = oracle.e8_compress_cols(x, N, w.seed, cols)
+    assert np.array_equal(host(groot)[cols], root)
+    gm = host(gmean)
+    assert np.array_equal(gm[cols], mean)
+    # every coordinate: the mean is N times a code value
+    assert np.all(np.isfinite(gm)) and np.abs(gm).max() <= float(N)
+    del xd, x
+    torch.cuda.empty_cache()
+    log(f"workload {key} ok")

@@ -185,3 +185,11 @@ def test_rerounding_variance_grows_like_one_plus_log2_n():
         tree.append(((val(oracle.e8_tree(codes, seed)) * float(N) - xbar) ** 2).sum())
     ratio = np.mean(tree) / np.mean(once)
     assert 3.0 < ratio < 5.0  # 1 + log2(8) = 4, far above (9/8)^3 = 1.42
+
+
+def test_column_pipeline_equals_whole_pipeline():
+    x = wl.random_rows(8, 300, seed=12, scale=0.4)
+    N, root, mean = oracle.e8_compress_mean(x, 2, 2, seed=21)
+    cols = np.array([0, 7, 8, 150, 299])
+    r2, m2 = oracle.e8_compress_cols(x, N, 21, cols)
+    assert np.array_equal(r2, root[cols]) and np.array_equal(m2, mean[cols])
