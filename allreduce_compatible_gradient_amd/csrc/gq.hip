@@ -66,7 +66,12 @@ inline int32_t ok()
 // ---------------------------------------------------------------------------
 // Host-side sizes
 
-inline bool order_ok(float v) { return v == 2.0f || (isinf(v) && v > 0.0f); }
+// q and p: a real >= 1 or +inf ("Global-QSGD: Practical Floatless Quantization ...",
+// Sec. 2 allows (1, inf) and inf; 1 is admitted as well)
+inline bool order_ok(float v) { return v >= 1.0f; }
+
+inline bool is_two(float v) { return v == 2.0f; }
+inline bool is_inf_order(float v) { return isinf(v) && v > 0.0f; }
 
 inline int64_t top_code(int32_t s, int32_t scheme)
 {
@@ -478,12 +483,14 @@ __device__ __forceinline__ double block_reduce(double v, double *lds)
 // Pass 1: per-(chunk, worker) partial norms.  Block b reads chunk b / n of
 // row b % n, so the last blocks to run read the ends of all rows.
 
-template <int DT, bool QINF>
+// QM: 0 = q 2 (exact squares), 1 = q inf (max |x|), 2 = other q (fp64 pow)
+template <int DT, int QM>
 __global__ __launch_bounds__(kThreads) void k_norm_partial(const void *__restrict__ x, int64_t n,
                                                            int64_t d, int64_t chunks,
-                                                           int64_t chunk_len,
+                                                           int64_t chunk_len, double qd,
                                                            double *__restrict__ partials)
 {
+    constexpr bool QINF = QM == 1;
     __shared__ double red[4];
     const int64_t b = blockIdx.x;
     const int64_t c = b / n, i = b % n;
@@ -507,11 +514,16 @@ __global__ __launch_bounds__(kThreads) void k_norm_partial(const void *__restric
                 if (QINF) {
                     mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v0[k]), fabsf(v1[k])),
                                          fmaxf(fabsf(v2[k]), fabsf(v3[k]))));
-                } else {
+                } else if (QM == 0) {
                     s0 += (double)v0[k] * (double)v0[k];
                     s1 += (double)v1[k] * (double)v1[k];
                     s0 += (double)v2[k] * (double)v2[k];
                     s1 += (double)v3[k] * (double)v3[k];
+                } else {
+                    s0 += pow(fabs((double)v0[k]), qd);
+                    s1 += pow(fabs((double)v1[k]), qd);
+                    s0 += pow(fabs((double)v2[k]), qd);
+                    s1 += pow(fabs((double)v3[k]), qd);
                 }
             }
         }
@@ -523,8 +535,10 @@ __global__ __launch_bounds__(kThreads) void k_norm_partial(const void *__restric
         for (int k = 0; k < kPer; ++k) {
             if (QINF)
                 mx = fmaxf(mx, fabsf(v[k]));
-            else
+            else if (QM == 0)
                 s0 += (double)v[k] * (double)v[k];
+            else
+                s0 += pow(fabs((double)v[k]), qd);
         }
     }
     const double r = QINF ? block_reduce<true>((double)mx, red) : block_reduce<false>(s0 + s1, red);
@@ -553,12 +567,15 @@ __device__ __forceinline__ double butterfly(double v, int width)
     return v;
 }
 
-template <bool QINF, bool PINF, bool LOCAL>
+// GEN: (q, p) not both in {2, inf}: w_i = m_i, sqrt(S_i) (q = 2) or S_i^(1/q),
+// then N = max_i w_i, sqrt(sum_i w_i^2) (p = 2) or (sum_i w_i^p)^(1/p), in fp64.
+template <bool QINF, bool PINF, bool LOCAL, bool GEN>
 __global__ __launch_bounds__(kFinThreads) void k_norm_finalize(const double *__restrict__ partials,
                                                                int64_t n, int64_t chunks,
                                                                double *__restrict__ per_worker,
                                                                float *__restrict__ norm_out, int s,
-                                                               WorkerParams *__restrict__ params)
+                                                               WorkerParams *__restrict__ params,
+                                                               double qd, double pd)
 {
     __shared__ double red[kFinThreads / 64];
     const int t = threadIdx.x, lane64 = t & 63, wave = t >> 6;
@@ -616,10 +633,16 @@ __global__ __launch_bounds__(kFinThreads) void k_norm_finalize(const double *__r
         return;
     }
     // combine over workers: strided in-order partial per thread, then a fixed tree
+    const bool q2 = qd == 2.0, p2 = pd == 2.0;
     double acc = 0.0;
     for (int64_t i = t; i < n; i += kFinThreads) {
         const double w = per_worker[i];
-        acc = combine<PINF>(acc, (QINF && !PINF) ? w * w : w);
+        if (GEN) {
+            const double wi = QINF ? w : (q2 ? sqrt(w) : pow(w, 1.0 / qd));
+            acc = combine<PINF>(acc, PINF ? wi : (p2 ? wi * wi : pow(wi, pd)));
+        } else {
+            acc = combine<PINF>(acc, (QINF && !PINF) ? w * w : w);
+        }
     }
     acc = butterfly<PINF>(acc, 64);
     if (lane64 == 0)
@@ -629,7 +652,10 @@ __global__ __launch_bounds__(kFinThreads) void k_norm_finalize(const double *__r
         double tot = red[0];
         for (int w = 1; w < kFinThreads / 64; ++w)
             tot = combine<PINF>(tot, red[w]);
-        norm_out[0] = (QINF && PINF) ? (float)tot : (float)sqrt(tot);
+        if (GEN)
+            norm_out[0] = PINF ? (float)tot : (float)(p2 ? sqrt(tot) : pow(tot, 1.0 / pd));
+        else
+            norm_out[0] = (QINF && PINF) ? (float)tot : (float)sqrt(tot);
     }
 }
 
@@ -1224,7 +1250,7 @@ int32_t validate_ws(const void *ws, int64_t ws_bytes, int64_t n, int64_t d)
     } while (0)
 
 // Enqueue pass 1 (partials + finalize).  Arguments already validated.
-int32_t launch_norm(const void *x, int32_t dtype, int64_t n, int64_t d, bool qinf, bool pinf,
+int32_t launch_norm(const void *x, int32_t dtype, int64_t n, int64_t d, float q, float p,
                     bool local, float *norm_out, void *ws, int s, hipStream_t st)
 {
     const NormGeom g = norm_geom(n, d);
@@ -1232,34 +1258,43 @@ int32_t launch_norm(const void *x, int32_t dtype, int64_t n, int64_t d, bool qin
     double *partials = (double *)((char *)ws + L.partials);
     double *per_worker = (double *)((char *)ws + L.per_worker);
     WorkerParams *params = (WorkerParams *)((char *)ws + L.params);
+    const bool qinf = is_inf_order(q), pinf = is_inf_order(p);
+    const int qm = qinf ? 1 : (is_two(q) ? 0 : 2);
+    const bool gen = !((qinf || is_two(q)) && (pinf || is_two(p)));
+    const double qd = qinf ? 0.0 : (double)q, pd = pinf ? 0.0 : (double)p;
     if (g.blocks > 0) {
         if (g.blocks > kMaxGrid)
             return fail(GQ_ERR_UNSUPPORTED, "norm grid too large");
         const dim3 grid((unsigned)g.blocks), block(kThreads);
+#define GQ_PARTIAL(DT, QM) \
+    k_norm_partial<DT, QM><<<grid, block, 0, st>>>(x, n, d, g.chunks, g.chunk_len, qd, partials)
         if (dtype == GQ_IN_F32) {
-            if (qinf)
-                k_norm_partial<GQ_IN_F32, true><<<grid, block, 0, st>>>(x, n, d, g.chunks, g.chunk_len, partials);
-            else
-                k_norm_partial<GQ_IN_F32, false><<<grid, block, 0, st>>>(x, n, d, g.chunks, g.chunk_len, partials);
+            if (qm == 0) GQ_PARTIAL(GQ_IN_F32, 0); else if (qm == 1) GQ_PARTIAL(GQ_IN_F32, 1); else GQ_PARTIAL(GQ_IN_F32, 2);
         } else {
-            if (qinf)
-                k_norm_partial<GQ_IN_BF16, true><<<grid, block, 0, st>>>(x, n, d, g.chunks, g.chunk_len, partials);
-            else
-                k_norm_partial<GQ_IN_BF16, false><<<grid, block, 0, st>>>(x, n, d, g.chunks, g.chunk_len, partials);
+            if (qm == 0) GQ_PARTIAL(GQ_IN_BF16, 0); else if (qm == 1) GQ_PARTIAL(GQ_IN_BF16, 1); else GQ_PARTIAL(GQ_IN_BF16, 2);
         }
+#undef GQ_PARTIAL
         GQ_TRY(check_launch("k_norm_partial"));
     }
     const dim3 one(1), block(kFinThreads);
+#define GQ_FIN(QI, PI, LO, GE) \
+    k_norm_finalize<QI, PI, LO, GE><<<one, block, 0, st>>>(partials, n, g.chunks, per_worker, norm_out, s, params, qd, pd)
     if (local)
-        k_norm_finalize<false, false, true><<<one, block, 0, st>>>(partials, n, g.chunks, per_worker, norm_out, s, params);
-    else if (qinf && pinf)
-        k_norm_finalize<true, true, false><<<one, block, 0, st>>>(partials, n, g.chunks, per_worker, norm_out, s, params);
+        GQ_FIN(false, false, true, false);
+    else if (gen) {
+        if (qinf && pinf) GQ_FIN(true, true, false, true);
+        else if (qinf) GQ_FIN(true, false, false, true);
+        else if (pinf) GQ_FIN(false, true, false, true);
+        else GQ_FIN(false, false, false, true);
+    } else if (qinf && pinf)
+        GQ_FIN(true, true, false, false);
     else if (qinf)
-        k_norm_finalize<true, false, false><<<one, block, 0, st>>>(partials, n, g.chunks, per_worker, norm_out, s, params);
+        GQ_FIN(true, false, false, false);
     else if (pinf)
-        k_norm_finalize<false, true, false><<<one, block, 0, st>>>(partials, n, g.chunks, per_worker, norm_out, s, params);
+        GQ_FIN(false, true, false, false);
     else
-        k_norm_finalize<false, false, false><<<one, block, 0, st>>>(partials, n, g.chunks, per_worker, norm_out, s, params);
+        GQ_FIN(false, false, false, false);
+#undef GQ_FIN
     return check_launch("k_norm_finalize");
 }
 
@@ -1339,10 +1374,9 @@ int32_t gq_global_norm(const void *x, int32_t dtype, int64_t n, int64_t d, float
     if (!norm_dev)
         return fail(GQ_ERR_NULL, "norm_dev is NULL");
     if (!order_ok(q) || !order_ok(p))
-        return fail(GQ_ERR_UNSUPPORTED, "q and p must be 2 or +inf");
+        return fail(GQ_ERR_UNSUPPORTED, "q and p must be reals >= 1 or +inf");
     GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
-    return launch_norm(x, dtype, n, d, isinf(q), isinf(p), false, norm_dev, workspace, 0,
-                       (hipStream_t)stream);
+    return launch_norm(x, dtype, n, d, q, p, false, norm_dev, workspace, 0, (hipStream_t)stream);
 }
 
 int32_t gq_quantize(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s, int32_t scheme,
@@ -1459,7 +1493,7 @@ int32_t gq_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int
     if (!norm_dev || (!mean && d > 0))
         return fail(GQ_ERR_NULL, "norm_dev or mean is NULL");
     if (!order_ok(q) || !order_ok(p))
-        return fail(GQ_ERR_UNSUPPORTED, "q and p must be 2 or +inf");
+        return fail(GQ_ERR_UNSUPPORTED, "q and p must be reals >= 1 or +inf");
     if (min_bits(n, s, scheme) > 32)
         return fail(GQ_ERR_CODE_WIDTH, "sums of %lld codes do not fit 32 bits", (long long)n);
     if (code_sum_or_null) {
@@ -1471,7 +1505,7 @@ int32_t gq_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int
         return fail(GQ_ERR_ALIGN, "mean is not 16-byte aligned");
     GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
     hipStream_t st = (hipStream_t)stream;
-    GQ_TRY(launch_norm(x, dtype, n, d, isinf(q), isinf(p), false, norm_dev, workspace, 0, st));
+    GQ_TRY(launch_norm(x, dtype, n, d, q, p, false, norm_dev, workspace, 0, st));
     return launch_compress(x, dtype, n, d, s, scheme, seed, norm_dev, code_bits, mean,
                            code_sum_or_null, st);
 }
@@ -1494,7 +1528,7 @@ int32_t gq_qsgd_local_mean(const void *x, int32_t dtype, int64_t n, int64_t d, i
         return fail(GQ_ERR_ALIGN, "mean is not 16-byte aligned");
     GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
     hipStream_t st = (hipStream_t)stream;
-    GQ_TRY(launch_norm(x, dtype, n, d, false, false, true, norms_dev, workspace, s, st));
+    GQ_TRY(launch_norm(x, dtype, n, d, 2.0f, 2.0f, true, norms_dev, workspace, s, st));
     const int64_t tiles = (d + kTile - 1) / kTile;
     if (tiles == 0)
         return ok();
@@ -1617,12 +1651,12 @@ int32_t gq_e8_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, 
     if (!norm_dev || (!mean && d > 0))
         return fail(GQ_ERR_NULL, "norm_dev or mean is NULL");
     if (!order_ok(q) || !order_ok(p))
-        return fail(GQ_ERR_UNSUPPORTED, "q and p must be 2 or +inf");
+        return fail(GQ_ERR_UNSUPPORTED, "q and p must be reals >= 1 or +inf");
     if (!aligned16(mean) || !aligned16(root_or_null))
         return fail(GQ_ERR_ALIGN, "mean or root is not 16-byte aligned");
     GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
     hipStream_t st = (hipStream_t)stream;
-    GQ_TRY(launch_norm(x, dtype, n, d, isinf(q), isinf(p), false, norm_dev, workspace, 0, st));
+    GQ_TRY(launch_norm(x, dtype, n, d, q, p, false, norm_dev, workspace, 0, st));
     const int64_t tiles = (d + kTile - 1) / kTile;
     if (tiles == 0)
         return ok();

@@ -18,8 +18,9 @@
  * Conventions shared by every entry point
  *   - x is row-major [n][d]; row i is worker i.  dtype GQ_IN_F32 (float) or
  *     GQ_IN_BF16 (bfloat16, widened exactly to float).
- *   - q, p are 2.0f or +INFINITY (the (q,p)-norm: q inside a worker, p over
- *     the n per-worker norms).
+ *   - q, p are reals >= 1 or +INFINITY (the (q,p)-norm: q inside a worker,
+ *     p over the n per-worker norms).  The pairs from {2, inf} are exact
+ *     forms; other orders go through fp64 pow.
  *   - s: number of level intervals.  L: 1 <= s <= 2^24; the integer code of
  *     a coordinate is in [-s, s].  E: 1 <= s <= 31; levels 2^-k (k < s)
  *     are coded as the integers 2^(s-1-k), so codes are in [-2^(s-1), 2^(s-1)].
@@ -89,9 +90,12 @@ int64_t gq_workspace_bytes(int64_t n, int64_t d);
 
 /* Global (q,p)-norm of the concatenation (Sec. 2 notation):
  *   q = 2: S_i = sum_j x_ij^2 in fp64 (each square exact); q = inf:
- *   m_i = max_j |x_ij|.  p = 2: N = fp32(sqrt(sum_i S_i)) (q = 2) or
- *   fp32(sqrt(sum_i m_i^2)) (q = inf); p = inf: N = fp32(sqrt(max_i S_i))
- *   or max_i m_i.  Writes N to norm_dev[0] (one float, device).
+ *   m_i = max_j |x_ij|; other q: S_i = sum_j |x_ij|^q (fp64 pow).
+ *   (2,2): N = fp32(sqrt(sum_i S_i)); (inf,2): fp32(sqrt(sum_i m_i^2));
+ *   (2,inf): fp32(sqrt(max_i S_i)); (inf,inf): max_i m_i.  Other pairs:
+ *   w_i = m_i, sqrt(S_i) (q = 2) or S_i^(1/q); N = fp32 of max_i w_i (p = inf),
+ *   sqrt(sum_i w_i^2) (p = 2) or (sum_i w_i^p)^(1/p).
+ *   Writes N to norm_dev[0] (one float, device).
  * The reduction tree is fixed by (n, d), so repeated calls give identical
  * bits.  d == 0 gives N = 0.                                               */
 int32_t gq_global_norm(const void *x, int32_t dtype, int64_t n, int64_t d, float q, float p,

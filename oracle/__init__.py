@@ -128,9 +128,9 @@ def _rows(x: np.ndarray) -> np.ndarray:
 
 def _order(v) -> float:
     v = float(v)
-    if v == 2.0 or math.isinf(v):
+    if v >= 1.0:  # a real >= 1 or +inf
         return v
-    raise ValueError("q and p are 2 or inf")
+    raise ValueError("q and p are reals >= 1 or inf")
 
 
 # ---------------------------------------------------------------------------

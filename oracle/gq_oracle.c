@@ -134,28 +134,55 @@ static void nsum_add(nsum *a, double v)
 }
 
 /* ------------------------------------------------------------------------ */
-/* (q,p)-norm of the concatenation, Sec. 2.  q selects the per-worker norm
- * (2 or infinity), p the norm taken over the n per-worker norms.
- * per_worker[i] receives sum_j x_ij^2 (q = 2) or max_j |x_ij| (q = inf).   */
+/* (q,p)-norm of the concatenation, Sec. 2.  q selects the per-worker norm,
+ * p the norm taken over the n per-worker norms; each is a real >= 1 or
+ * +infinity (Sec. 2 allows (1, inf) and inf; 1 is admitted as well).
+ * per_worker[i] receives max_j |x_ij| (q = inf) or sum_j |x_ij|^q (finite q;
+ * for q = 2 every square is exact in fp64, other q use fp64 pow).
+ * The four combinations of {2, inf} are formed without pow:
+ *   (2,2) sqrt(sum_i S_i)   (2,inf) sqrt(max_i S_i)
+ *   (inf,2) sqrt(sum_i m_i^2)   (inf,inf) max_i m_i
+ * Any other pair: w_i = m_i, sqrt(S_i) (q = 2) or S_i^(1/q); then
+ * N = max_i w_i (p = inf), sqrt(sum_i w_i^2) (p = 2) or (sum_i w_i^p)^(1/p).
+ * N is that fp64 value rounded once to fp32.                               */
 
 static int is_inf_order(float v) { return isinf(v) && v > 0; }
 
-/* Combination over workers of the per-worker values (sum of squares for
- * q = 2, max |x| for q = inf) with the outer order p.                    */
+/* Combination over workers of the per-worker values. */
 float oracle_norm_from_partials(const double *per_worker, int64_t n, float q, float p)
 {
     int q_inf = is_inf_order(q), p_inf = is_inf_order(p);
-    if (p_inf) {
-        double m = 0.0;
+    int q_two = (q == 2.0f), p_two = (p == 2.0f);
+    if ((q_inf || q_two) && (p_inf || p_two)) {
+        if (p_inf) {
+            double m = 0.0;
+            for (int64_t i = 0; i < n; ++i)
+                if (per_worker[i] > m)
+                    m = per_worker[i];
+            return q_inf ? (float)m : (float)sqrt(m);
+        }
+        nsum tot = {0.0, 0.0};
         for (int64_t i = 0; i < n; ++i)
-            if (per_worker[i] > m)
-                m = per_worker[i];
-        return q_inf ? (float)m : (float)sqrt(m);
+            nsum_add(&tot, q_inf ? per_worker[i] * per_worker[i] : per_worker[i]);
+        return (float)sqrt(tot.s + tot.c);
     }
+    /* general orders */
+    double m = 0.0;
     nsum tot = {0.0, 0.0};
-    for (int64_t i = 0; i < n; ++i)
-        nsum_add(&tot, q_inf ? per_worker[i] * per_worker[i] : per_worker[i]);
-    return (float)sqrt(tot.s + tot.c);
+    for (int64_t i = 0; i < n; ++i) {
+        double w = q_inf ? per_worker[i]
+                         : (q_two ? sqrt(per_worker[i]) : pow(per_worker[i], 1.0 / (double)q));
+        if (p_inf) {
+            if (w > m)
+                m = w;
+        } else {
+            nsum_add(&tot, p_two ? w * w : pow(w, (double)p));
+        }
+    }
+    if (p_inf)
+        return (float)m;
+    double t = tot.s + tot.c;
+    return (float)(p_two ? sqrt(t) : pow(t, 1.0 / (double)p));
 }
 
 float oracle_global_norm(const void *x, int dtype, int64_t n, int64_t d,
@@ -175,7 +202,8 @@ float oracle_global_norm(const void *x, int dtype, int64_t n, int64_t d,
             nsum acc = {0.0, 0.0};
             for (int64_t j = 0; j < d; ++j) {
                 double v = (double)load_x(x, dtype, (uint64_t)(i * d + j));
-                nsum_add(&acc, v * v); /* exact: a 24-bit significand squared */
+                /* q = 2: exact, a 24-bit significand squared; else fp64 pow */
+                nsum_add(&acc, q == 2.0f ? v * v : pow(fabs(v), (double)q));
             }
             per_worker[i] = acc.s + acc.c;
         }

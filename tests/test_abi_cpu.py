@@ -69,8 +69,9 @@ def _err(status):
     ((A, 0, 0, 1000, 2.0, 2.0, A, A, WS, NUL), 2),        # n = 0
     ((A, 0, 4, -1, 2.0, 2.0, A, A, WS, NUL), 2),          # d < 0
     ((A, 0, 1 << 30, 1 << 40, 2.0, 2.0, A, A, WS, NUL), 2),  # n d overflow
-    ((A, 0, 4, 1000, 3.0, 2.0, A, A, WS, NUL), 3),        # q = 3
-    ((A, 0, 4, 1000, 2.0, 1.0, A, A, WS, NUL), 3),        # p = 1
+    ((A, 0, 4, 1000, 0.5, 2.0, A, A, WS, NUL), 3),        # q < 1
+    ((A, 0, 4, 1000, 2.0, 0.99, A, A, WS, NUL), 3),       # p < 1
+    ((A, 0, 4, 1000, math.nan, 2.0, A, A, WS, NUL), 3),   # q NaN
     ((A, 0, 4, 1000, 2.0, -math.inf, A, A, WS, NUL), 3),  # p = -inf
     ((U, 0, 4, 1000, 2.0, 2.0, A, A, WS, NUL), 6),        # x misaligned
     ((A, 0, 4, 1000, 2.0, 2.0, A, A, WS - 1, NUL), 5),    # workspace too small
@@ -111,7 +112,7 @@ def test_other_entry_points_reject():
     assert L.gq_compress_mean_from_norm(A, 0, 4, 100, 7, 0, 1, A, 5, A, A, NUL) == 4
     assert L.gq_compress_mean_from_norm(A, 0, 4, 100, 7, 0, 1, NUL, 8, A, NUL, NUL) == 1
     ws = gq.gq_workspace_bytes(4, 100)
-    assert L.gq_compress_mean(A, 0, 4, 100, 7, 2.0, 5.0, 0, 1, 8, A, A, NUL, A, ws, NUL) == 3
+    assert L.gq_compress_mean(A, 0, 4, 100, 7, 2.0, 0.0, 0, 1, 8, A, A, NUL, A, ws, NUL) == 3
     assert L.gq_compress_mean(A, 0, 4, 100, 7, 2.0, 2.0, 0, 1, 8, A, A, NUL, A, ws - 1, NUL) == 5
     assert L.gq_compress_mean(A, 1, 4, 100, 0, 2.0, 2.0, 0, 1, 8, A, A, NUL, A, ws, NUL) == 2
     assert L.gq_qsgd_local_mean(A, 0, 4, 100, 3, 1, A, A, A, 2, A, ws, NUL) == 4

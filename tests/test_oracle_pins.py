@@ -553,3 +553,31 @@ def test_local_ablation_pieces_compose():
     cols = np.array([0, 17, 300, 150])
     c2, m2 = oracle.qsgd_local_cols(x, norms, 4, 2, cols)
     assert np.array_equal(c2, codes[:, cols]) and np.array_equal(m2, mean[cols])
+
+
+# ---------------------------------------------------------------------------
+# General real orders (Sec. 2 allows p in (1, inf) and inf)
+
+@pytest.mark.parametrize("q,p", [(1.0, 1.0), (1.5, 3.0), (3.0, INF), (INF, 1.5), (2.0, 4.0),
+                                 (7.25, 2.0), (1.0, INF)])
+def test_general_orders_against_numpy(q, p):
+    x = wl.random_rows(5, 200, seed=int(10 * min(q, 99.0) + p if p < INF else 3), scale=0.3)
+    N, _ = oracle.global_norm(x, q, p)
+    xr = x.astype(np.float64)
+    w = np.array([np.linalg.norm(xr[i], ord=q) for i in range(5)])
+    ref = np.linalg.norm(w, ord=p)
+    assert abs(float(N) - ref) <= 2 ** -23 * ref  # one fp32 rounding of a ~1e-15-accurate value
+
+
+def test_general_orders_closed_forms():
+    x = np.array([[3.0, -4.0, 0.0], [1.0, 1.0, -2.0]], np.float32)
+    assert oracle.global_norm(x, 1.0, 1.0)[0] == np.float32(11.0)       # sum of |x|
+    assert oracle.global_norm(x, 1.0, INF)[0] == np.float32(7.0)        # max row l1
+    assert oracle.global_norm(x, INF, 1.0)[0] == np.float32(6.0)        # 4 + 2
+    assert oracle.global_norm(x, 3.0, 3.0)[0] == np.float32((27 + 64 + 1 + 1 + 8) ** (1 / 3))
+    # the {2, inf} pairs keep their exact forms
+    assert oracle.global_norm(x, 2.0, 2.0)[0] == np.float32(math.sqrt(31.0))
+    # norms decrease with the order
+    y = wl.random_rows(3, 50, seed=3)
+    vals = [float(oracle.global_norm(y, q, q)[0]) for q in (1.0, 1.5, 2.0, 3.0, 8.0, INF)]
+    assert all(a >= b for a, b in zip(vals, vals[1:]))
