@@ -319,6 +319,22 @@ __device__ __forceinline__ void load_group(const void *__restrict__ x, int64_t r
     }
 }
 
+// 8 consecutive floats of the mean: two 128-bit stores when the group lies
+// inside an aligned row (d % 8 == 0), else per-element stores up to d.
+__device__ __forceinline__ void store_mean8(float *__restrict__ mean, int64_t j0, int64_t d,
+                                            const float (&m)[kPer])
+{
+    if ((d & 7) == 0) {
+        *(float4 *)(mean + j0) = make_float4(m[0], m[1], m[2], m[3]);
+        *(float4 *)(mean + j0 + 4) = make_float4(m[4], m[5], m[6], m[7]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            if (j0 + k < d)
+                mean[j0 + k] = m[k];
+    }
+}
+
 // Store 8 W-bit fields per thread (thread-major: coordinate tile*2048 +
 // 8*t + k) into one packed row.  W = 8/16/32: direct vector stores.  Other
 // W: fields go through LDS and each thread assembles whole output words, so
@@ -729,15 +745,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restri
 #pragma unroll
         for (int k = 0; k < kPer; ++k)
             m[k] = (float)((double)acc[k] * q.kappa);
-        if (((d & 7) == 0)) {
-            *(float4 *)(mean + j0) = make_float4(m[0], m[1], m[2], m[3]);
-            *(float4 *)(mean + j0 + 4) = make_float4(m[4], m[5], m[6], m[7]);
-        } else {
-#pragma unroll
-            for (int k = 0; k < kPer; ++k)
-                if (j0 + k < d)
-                    mean[j0 + k] = m[k];
-        }
+        store_mean8(mean, j0, d, m);
     }
     if (code_sum)
         store_tile_packed(lds, acc, W, code_sum, tile, row_bytes(d, W));
@@ -819,11 +827,14 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t *__restri
     const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
     int v[kPer];
     load_tile_fields(lds, code_sum, W, tile, row_bytes(d, W), v);
+    if (j0 >= d)
+        return;
     const QParams q = make_qparams(*norm_dev, n, s, SCH);
+    float m[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k)
-        if (j0 + k < d)
-            mean[j0 + k] = (float)((double)v[k] * q.kappa);
+        m[k] = (float)((double)v[k] * q.kappa);
+    store_mean8(mean, j0, d, m);
 }
 
 // Ablation: local-norm QSGD.  Worker i uses its own scalars; the mean is an
@@ -880,10 +891,11 @@ __global__ __launch_bounds__(kThreads) void k_local_mean(const void *__restrict_
             store_tile_packed(lds, code, W, codes + i * rbytes, tile, rbytes);
     }
     if (j0 < d) {
+        float m[kPer];
 #pragma unroll
         for (int k = 0; k < kPer; ++k)
-            if (j0 + k < d)
-                mean[j0 + k] = (float)acc[k];
+            m[k] = (float)acc[k];
+        store_mean8(mean, j0, d, m);
     }
 }
 
@@ -1129,10 +1141,11 @@ __global__ __launch_bounds__(kThreads) void k_e8_dequantize(const uint8_t *__res
         return;
     const double N = (double)*norm_dev;
     const uint2 w = load_codes8(root, j0, d);
+    float m[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k)
-        if (j0 + k < d)
-            mean[j0 + k] = (float)(N * e8_value(byte_of(w, k)));
+        m[k] = (float)(N * e8_value(byte_of(w, k)));
+    store_mean8(mean, j0, d, m);
 }
 
 // Fused: quantize the n workers' coordinates, reduce them through the tree in
@@ -1169,15 +1182,7 @@ __global__ __launch_bounds__(kThreads) void k_e8_compress_mean(const void *__res
 #pragma unroll
     for (int k = 0; k < kPer; ++k)
         m[k] = (float)((double)N * e8_value(byte_of(cur, k)));
-    if ((d & 7) == 0) {
-        *(float4 *)(mean + j0) = make_float4(m[0], m[1], m[2], m[3]);
-        *(float4 *)(mean + j0 + 4) = make_float4(m[4], m[5], m[6], m[7]);
-    } else {
-#pragma unroll
-        for (int k = 0; k < kPer; ++k)
-            if (j0 + k < d)
-                mean[j0 + k] = m[k];
-    }
+    store_mean8(mean, j0, d, m);
 }
 
 // ---------------------------------------------------------------------------
