@@ -319,14 +319,48 @@ __device__ __forceinline__ void load_group(const void *__restrict__ x, int64_t r
     }
 }
 
+// Results are written once and never re-read by these kernels.  Where the
+// writes interleave with a heavy read stream (the fused, quantize, reduce and
+// ablation passes), non-temporal 128-bit stores are faster (measured: the
+// fused pass 4.5% on an 8 x 25.6M input, neutral on larger ones; non-temporal
+// loads do worse).  Write-dominated kernels (dequantize) keep plain stores,
+// which measured faster there.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void nt_store(float *p, float a, float b, float c, float d)
+{
+    const f32x4 v = {a, b, c, d};
+    __builtin_nontemporal_store(v, (f32x4 *)p);
+}
+
+__device__ __forceinline__ void nt_store(uint8_t *p, const uint4 &w)
+{
+    const u32x4 v = {w.x, w.y, w.z, w.w};
+    __builtin_nontemporal_store(v, (u32x4 *)p);
+}
+
+__device__ __forceinline__ void nt_store(uint8_t *p, const uint2 &w)
+{
+    const u32x2 v = {w.x, w.y};
+    __builtin_nontemporal_store(v, (u32x2 *)p);
+}
+
 // 8 consecutive floats of the mean: two 128-bit stores when the group lies
 // inside an aligned row (d % 8 == 0), else per-element stores up to d.
+template <bool NT = true>
 __device__ __forceinline__ void store_mean8(float *__restrict__ mean, int64_t j0, int64_t d,
                                             const float (&m)[kPer])
 {
     if ((d & 7) == 0) {
-        *(float4 *)(mean + j0) = make_float4(m[0], m[1], m[2], m[3]);
-        *(float4 *)(mean + j0 + 4) = make_float4(m[4], m[5], m[6], m[7]);
+        if (NT) {
+            nt_store(mean + j0, m[0], m[1], m[2], m[3]);
+            nt_store(mean + j0 + 4, m[4], m[5], m[6], m[7]);
+        } else {
+            *(float4 *)(mean + j0) = make_float4(m[0], m[1], m[2], m[3]);
+            *(float4 *)(mean + j0 + 4) = make_float4(m[4], m[5], m[6], m[7]);
+        }
     } else {
 #pragma unroll
         for (int k = 0; k < kPer; ++k)
@@ -351,7 +385,7 @@ __device__ void store_tile_packed(uint32_t *lds, const int (&val)[kPer], int W, 
             uint2 o;
             o.x = (val[0] & 0xFF) | (val[1] & 0xFF) << 8 | (val[2] & 0xFF) << 16 | (uint32_t)val[3] << 24;
             o.y = (val[4] & 0xFF) | (val[5] & 0xFF) << 8 | (val[6] & 0xFF) << 16 | (uint32_t)val[7] << 24;
-            *(uint2 *)(row + off) = o;
+            nt_store(row + off, o);
         }
         return;
     }
@@ -363,16 +397,16 @@ __device__ void store_tile_packed(uint32_t *lds, const int (&val)[kPer], int W, 
             o.y = (val[2] & 0xFFFF) | (uint32_t)val[3] << 16;
             o.z = (val[4] & 0xFFFF) | (uint32_t)val[5] << 16;
             o.w = (val[6] & 0xFFFF) | (uint32_t)val[7] << 16;
-            *(uint4 *)(row + off) = o;
+            nt_store(row + off, o);
         }
         return;
     }
     if (W == 32) {
         const int64_t off = 4 * j0;
         if (off < rbytes)
-            *(uint4 *)(row + off) = make_uint4(val[0], val[1], val[2], val[3]);
+            nt_store(row + off, make_uint4(val[0], val[1], val[2], val[3]));
         if (off + 16 < rbytes)
-            *(uint4 *)(row + off + 16) = make_uint4(val[4], val[5], val[6], val[7]);
+            nt_store(row + off + 16, make_uint4(val[4], val[5], val[6], val[7]));
         return;
     }
     const uint32_t mask = (1u << W) - 1u;
@@ -395,7 +429,7 @@ __device__ void store_tile_packed(uint32_t *lds, const int (&val)[kPer], int W, 
             const uint32_t f = lds[e];
             word |= (sh >= 0) ? (f << sh) : (f >> -sh);
         }
-        rw[w0 + w] = word;
+        __builtin_nontemporal_store(word, rw + w0 + w);
     }
     __syncthreads();
 }
@@ -834,7 +868,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t *__restri
 #pragma unroll
     for (int k = 0; k < kPer; ++k)
         m[k] = (float)((double)v[k] * q.kappa);
-    store_mean8(mean, j0, d, m);
+    store_mean8<false>(mean, j0, d, m);
 }
 
 // Ablation: local-norm QSGD.  Worker i uses its own scalars; the mean is an
@@ -1054,7 +1088,7 @@ __device__ __forceinline__ uint2 load_codes8(const uint8_t *row, int64_t j0, int
 __device__ __forceinline__ void store_codes8(uint8_t *row, int64_t j0, int64_t d, const uint2 &w)
 {
     if (j0 + kPer <= d) {
-        *(uint2 *)(row + j0) = w;
+        nt_store(row + j0, w);
         return;
     }
 #pragma unroll
@@ -1145,7 +1179,7 @@ __global__ __launch_bounds__(kThreads) void k_e8_dequantize(const uint8_t *__res
 #pragma unroll
     for (int k = 0; k < kPer; ++k)
         m[k] = (float)(N * e8_value(byte_of(w, k)));
-    store_mean8(mean, j0, d, m);
+    store_mean8<false>(mean, j0, d, m);
 }
 
 // Fused: quantize the n workers' coordinates, reduce them through the tree in
