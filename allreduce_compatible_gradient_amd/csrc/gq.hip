@@ -638,19 +638,22 @@ __global__ __launch_bounds__(kFinThreads) void k_norm_finalize(const double *__r
         const int lane = t % seg;
         double acc = 0.0;
         if (i < n) {
+            // rounds of eight loads issued together; past the end a load is
+            // replaced by 0, the identity of both the sum and the max of
+            // non-negative partials, so a short tail costs one round trip
+            // instead of one per partial
             const double *p = partials + i * chunks;
-            int64_t c = lane;
-            for (; c + 7 * (int64_t)seg < chunks; c += 8 * (int64_t)seg) {
+            for (int64_t c = lane; c < chunks; c += 8 * (int64_t)seg) {
                 double v[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    v[u] = p[c + u * (int64_t)seg];
+                for (int u = 0; u < 8; ++u) {
+                    const int64_t cu = c + u * (int64_t)seg;
+                    v[u] = cu < chunks ? p[cu] : 0.0;
+                }
 #pragma unroll
                 for (int u = 0; u < 8; ++u)
                     acc = combine<QINF>(acc, v[u]);
             }
-            for (; c < chunks; c += seg)
-                acc = combine<QINF>(acc, p[c]);
         }
         acc = butterfly<QINF>(acc, seg < 64 ? seg : 64);
         if (seg > 64) {
@@ -952,25 +955,36 @@ __device__ __forceinline__ double e8_value(uint32_t c)
     return idx ? __longlong_as_double((long long)bits) : 0.0;
 }
 
-// Neighbouring codes of v (|v| <= 1) on the grid and the threshold F
-// (upper iff u < F): r = 2^e (1 + phi) >= 2^-126 gives 2^e / 2^(e+1) and the
-// top 32 fraction bits of phi; 0 < r < 2^-126 gives 0 / 2^-126 and
-// floor(r 2^126 2^32).
-__device__ __forceinline__ void e8_bracket(double v, uint32_t &lo, uint32_t &hi, uint32_t &F)
+// Half the value of a code, exactly: exponent field 1023 - k, so that the
+// parent of two codes is the plain fp64 sum of their halves (no rounding:
+// both are powers of two >= 2^-128, far above fp64's subnormal range).
+__device__ __forceinline__ double e8_half_value(uint32_t c)
 {
-    const uint32_t sign = (uint32_t)((uint64_t)__double_as_longlong(v) >> 56) & 0x80u;
-    const double r = fmin(fabs(v), 1.0);
-    const uint64_t rb = (uint64_t)__double_as_longlong(r);
-    const uint32_t ef = (uint32_t)(rb >> 52); // biased exponent, e = ef - 1023
-    if (r >= 0x1p-126) {
-        F = (uint32_t)(rb >> 20);
-        lo = sign | (1024u - ef);
-        hi = sign | (1023u - ef);
-    } else {
-        F = (uint32_t)((r * 0x1p126) * 0x1p32);
-        lo = 0u;
-        hi = (r == 0.0) ? 0u : (sign | 127u);
-    }
+    const uint32_t idx = c & 0x7Fu;
+    const uint32_t hi = ((c & 0x80u) << 24) | ((1023u - idx) << 20);
+    return __hiloint2double((int)(idx ? hi : 0u), 0);
+}
+
+// Rounding fields of a parent value v.  The parent of two codes has |v| <= 1
+// and is 0, +-2^-127 or at least 2^-126 in magnitude (the smallest nonzero
+// halves and half-differences of two levels >= 2^-126 are 2^-127).
+// |v| >= 2^-126: v = 2^e (1 + phi) lies between the codes of 2^e (index
+// lo = 1 - e, returned) and 2^(e+1) (index lo - 1), F = the top 32 bits of
+// phi.  +-2^-127: lo = 128, standing for the level 0, below 2^-126 (index
+// 127), F = 2^31.  0: lo = 1024, F = 0.  Indices above 127 are the level 0.
+// The code taken is sign | (lo - [u < F]), upper iff u < F.
+__device__ __forceinline__ uint32_t e8_pair_fields(double v, uint32_t &sign, uint32_t &F)
+{
+    const uint32_t vh = (uint32_t)__double2hiint(v), vl = (uint32_t)__double2loint(v);
+    const uint32_t ef = (vh >> 20) & 0x7FFu; // biased exponent, e = ef - 1023
+    sign = (vh >> 24) & 0x80u;
+    F = ef == 896u ? 0x80000000u : __builtin_amdgcn_alignbit(vh, vl, 20);
+    return 1024u - ef;
+}
+
+__device__ __forceinline__ uint32_t e8_pair_code(uint32_t sign, uint32_t idx)
+{
+    return idx > 127u ? 0u : (sign | idx);
 }
 
 // Quantization to 8-bit codes: Global-E_s with s = 127 in the byte format.
@@ -1035,18 +1049,35 @@ __device__ __forceinline__ void e8_decide(BracketFn bracket_k, uint32_t blo, uin
     }
 }
 
-// One custom reduction of 8 coordinates: codes a (left child) and b (right).
+// One custom reduction of 8 coordinates: codes a (left child) and b (right),
+// with the same draws and lazy second draw as the quantization.
 __device__ __forceinline__ uint2 e8_combine(const uint2 &a, const uint2 &b, uint32_t blo,
                                             uint32_t bhi, uint32_t node, uint32_t level,
                                             uint32_t k0, uint32_t k1)
 {
+    const uint4 A = philox10(make_uint4(blo, bhi, node, 2u * level), k0, k1);
     double v[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k)
-        v[k] = 0.5 * (e8_value(byte_of(a, k)) + e8_value(byte_of(b, k)));
     uint32_t c[kPer];
-    e8_decide([&](int k, uint32_t &lo, uint32_t &hi, uint32_t &F) { e8_bracket(v[k], lo, hi, F); },
-              blo, bhi, node, level, k0, k1, c);
+    bool tie = false;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        v[k] = e8_half_value(byte_of(a, k)) + e8_half_value(byte_of(b, k));
+        uint32_t sign, F;
+        const uint32_t lo = e8_pair_fields(v[k], sign, F);
+        const uint32_t h = half16(A, k), Fh = F >> 16;
+        c[k] = e8_pair_code(sign, lo - (h < Fh ? 1u : 0u));
+        tie |= (h == Fh);
+    }
+    if (tie) {
+        const uint4 B = philox10(make_uint4(blo, bhi, node, 2u * level + 1u), k0, k1);
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            uint32_t sign, F;
+            const uint32_t lo = e8_pair_fields(v[k], sign, F);
+            if (half16(A, k) == (F >> 16) && half16(B, k) < (F & 0xFFFFu))
+                c[k] = e8_pair_code(sign, lo - 1u);
+        }
+    }
     return pack_bytes(c);
 }
 

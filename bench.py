@@ -106,15 +106,28 @@ def eq8_threshold(rho: float, omega: float) -> float:
 
 
 def _time_us(torch, stream, fn, reps):
-    for _ in range(3):
-        fn()
+    """Device time per call of fn(stream), in microseconds.  The reps calls
+    are captured in one HIP graph and replayed, so that calls shorter than
+    the host's per-call overhead are still timed back to back on the GPU."""
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn(side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for _ in range(reps):
+            fn(side)
+    graph.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(reps):
-        fn()
+    graph.replay()
     e1.record(stream)
     torch.cuda.synchronize()
+    del graph
     return e0.elapsed_time(e1) / reps * 1e3
 
 
@@ -128,13 +141,13 @@ def e8_report(gq, torch, w, xd, stream, steps, ws):
         a = torch.randn(d, generator=g).to(xd.device)
         b = torch.randn(d, generator=g).to(xd.device)
         c = torch.empty_like(a)
-        t_f32 = _time_us(torch, stream, lambda: torch.add(a, b, out=c), 50)
+        t_f32 = _time_us(torch, stream, lambda st: torch.add(a, b, out=c), 50)
         au = torch.randint(0, 256, (d,), dtype=torch.uint8, generator=g).to(xd.device)
         bu = torch.randint(0, 256, (d,), dtype=torch.uint8, generator=g).to(xd.device)
         cu = torch.empty_like(au)
-        t_u8 = _time_us(torch, stream, lambda: torch.add(au, bu, out=cu), 50)
-        t_e8 = _time_us(torch, stream, lambda: gq.gq_e8_reduce_pair(au, bu, d, 1, 1, 0, out=cu,
-                                                                    stream=stream), 50)
+        t_u8 = _time_us(torch, stream, lambda st: torch.add(au, bu, out=cu), 50)
+        t_e8 = _time_us(torch, stream, lambda st: gq.gq_e8_reduce_pair(au, bu, d, 1, 1, 0, out=cu,
+                                                                       stream=st), 50)
         del a, b, c
         # byte rates: the fp32 sum reduces 4d bytes, the code sums d bytes
         om_e, om_s = (d / t_e8) / (4 * d / t_f32), (d / t_u8) / (4 * d / t_f32)
@@ -146,11 +159,25 @@ def e8_report(gq, torch, w, xd, stream, steps, ws):
     if n & (n - 1) == 0:
         mean = torch.empty(d, dtype=torch.float32, device=xd.device)
         norm = torch.empty(1, dtype=torch.float32, device=xd.device)
-        t = _time_us(torch, stream, lambda: gq.gq_e8_compress_mean(
-            xd, w.q, w.p, w.seed, mean=mean, norm=norm, workspace=ws, stream=stream), steps)
+        t = _time_us(torch, stream, lambda st: gq.gq_e8_compress_mean(
+            xd, w.q, w.p, w.seed, mean=mean, norm=norm, workspace=ws, stream=st), steps)
         out["fused"] = {"ms_per_step": round(t * 1e-3, 6),
                         "input_GBs": round(n * d * w.elem_bytes / (t * 1e-6) / 1e9, 3),
                         "bits_per_element": 8}
+        # the same steps as separate calls: codes of every worker, the tree
+        # over the stored codes, dequantization of the root
+        codes = torch.empty((n, gq.gq_e8_row_bytes(d)), dtype=torch.uint8, device=xd.device)
+        root = torch.empty(gq.gq_e8_row_bytes(d), dtype=torch.uint8, device=xd.device)
+        gq.gq_global_norm(xd, w.q, w.p, norm=norm, workspace=ws, stream=stream)
+        parts = {
+            "e8_quantize_us": lambda st: gq.gq_e8_quantize(xd, norm, w.seed, codes=codes,
+                                                           stream=st),
+            "e8_tree_us": lambda st: gq.gq_e8_tree(codes, n, d, w.seed, root=root, stream=st),
+            "e8_dequantize_us": lambda st: gq.gq_e8_dequantize(root, d, norm, mean=mean,
+                                                               stream=st),
+        }
+        out["unfused"] = {k: round(_time_us(torch, stream, f, steps), 3) for k, f in parts.items()}
+        del codes, root
     return out
 
 

@@ -102,6 +102,28 @@ def test_pair_reduction_matches_oracle(level, node):
     assert np.array_equal(host(out)[:d], exp)
 
 
+def test_every_byte_pair():
+    """All 256 x 256 ordered pairs of code bytes (both zero encodings, every
+    sign and level combination), through the pair kernel at several tree
+    positions and through a two-leaf tree, bit-exact against the oracle."""
+    a = np.repeat(np.arange(256, dtype=np.uint8), 256)
+    b = np.tile(np.arange(256, dtype=np.uint8), 256)
+    a = np.concatenate([a, a[:3]])  # a ragged tail past the last full group of 8
+    b = np.concatenate([b, b[-3:]])
+    d = a.size
+    rb = gq.gq_e8_row_bytes(d)
+    pa, pb = np.zeros(rb, np.uint8), np.zeros(rb, np.uint8)
+    pa[:d], pb[:d] = a, b
+    ta, tb = torch.from_numpy(pa).to(DEV), torch.from_numpy(pb).to(DEV)
+    for seed, level, node in [(0, 1, 0), (2**64 - 1, 4, 3), (12345, 10, 0)]:
+        exp = oracle.e8_reduce_pair(a, b, seed, level, node)
+        out = gq.gq_e8_reduce_pair(ta, tb, d, seed, level, node)
+        assert np.array_equal(host(out)[:d], exp), (seed, level, node)
+    leaves = np.stack([pa, pb])
+    root = gq.gq_e8_tree(torch.from_numpy(leaves).to(DEV), 2, d, 7)
+    assert np.array_equal(host(root)[:d], oracle.e8_tree(np.stack([a, b]), 7))
+
+
 def test_largest_tree_and_edge_inputs():
     n, d = 1024, 64
     x = wl.random_rows(n, d, seed=4)
