@@ -748,7 +748,89 @@ __device__ __forceinline__ void accumulate_workers(const void *__restrict__ x, i
     }
 }
 
-template <int DT, int SCH, bool FACC>
+// Accumulators of the fused pass: int32, fp32 (exact while every partial
+// sum is an integer of magnitude <= 2^24), or packed int16 pairs.
+enum { kAccInt = 0, kAccF32 = 1, kAccPk16 = 2 };
+
+// Standard dithering with n s < 2^15: the per-coordinate sums fit int16,
+// so the magnitudes are formed with one 32-bit add each and pairs of
+// coordinates are signed and summed in packed 16-bit lanes.  With
+// sigma16 = sigma 2^16 and top16 = s 2^16, min(|x| pre sigma16, top16) equals
+// t 2^16 exactly (a power-of-two scaling of the same rounding; a t below
+// fp32's normal range gives lo = 0 and F < 2^16 either way), so
+// T = (uint32)(t 2^16) = lo 2^16 + (F >> 16).  Adding 0xFFFF - h, h the 16-bit
+// half of the uniform, carries into bit 16 iff F >> 16 > h, so the magnitude
+// lo + [h < F >> 16] is the high half of T + (0xFFFF - h).  A tie
+// (h == F >> 16) is settled with the second draw exactly as in the other
+// paths.  The sign is applied as a multiply by +-1 from the sign bit.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ i16x2 as_i16x2(uint32_t w) { return __builtin_bit_cast(i16x2, w); }
+
+template <int DT, bool PRE>
+__device__ __forceinline__ void accumulate_workers_pk16(const void *__restrict__ x, int64_t n,
+                                                        int64_t d, int64_t j0, bool vec,
+                                                        const QParams &q, uint32_t k0,
+                                                        uint32_t k1, int (&acc)[kPer])
+{
+    const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
+    const float sigma16 = q.sigma * 0x1p16f, top16 = q.top * 0x1p16f;
+    i16x2 acc2[kPer / 2];
+#pragma unroll
+    for (int p = 0; p < kPer / 2; ++p)
+        acc2[p] = as_i16x2(0u);
+    for (int64_t i = 0; i < n; ++i) {
+        float v[kPer];
+        load_group<DT>(x, i * d, j0, d, vec, v);
+        const uint4 A = philox10(make_uint4(blo, bhi, (uint32_t)i, 0u), k0, k1);
+        const uint32_t Aw[kPer / 2] = {A.x, A.y, A.z, A.w};
+        uint32_t T[kPer];
+        bool tie = false;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            float a = fabsf(v[k]);
+            if (PRE)
+                a = a * q.pre;
+            T[k] = (uint32_t)fminf(a * sigma16, top16);
+            tie |= (half16(A, k) == (T[k] & 0xFFFFu));
+        }
+        uint32_t m2[kPer / 2];
+#pragma unroll
+        for (int p = 0; p < kPer / 2; ++p) {
+            const uint32_t hx = ~Aw[p]; // 0xFFFF - h of both coordinates
+            const uint32_t S0 = T[2 * p] + (hx & 0xFFFFu), S1 = T[2 * p + 1] + (hx >> 16);
+            m2[p] = __builtin_amdgcn_perm(S1, S0, 0x07060302u); // high halves of S0, S1
+        }
+        if (tie) {
+            const uint4 B = philox10(make_uint4(blo, bhi, (uint32_t)i, 1u), k0, k1);
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                if (half16(A, k) == (T[k] & 0xFFFFu)) {
+                    float lo, step;
+                    uint32_t Fh, F;
+                    bracket<GQ_SCHEME_L, PRE>(v[k], q, lo, step, Fh, &F);
+                    if (half16(B, k) < (F & 0xFFFFu))
+                        m2[k >> 1] += (k & 1) ? 0x00010000u : 0x00000001u;
+                }
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < kPer / 2; ++p) {
+            // +1 / -1 per lane from the sign bits of the two inputs
+            const uint32_t sb = (__float_as_uint(v[2 * p]) >> 16) | (__float_as_uint(v[2 * p + 1]) & 0xFFFF0000u);
+            const i16x2 sgn = (as_i16x2(sb) >> (i16x2)15) | (i16x2)1;
+            acc2[p] += as_i16x2(m2[p]) * sgn;
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < kPer / 2; ++p) {
+        acc[2 * p] = acc2[p].x;
+        acc[2 * p + 1] = acc2[p].y;
+    }
+}
+
+template <int DT, int SCH, int ACC>
 __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restrict__ x, int64_t n,
                                                             int64_t d, int s, uint64_t seed,
                                                             const float *__restrict__ norm_dev,
@@ -767,11 +849,16 @@ __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restri
     if (!q.zero && j0 < d) {
         const bool vec = (d & 7) == 0;
         const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-        if (q.prescale)
-            accumulate_workers<DT, SCH, true, FACC>(x, n, d, j0, vec, q, k0, k1, accf, acc);
+        if constexpr (ACC == kAccPk16) {
+            if (q.prescale)
+                accumulate_workers_pk16<DT, true>(x, n, d, j0, vec, q, k0, k1, acc);
+            else
+                accumulate_workers_pk16<DT, false>(x, n, d, j0, vec, q, k0, k1, acc);
+        } else if (q.prescale)
+            accumulate_workers<DT, SCH, true, ACC == kAccF32>(x, n, d, j0, vec, q, k0, k1, accf, acc);
         else
-            accumulate_workers<DT, SCH, false, FACC>(x, n, d, j0, vec, q, k0, k1, accf, acc);
-        if (FACC) {
+            accumulate_workers<DT, SCH, false, ACC == kAccF32>(x, n, d, j0, vec, q, k0, k1, accf, acc);
+        if (ACC == kAccF32) {
 #pragma unroll
             for (int k = 0; k < kPer; ++k)
                 acc[k] = (int)accf[k];
@@ -1377,19 +1464,24 @@ int32_t launch_compress(const void *x, int32_t dtype, int64_t n, int64_t d, int3
         return ok();
     const dim3 grid((unsigned)tiles), block(kThreads);
     uint8_t *cs = (uint8_t *)code_sum;
-    // fp32 accumulation is exact while every partial sum stays within 2^24
-    const bool facc = n * top_code(s, scheme) <= ((int64_t)1 << 24);
-#define GQ_COMPRESS(DT, SCH, FA) \
-    k_compress_mean<DT, SCH, FA><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, mean, cs, W)
-#define GQ_COMPRESS_DT(DT)                                                        \
-    do {                                                                          \
-        if (scheme == GQ_SCHEME_L)                                                \
-            facc ? GQ_COMPRESS(DT, GQ_SCHEME_L, true) : GQ_COMPRESS(DT, GQ_SCHEME_L, false); \
-        else                                                                      \
-            facc ? GQ_COMPRESS(DT, GQ_SCHEME_E, true) : GQ_COMPRESS(DT, GQ_SCHEME_E, false); \
+    // fp32 accumulation is exact while every partial sum stays within 2^24;
+    // packed int16 sums for bf16 standard dithering while n s < 2^15
+    const int64_t nm = n * top_code(s, scheme);
+    const bool facc = nm <= ((int64_t)1 << 24);
+    const bool pk16 = dtype == GQ_IN_BF16 && scheme == GQ_SCHEME_L && nm < ((int64_t)1 << 15);
+#define GQ_COMPRESS(DT, SCH, ACC) \
+    k_compress_mean<DT, SCH, ACC><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, mean, cs, W)
+#define GQ_COMPRESS_DT(DT)                                                                      \
+    do {                                                                                        \
+        if (scheme == GQ_SCHEME_L)                                                              \
+            facc ? GQ_COMPRESS(DT, GQ_SCHEME_L, kAccF32) : GQ_COMPRESS(DT, GQ_SCHEME_L, kAccInt); \
+        else                                                                                    \
+            facc ? GQ_COMPRESS(DT, GQ_SCHEME_E, kAccF32) : GQ_COMPRESS(DT, GQ_SCHEME_E, kAccInt); \
     } while (0)
     if (dtype == GQ_IN_F32)
         GQ_COMPRESS_DT(GQ_IN_F32);
+    else if (pk16)
+        GQ_COMPRESS(GQ_IN_BF16, GQ_SCHEME_L, kAccPk16);
     else
         GQ_COMPRESS_DT(GQ_IN_BF16);
 #undef GQ_COMPRESS_DT
