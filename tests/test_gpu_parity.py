@@ -115,6 +115,29 @@ def test_every_code_width(scheme, s, n):
         assert np.array_equal(host(fsum), host(csum)), W
 
 
+@pytest.mark.parametrize("n,s", [(1, 32767), (2, 16383), (2, 16384), (3, 10922), (9, 3641)])
+def test_packed_int16_sum_limits(n, s):
+    """bf16 standard dithering sums pairs of coordinates in int16 lanes while
+    n s < 2^15: sums at +-n s exactly (every input at the norm, q = p = inf),
+    mixed signs, ties and a ragged tail, on both sides of the limit."""
+    d = 4099
+    x = wl.random_rows(n, d, seed=s, dtype="f32", scale=1.0)
+    x[:, :300] = 8.0   # the largest magnitude: t = s exactly, sum n s
+    x[:, 300:600] = -8.0
+    x[0, 600] = 8.0
+    x = wl.f32_to_bf16_bits(x)
+    W = gq.gq_min_code_bits(n, s, "L")
+    for q, p, seed in ((INF, INF, 5), (2.0, 2.0, 6), (INF, 2.0, 2**64 - 3)):
+        N, sums, mean = oracle.compress_mean(x, s, q, p, SCH["L"], seed)
+        gmean, gnorm, gsum = gq.gq_compress_mean(to_dev(x), s, q, p, "L", seed, code_bits=W,
+                                                 want_code_sum=True)
+        check_norm(host(gnorm)[0], N)
+        if q == INF and p == INF:
+            assert sums[:300].tolist() == [n * s] * 300 and sums[300:600].tolist() == [-n * s] * 300
+        assert np.array_equal(host(gsum), oracle.pack(sums.astype(np.int32), W)[0])
+        assert np.array_equal(host(gmean), mean)
+
+
 def test_worker_base_shards_reproduce_the_whole():
     n, d, s = 6, 3000, 9
     x = wl.random_rows(n, d, seed=5)
