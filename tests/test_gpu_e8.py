@@ -124,6 +124,26 @@ def test_every_byte_pair():
     assert np.array_equal(host(root)[:d], oracle.e8_tree(np.stack([a, b]), 7))
 
 
+def test_dense_sweep_of_t_bit_patterns():
+    """Every 61st fp32 bit pattern of t in [0, 1] (about 17M values across all
+    exponents, subnormals included, with mixed signs), quantized with N = 1 so
+    that t = |x| exactly: the standalone quantization kernel and the fused
+    path (n = 1, where the root is the leaf codes) against the oracle."""
+    tb = np.arange(0, 0x3F800000 + 1, 61, dtype=np.uint32)
+    tb[-1] = 0x3F800000  # t = 1: the norm under q = p = inf
+    sign = (np.random.default_rng(3).random(tb.size) < 0.5).astype(np.uint32) << 31
+    x = (tb | sign).view(np.float32).reshape(1, -1)
+    d = x.shape[1]
+    seed = 0xDEADBEEF12345
+    exp = oracle.e8_quantize(x, np.float32(1.0), seed)[0]
+    xd = to_dev(x)
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    assert np.array_equal(rows(gq.gq_e8_quantize(xd, one, seed), 1, d)[0], exp)
+    gmean, gnorm, groot = gq.gq_e8_compress_mean(xd, INF, INF, seed, want_root=True)
+    assert host(gnorm)[0] == 1.0
+    assert np.array_equal(host(groot)[:d], exp)
+
+
 def test_largest_tree_and_edge_inputs():
     n, d = 1024, 64
     x = wl.random_rows(n, d, seed=4)
