@@ -26,10 +26,18 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
+# A compile normally takes well under a minute; a stalled compiler fails the
+# build instead of blocking it.
+BUILD_TIMEOUT_S = 900
+
+
 def build_library(verbose: bool = False) -> str:
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=BUILD_TIMEOUT_S)
+    except subprocess.TimeoutExpired as e:
+        raise RuntimeError(f"hipcc did not finish within {BUILD_TIMEOUT_S} s") from e
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
     if verbose and r.stderr:

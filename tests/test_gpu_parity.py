@@ -314,6 +314,37 @@ def test_workload_full_size(key):
 
 
 # ---------------------------------------------------------------------------
+# fp32 inputs above 1 GiB take the one-shot norm pass (16 KB blocks, a
+# middle reduction): ragged, unaligned and aligned rows, every kind of order,
+# and the per-worker norms of the ablation; a bf16 input of the same size
+# stays on the chunk-major pass.
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("n,d,dtype,q,p", [(3, 89_478_487, "f32", 2.0, 2.0),
+                                           (5, 53_687_093, "f32", INF, 2.0),
+                                           (1, 268_435_464, "f32", 2.0, INF),
+                                           (4, 67_108_869, "f32", 1.5, 3.0),
+                                           (5, 107_374_185, "bf16", INF, 2.0)])
+def test_large_input_norm(n, d, dtype, q, p):
+    log(f"large-input norm n={n} d={d} {dtype} q={q} p={p}")
+    x = np.empty((n, d), np.float32)
+    for i in range(n):
+        x[i] = wl.random_rows(1, d, seed=d + i, scale=0.01)[0]
+    if dtype == "bf16":
+        x = wl.f32_to_bf16_bits(x)
+    N, _ = oracle.global_norm_rows(x, q, p, threads=min(16, n))
+    xd = to_dev(x)
+    gN = np.float32(host(gq.gq_global_norm(xd, q, p))[0])
+    assert abs(float(gN) - float(N)) <= 1e-6 * float(N)
+    assert gN == N, f"norm differs in the last bit ({gN!r} vs {N!r})"
+    if q == 2.0 and p == 2.0:
+        _, gnorms, _ = gq.gq_qsgd_local_mean(xd, 3, 1)
+        assert np.array_equal(host(gnorms), oracle.local_norms(x, threads=n))
+    del xd, x
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
 # General real orders (fp64 pow): the norm within 1e-6 relative; codes and
 # means bit-exact whenever the fp32 norm agrees to the bit
 
