@@ -83,9 +83,10 @@ int32_t gq_min_code_bits(int64_t n, int32_t s, int32_t scheme);
  * Returns -1 for d < 0 or W outside [1, 32].                               */
 int64_t gq_code_row_bytes(int64_t d, int32_t code_bits);
 
-/* Device workspace needed by gq_global_norm, gq_compress_mean and
- * gq_qsgd_local_mean for an [n][d] input (per-block partial norms and the
- * per-worker norms).  Returns -1 for invalid sizes.                        */
+/* Device workspace needed by gq_global_norm, gq_compress_mean,
+ * gq_qsgd_local_mean and gq_e8_compress_mean for an [n][d] input of either
+ * type (per-block partial norms and the per-worker norms).  Returns -1 for
+ * invalid sizes.                                                           */
 int64_t gq_workspace_bytes(int64_t n, int64_t d);
 
 /* Global (q,p)-norm of the concatenation (Sec. 2 notation):
@@ -96,8 +97,8 @@ int64_t gq_workspace_bytes(int64_t n, int64_t d);
  *   w_i = m_i, sqrt(S_i) (q = 2) or S_i^(1/q); N = fp32 of max_i w_i (p = inf),
  *   sqrt(sum_i w_i^2) (p = 2) or (sum_i w_i^p)^(1/p).
  *   Writes N to norm_dev[0] (one float, device).
- * The reduction tree is fixed by (n, d), so repeated calls give identical
- * bits.  d == 0 gives N = 0.                                               */
+ * The reduction tree is fixed by (n, d) and the input type, so repeated
+ * calls give identical bits.  d == 0 gives N = 0.                          */
 int32_t gq_global_norm(const void *x, int32_t dtype, int64_t n, int64_t d, float q, float p,
                        float *norm_dev, void *workspace, int64_t workspace_bytes, void *stream);
 
