@@ -85,8 +85,10 @@ int64_t gq_code_row_bytes(int64_t d, int32_t code_bits);
 
 /* Device workspace needed by gq_global_norm, gq_compress_mean,
  * gq_qsgd_local_mean and gq_e8_compress_mean for an [n][d] input of either
- * type (per-block partial norms and the per-worker norms).  Returns -1 for
- * invalid sizes.                                                           */
+ * type (per-block partial norms and the per-worker norms).  Its contents
+ * need no initialization and are scratch between calls; calls that may run
+ * concurrently (on different streams) need separate workspaces.  Returns -1
+ * for invalid sizes.                                                       */
 int64_t gq_workspace_bytes(int64_t n, int64_t d);
 
 /* Global (q,p)-norm of the concatenation (Sec. 2 notation):
