@@ -414,13 +414,22 @@ __device__ __forceinline__ void store_mean8(float *__restrict__ mean, int64_t j0
     }
 }
 
+// Orders one wave's LDS accesses before and after a phase of the wave-level
+// packing (a wave's LDS operations execute in order; this keeps the
+// compiler from moving them across the phase boundary).
+__device__ __forceinline__ void wave_lds_fence()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Store 8 W-bit fields per thread (thread-major: coordinate tile*2048 +
 // 8*t + k) into one packed row.  W = 8/16/32: direct vector stores.  Other
-// W: fields go through LDS and each thread assembles whole output words, so
-// global stores stay coalesced.  Every thread of the block must call this.
-// Bytes past the row's end are never written; pad fields are zero.
+// W: each wave assembles its whole words in LDS and writes them with 16-byte
+// stores.  Every thread of the block must call this.  Bytes past the row's
+// end are never written; pad fields are zero.
 template <bool NT = true>
-__device__ void store_tile_packed(uint32_t *lds, const int (&val)[kPer], int W, uint8_t *row,
+__device__ __forceinline__ void store_tile_packed(uint32_t *lds, const int (&val)[kPer], int W, uint8_t *row,
                                   int64_t tile, int64_t rbytes)
 {
     const int t = threadIdx.x;
@@ -470,37 +479,46 @@ __device__ void store_tile_packed(uint32_t *lds, const int (&val)[kPer], int W, 
         }
         return;
     }
+    // Other widths, one wave at a time (no block barrier): wave v holds the
+    // tile's coordinates [512 v, 512 v + 512), whose bits [512 v W,
+    // 512 (v + 1) W) are 16 W whole words.  The wave clears its own LDS
+    // region of 16 W words, ORs every field into place (LDS atomics; a field
+    // may straddle two words), then writes the region out as 16-byte stores.
+    const int lane = t & 63, wave = t >> 6;
+    const int nw = 16 * W;
+    uint32_t *wl = lds + wave * nw;
+    for (int j = lane; j < nw; j += 64)
+        wl[j] = 0u;
+    wave_lds_fence();
     const uint32_t mask = (1u << W) - 1u;
-    uint4 *l4 = (uint4 *)lds;
-    l4[2 * t] = make_uint4(val[0] & mask, val[1] & mask, val[2] & mask, val[3] & mask);
-    l4[2 * t + 1] = make_uint4(val[4] & mask, val[5] & mask, val[6] & mask, val[7] & mask);
-    __syncthreads();
-    const int words = 64 * W; // 2048 W bits
-    const int64_t w0 = tile * words;
-    const int64_t rwords = rbytes / 4;
-    uint32_t *rw = (uint32_t *)row;
-    for (int w = t; w < words; w += kThreads) {
-        if (w0 + w >= rwords)
-            break;
-        const int bit0 = w * 32;
-        const int e_last = (bit0 + 31) / W;
-        uint32_t word = 0;
-        for (int e = bit0 / W; e <= e_last; ++e) {
-            const int sh = e * W - bit0; // in (-W, 32)
-            const uint32_t f = lds[e];
-            word |= (sh >= 0) ? (f << sh) : (f >> -sh);
-        }
-        if (NT)
-            __builtin_nontemporal_store(word, rw + w0 + w);
-        else
-            rw[w0 + w] = word;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int bit = (lane * kPer + k) * W;
+        const int wi = bit >> 5, sh = bit & 31;
+        const uint32_t f = (uint32_t)val[k] & mask;
+        atomicOr(&wl[wi], f << sh);
+        if (sh + W > 32)
+            atomicOr(&wl[wi + 1], f >> (32 - sh));
     }
-    __syncthreads();
+    wave_lds_fence();
+    const int64_t wbase = tile * 64 * W + (int64_t)wave * nw; // first word of the region
+    for (int u = lane; u < 4 * W; u += 64) {
+        const int64_t off = (wbase + 4 * u) * 4;
+        if (off < rbytes) {
+            const uint4 o = ((const uint4 *)wl)[u];
+            if (NT)
+                nt_store(row + off, o);
+            else
+                *(uint4 *)(row + off) = o;
+        }
+    }
+    wave_lds_fence();
 }
 
 // Inverse of store_tile_packed: 8 sign-extended fields per thread.  Fields
-// past the row's end read as 0.  Every thread of the block must call this.
-__device__ void load_tile_fields(uint32_t *lds, const uint8_t *row, int W, int64_t tile,
+// past the row's end read as 0.  Every thread of the block must call this;
+// the LDS staging is per wave, so no block barrier is taken.
+__device__ __forceinline__ void load_tile_fields(uint32_t *lds, const uint8_t *row, int W, int64_t tile,
                                  int64_t rbytes, int (&val)[kPer])
 {
     const int t = threadIdx.x;
@@ -535,22 +553,27 @@ __device__ void load_tile_fields(uint32_t *lds, const uint8_t *row, int W, int64
         val[4] = (int)b.x; val[5] = (int)b.y; val[6] = (int)b.z; val[7] = (int)b.w;
         return;
     }
-    const int words = 64 * W;
-    const int64_t w0 = tile * words;
-    const int64_t rwords = rbytes / 4;
-    const uint32_t *rw = (const uint32_t *)row;
-    for (int w = t; w < words; w += kThreads)
-        lds[w] = (w0 + w < rwords) ? rw[w0 + w] : 0u;
-    __syncthreads();
+    // Other widths, one wave at a time (no block barrier): the wave loads
+    // its 16 W words (see store_tile_packed) with 16-byte loads into its own
+    // LDS region, then every lane extracts its 8 fields from a 64-bit window.
+    const int lane = t & 63, wave = t >> 6;
+    const int nw = 16 * W;
+    uint32_t *wl = lds + wave * nw;
+    const int64_t wbase = tile * 64 * W + (int64_t)wave * nw;
+    for (int u = lane; u < 4 * W; u += 64) {
+        const int64_t off = (wbase + 4 * u) * 4;
+        ((uint4 *)wl)[u] = off < rbytes ? *(const uint4 *)(row + off) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    wave_lds_fence();
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-        const int bit = (t * kPer + k) * W;
+        const int bit = (lane * kPer + k) * W;
         const int wi = bit >> 5, sh = bit & 31;
-        const uint64_t two = (uint64_t)lds[wi] | ((uint64_t)(wi + 1 < words ? lds[wi + 1] : 0u) << 32);
+        const uint64_t two = (uint64_t)wl[wi] | ((uint64_t)(wi + 1 < nw ? wl[wi + 1] : 0u) << 32);
         const uint32_t f = (uint32_t)(two >> sh);
         val[k] = (int)(f << (32 - W)) >> (32 - W);
     }
-    __syncthreads();
+    wave_lds_fence();
 }
 
 __device__ __forceinline__ double wave_sum(double v)
@@ -1002,7 +1025,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restri
                                                             float *__restrict__ mean,
                                                             uint8_t *__restrict__ code_sum, int W)
 {
-    __shared__ uint32_t lds[kTile];
+    __shared__ alignas(16) uint32_t lds[kTile];
     // Reverse of pass 1's order: pass 1's blocks finish on the last chunks of
     // every row, so starting pass 2 there re-reads data the memory-side cache
     // still holds (measured: -7% time on an 0.8 GB input, neutral on 7-16 GB).
@@ -1076,7 +1099,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void *__restrict__ 
                                                        uint8_t *__restrict__ codes, int W,
                                                        int64_t rbytes, int64_t tiles)
 {
-    __shared__ uint32_t lds[kTile];
+    __shared__ alignas(16) uint32_t lds[kTile];
     const int64_t i = blockIdx.x / tiles, tile = blockIdx.x % tiles;
     const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
     const QParams q = make_qparams(*norm_dev, n, s, SCH);
@@ -1101,7 +1124,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize2(const void *__restrict__
                                                         uint8_t *__restrict__ codes, int W,
                                                         int64_t rbytes, int64_t tiles)
 {
-    __shared__ uint32_t lds[kTile];
+    __shared__ alignas(16) uint32_t lds[kTile];
     const int64_t pairs = (tiles + 1) / 2;
     const int64_t i = blockIdx.x / pairs, t0 = (blockIdx.x % pairs) * 2;
     const QParams q = make_qparams(*norm_dev, n, s, SCH);
@@ -1133,7 +1156,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_codes(const uint8_t *__rest
                                                            int64_t n, int W, int64_t rbytes,
                                                            uint8_t *__restrict__ out)
 {
-    __shared__ uint32_t lds[kTile];
+    __shared__ alignas(16) uint32_t lds[kTile];
     const int64_t tile = blockIdx.x;
     int acc[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int64_t i = 0; i < n; ++i) {
@@ -1158,7 +1181,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t *__restri
                                                          const float *__restrict__ norm_dev,
                                                          float *__restrict__ mean)
 {
-    __shared__ uint32_t lds[kTile];
+    __shared__ alignas(16) uint32_t lds[kTile];
     const int64_t tile = blockIdx.x;
     const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
     int v[kPer];
@@ -1184,7 +1207,7 @@ __global__ __launch_bounds__(kThreads) void k_local_mean(const void *__restrict_
                                                          uint8_t *__restrict__ codes, int W,
                                                          int64_t rbytes)
 {
-    __shared__ uint32_t lds[kTile];
+    __shared__ alignas(16) uint32_t lds[kTile];
     const int64_t tile = blockIdx.x;
     const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
     const bool vec = (d & 7) == 0;
