@@ -333,28 +333,32 @@ def main():
         "input_gen_s": round(gen_s, 2),
     }
     if args.unfused:
-        codes = torch.empty((n, gq.gq_code_row_bytes(d, w.code_bits)), dtype=torch.uint8,
-                            device=dev)
-        csum = torch.empty(gq.gq_code_row_bytes(d, w.code_bits), dtype=torch.uint8, device=dev)
+        def unfused_at(W, reps):
+            codes = torch.empty((n, gq.gq_code_row_bytes(d, W)), dtype=torch.uint8, device=dev)
+            csum = torch.empty(gq.gq_code_row_bytes(d, W), dtype=torch.uint8, device=dev)
 
-        def ustep():
-            gq.gq_global_norm(xd, w.q, w.p, norm=norm, workspace=ws, stream=stream)
-            gq.gq_quantize(xd, w.s, w.scheme, norm, w.seed, w.code_bits, codes=codes,
-                           stream=stream)
-            gq.gq_reduce_codes(codes, n, d, w.code_bits, code_sum=csum, stream=stream)
-            gq.gq_dequantize(csum, n, d, w.s, w.scheme, w.code_bits, norm, mean=mean,
-                             stream=stream)
-        for _ in range(3):
-            ustep()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.steps):
-            ustep()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ums = e0.elapsed_time(e1) / args.steps
-        out["unfused"] = {"ms_per_step": round(ums, 6),
-                          "input_GBs": round(in_bytes / (ums * 1e-3) / 1e9, 3)}
+            def ustep():
+                gq.gq_global_norm(xd, w.q, w.p, norm=norm, workspace=ws, stream=stream)
+                gq.gq_quantize(xd, w.s, w.scheme, norm, w.seed, W, codes=codes, stream=stream)
+                gq.gq_reduce_codes(codes, n, d, W, code_sum=csum, stream=stream)
+                gq.gq_dequantize(csum, n, d, w.s, w.scheme, W, norm, mean=mean, stream=stream)
+            for _ in range(3):
+                ustep()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                ustep()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ums = e0.elapsed_time(e1) / reps
+            del codes, csum
+            return {"ms_per_step": round(ums, 6), "input_GBs": round(in_bytes / (ums * 1e-3) / 1e9, 3),
+                    "code_bits": W}
+        out["unfused"] = unfused_at(w.code_bits, args.steps)
+        wmin = gq.gq_min_code_bits(n, w.s, w.scheme)
+        if wmin != w.code_bits:
+            # the same pipeline with codes packed to the minimal width
+            out["unfused_min_width"] = unfused_at(wmin, args.steps)
     if args.e8:
         out["e8"] = e8_report(gq, torch, w, xd, stream, min(args.steps, 50), ws)
     if args.ablation or w.key == 5:
