@@ -515,6 +515,21 @@ __device__ __forceinline__ void store_tile_packed(uint32_t *lds, const int (&val
     wave_lds_fence();
 }
 
+// Lane `lane`'s 8 sign-extended W-bit fields from a wave's staged region of
+// nw words (the lane's fields start at bit 8 lane W).
+__device__ __forceinline__ void extract_fields_wave(const uint32_t *wl, int nw, int W, int lane,
+                                                    int (&val)[kPer])
+{
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int bit = (lane * kPer + k) * W;
+        const int wi = bit >> 5, sh = bit & 31;
+        const uint64_t two = (uint64_t)wl[wi] | ((uint64_t)(wi + 1 < nw ? wl[wi + 1] : 0u) << 32);
+        const uint32_t f = (uint32_t)(two >> sh);
+        val[k] = (int)(f << (32 - W)) >> (32 - W);
+    }
+}
+
 // Inverse of store_tile_packed: 8 sign-extended fields per thread.  Fields
 // past the row's end read as 0.  Every thread of the block must call this;
 // the LDS staging is per wave, so no block barrier is taken.
@@ -565,14 +580,7 @@ __device__ __forceinline__ void load_tile_fields(uint32_t *lds, const uint8_t *r
         ((uint4 *)wl)[u] = off < rbytes ? *(const uint4 *)(row + off) : make_uint4(0u, 0u, 0u, 0u);
     }
     wave_lds_fence();
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int bit = (lane * kPer + k) * W;
-        const int wi = bit >> 5, sh = bit & 31;
-        const uint64_t two = (uint64_t)wl[wi] | ((uint64_t)(wi + 1 < nw ? wl[wi + 1] : 0u) << 32);
-        const uint32_t f = (uint32_t)(two >> sh);
-        val[k] = (int)(f << (32 - W)) >> (32 - W);
-    }
+    extract_fields_wave(wl, nw, W, lane, val);
     wave_lds_fence();
 }
 
@@ -1159,12 +1167,49 @@ __global__ __launch_bounds__(kThreads) void k_reduce_codes(const uint8_t *__rest
     __shared__ alignas(16) uint32_t lds[kTile];
     const int64_t tile = blockIdx.x;
     int acc[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int64_t i = 0; i < n; ++i) {
-        int v[kPer];
-        load_tile_fields(lds, codes + i * rbytes, W, tile, rbytes, v);
+    if (W == 8 || W == 16 || W == 32) {
+        for (int64_t i = 0; i < n; ++i) {
+            int v[kPer];
+            load_tile_fields(lds, codes + i * rbytes, W, tile, rbytes, v);
 #pragma unroll
-        for (int k = 0; k < kPer; ++k)
-            acc[k] += v[k]; // exact when W holds n M; otherwise wraps below
+            for (int k = 0; k < kPer; ++k)
+                acc[k] += v[k]; // exact when W holds n M; otherwise wraps below
+        }
+    } else {
+        // the wave-level staging of load_tile_fields with the next row's
+        // 16-byte chunks (u = lane and lane + 64 of the 4 W) loaded into
+        // registers while the current row is extracted
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int nw = 16 * W, nq = 4 * W;
+        uint32_t *wl = lds + wave * nw;
+        const int64_t wbase = tile * 64 * W + (int64_t)wave * nw;
+        uint4 nxt[2];
+        auto fetch = [&](int64_t i) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int u = lane + 64 * h;
+                const int64_t off = (wbase + 4 * u) * 4;
+                nxt[h] = (u < nq && off < rbytes) ? *(const uint4 *)(codes + i * rbytes + off)
+                                                  : make_uint4(0u, 0u, 0u, 0u);
+            }
+        };
+        fetch(0);
+        for (int64_t i = 0; i < n; ++i) {
+            const uint4 cur0 = nxt[0], cur1 = nxt[1];
+            if (i + 1 < n)
+                fetch(i + 1);
+            if (lane < nq)
+                ((uint4 *)wl)[lane] = cur0;
+            if (lane + 64 < nq)
+                ((uint4 *)wl)[lane + 64] = cur1;
+            wave_lds_fence();
+            int v[kPer];
+            extract_fields_wave(wl, nw, W, lane, v);
+            wave_lds_fence();
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+                acc[k] += v[k];
+        }
     }
     if (W < 32) {
 #pragma unroll
