@@ -113,8 +113,9 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Pass-1 geometry: each row is cut into `chunks` ranges of `chunk_len`
 // coordinates (a multiple of the 2048-coordinate tile); one block per
-// (chunk, worker).  Depends on (n, d) only, so the partial-sum tree -- and
-// the norm's bits -- are the same on every call.
+// (chunk, worker).  It and the one-shot geometry below depend on (n, d) and
+// the input type only, so the partial-sum tree -- and the norm's bits --
+// are the same on every call.
 struct NormGeom {
     int64_t chunks, chunk_len, blocks;
 };

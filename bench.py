@@ -48,10 +48,11 @@ def parse():
 
 
 def source_hash() -> str:
-    h = hashlib.sha256()
-    with open(os.path.join(ROOT, "allreduce_compatible_gradient_amd", "csrc", "gq.hip"), "rb") as f:
-        h.update(f.read())
-    return h.hexdigest()[:16]
+    """Hash of the kernel source with // comments and whitespace removed, so
+    that only code changes invalidate a stored counter record."""
+    with open(os.path.join(ROOT, "allreduce_compatible_gradient_amd", "csrc", "gq.hip")) as f:
+        code = "".join(line.split("//", 1)[0].strip() for line in f)
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def traffic_for(workload_name: str):
