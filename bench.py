@@ -48,8 +48,9 @@ def parse():
 
 
 def source_hash() -> str:
-    """Hash of the kernel source with // comments and whitespace removed, so
-    that only code changes invalidate a stored counter record."""
+    """Hash of the kernel source with // comments, indentation and line
+    breaks removed, so that only code changes invalidate a stored counter
+    record."""
     with open(os.path.join(ROOT, "allreduce_compatible_gradient_amd", "csrc", "gq.hip")) as f:
         code = "".join(line.split("//", 1)[0].strip() for line in f)
     return hashlib.sha256(code.encode()).hexdigest()[:16]
