@@ -1,0 +1,88 @@
+"""The library only enqueues kernels (no memset, synchronization or
+allocation), so its calls can be captured in a HIP graph and replayed.
+Each replay is compared bit-exactly with the eager result, with eager work
+and synchronizations between the replays, and the eager result with the
+oracle."""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import allreduce_compatible_gradient_amd as gq  # noqa: E402
+import oracle  # noqa: E402
+import workloads as wl  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+INF = math.inf
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gq.lib()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+@pytest.mark.parametrize("n,d,s,q,p,scheme,W", [(4, 70_001, 7, 2.0, 2.0, "L", 6),
+                                                (8, 300_000, 127, 2.0, INF, "L", 11),
+                                                (16, 50_000, 8, 2.0, 2.0, "E", 13)])
+def test_graph_replays_match_eager(n, d, s, q, p, scheme, W):
+    x = wl.random_rows(n, d, seed=n + d)
+    xd = torch.from_numpy(x).to(DEV)
+    ws = torch.empty(gq.gq_workspace_bytes(n, d), dtype=torch.uint8, device=DEV)
+    mean = torch.empty(d, dtype=torch.float32, device=DEV)
+    norm = torch.empty(1, dtype=torch.float32, device=DEV)
+    csum = torch.empty(gq.gq_code_row_bytes(d, W), dtype=torch.uint8, device=DEV)
+    codes = torch.empty((n, gq.gq_code_row_bytes(d, W)), dtype=torch.uint8, device=DEV)
+    csum2 = torch.empty_like(csum)
+    mean2 = torch.empty_like(mean)
+    seed = 1234
+
+    def fused(st):
+        gq.gq_compress_mean(xd, s, q, p, scheme, seed, code_bits=W, want_code_sum=True, mean=mean,
+                            norm=norm, code_sum=csum, workspace=ws, stream=st)
+
+    def unfused(st):
+        gq.gq_quantize(xd, s, scheme, norm, seed, W, codes=codes, stream=st)
+        gq.gq_reduce_codes(codes, n, d, W, code_sum=csum2, stream=st)
+        gq.gq_dequantize(csum2, n, d, s, scheme, W, norm, mean=mean2, stream=st)
+
+    cur = torch.cuda.current_stream()
+    fused(cur)
+    unfused(cur)
+    ref = [host(t).copy() for t in (mean, norm, csum, codes, csum2, mean2)]
+    N, sums, omean = oracle.compress_mean(x, s, q, p, oracle.SCHEME_L if scheme == "L" else oracle.SCHEME_E,
+                                          seed)
+    assert np.float32(ref[1][0]) == N
+    assert np.array_equal(ref[0], omean)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        fused(side)
+        unfused(side)
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        fused(side)
+        unfused(side)
+    for rep in range(3):
+        for t in (mean, norm, csum, codes, csum2, mean2):
+            t.zero_()  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        got = [host(t) for t in (mean, norm, csum, codes, csum2, mean2)]
+        for a, b in zip(ref, got):
+            assert np.array_equal(a, b), rep
+        fused(cur)  # eager call between replays
+        torch.cuda.synchronize()
+    del graph
