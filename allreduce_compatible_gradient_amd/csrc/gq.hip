@@ -1034,7 +1034,12 @@ __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restri
                                                             float *__restrict__ mean,
                                                             uint8_t *__restrict__ code_sum, int W)
 {
-    __shared__ alignas(16) uint32_t lds[kTile];
+    // fp32: 32 KB of LDS caps residency at 5 blocks (20 waves) per CU.
+    // Fewer concurrent waves interleave fewer HBM read and write streams:
+    // measured -6% on this pass for fp32 at 0.8-16 GB (4 and 5 blocks alike,
+    // 6 no gain); bf16, bound by vector ALU work, needs the full residency
+    // (5 blocks: +15%).  Only the code-sum packing uses the first 8 KB.
+    __shared__ alignas(16) uint32_t lds[DT == GQ_IN_F32 ? 8192 : kTile];
     // Reverse of pass 1's order: pass 1's blocks finish on the last chunks of
     // every row, so starting pass 2 there re-reads data the memory-side cache
     // still holds (measured: -7% time on an 0.8 GB input, neutral on 7-16 GB).
@@ -1254,7 +1259,8 @@ __global__ __launch_bounds__(kThreads) void k_local_mean(const void *__restrict_
                                                          int64_t rbytes)
 {
     __shared__ alignas(16) uint32_t lds[kTile];
-    const int64_t tile = blockIdx.x;
+    // reverse of pass 1's order, as in the fused pass
+    const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;
     const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
     const bool vec = (d & 7) == 0;
     const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
