@@ -138,6 +138,28 @@ def test_packed_int16_sum_limits(n, s):
         assert np.array_equal(host(gmean), mean)
 
 
+@pytest.mark.parametrize("n,d,scheme,s,q,p", [(3000, 37, "L", 5, 2.0, 2.0),
+                                               (2049, 130, "E", 6, INF, INF),
+                                               (1500, 4100, "L", 127, 2.0, INF)])
+def test_many_workers(n, d, scheme, s, q, p):
+    """More workers than the finalize block has threads: its rows go in
+    several passes; the fused pass walks thousands of rows per coordinate."""
+    x = wl.random_rows(n, d, seed=n, scale=0.1)
+    W = gq.gq_min_code_bits(n, s, scheme)
+    N, sums, mean = oracle.compress_mean(x, s, q, p, SCH[scheme], 9)
+    xd = to_dev(x)
+    gmean, gnorm, gsum = gq.gq_compress_mean(xd, s, q, p, scheme, 9, code_bits=W,
+                                             want_code_sum=True)
+    check_norm(host(gnorm)[0], N)
+    assert np.array_equal(host(gsum), oracle.pack(sums.astype(np.int32), W)[0])
+    assert np.array_equal(host(gmean), mean)
+    if scheme == "L" and q == 2.0 and p == 2.0:
+        norms, codes, lmean = oracle.qsgd_local_mean(x, s, 9)
+        gl, gn, _ = gq.gq_qsgd_local_mean(xd, s, 9)
+        assert np.array_equal(host(gn), norms)
+        assert np.array_equal(host(gl), lmean)
+
+
 def test_worker_base_shards_reproduce_the_whole():
     n, d, s = 6, 3000, 9
     x = wl.random_rows(n, d, seed=5)
