@@ -35,6 +35,8 @@ SIGNATURES = {
     "gq_code_row_bytes": (_i64, [_i64, _i32]),
     "gq_workspace_bytes": (_i64, [_i64, _i64]),
     "gq_global_norm": (_i32, [_vp, _i32, _i64, _i64, _f32, _f32, _vp, _vp, _i64, _vp]),
+    "gq_norm_term": (_i32, [_vp, _i32, _i64, _i64, _f32, _f32, _vp, _vp, _i64, _vp]),
+    "gq_norm_from_term": (_i32, [_vp, _f32, _f32, _vp, _vp]),
     "gq_quantize": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _vp, _u64, _i64, _i32, _vp, _vp]),
     "gq_reduce_codes": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp]),
     "gq_dequantize": (_i32, [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
@@ -152,6 +154,28 @@ def gq_global_norm(x: torch.Tensor, q=2.0, p=2.0, *, norm=None, workspace=None, 
     ws = _workspace(workspace, n, d, x.device)
     _check(lib().gq_global_norm(_ptr(x), dt, n, d, _order(q), _order(p), _ptr(norm), _ptr(ws),
                                 ws.numel(), _stream(stream)))
+    return norm
+
+
+def gq_norm_term(x: torch.Tensor, q=2.0, p=2.0, *, term=None, workspace=None, stream=None):
+    """fp64 term of the (q,p)-norm over the rows of x (a shard of the workers);
+    returns a 1-element float64 device tensor.  Terms of disjoint shards combine
+    by sum (finite p) or max (p = inf)."""
+    dt = _input(x)
+    n, d = x.shape
+    term = torch.empty(1, dtype=torch.float64, device=x.device) if term is None else term
+    ws = _workspace(workspace, n, d, x.device)
+    _check(lib().gq_norm_term(_ptr(x), dt, n, d, _order(q), _order(p), _ptr(term), _ptr(ws),
+                              ws.numel(), _stream(stream)))
+    return term
+
+
+def gq_norm_from_term(term: torch.Tensor, q=2.0, p=2.0, *, norm=None, stream=None):
+    """The norm N from a term combined over shards; 1-element float32 device tensor."""
+    if term.dtype != torch.float64 or term.numel() < 1 or not term.is_cuda:
+        raise ValueError("term must be a float64 device tensor")
+    norm = torch.empty(1, dtype=torch.float32, device=term.device) if norm is None else norm
+    _check(lib().gq_norm_from_term(_ptr(term), _order(q), _order(p), _ptr(norm), _stream(stream)))
     return norm
 
 

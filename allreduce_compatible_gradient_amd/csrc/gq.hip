@@ -906,15 +906,29 @@ __device__ __forceinline__ double butterfly(double v, int width)
     return v;
 }
 
+// N from the combination `tot` over workers (the term): fp32 of tot for
+// (inf, inf) and of its square root for the other {2, inf} pairs; for GEN
+// orders fp32 of tot (p = inf), sqrt(tot) (p = 2) or tot^(1/p).
+template <bool QINF, bool PINF, bool GEN>
+__device__ __forceinline__ float norm_from_term(double tot, double pd)
+{
+    if (GEN)
+        return PINF ? (float)tot : (float)(pd == 2.0 ? sqrt(tot) : pow(tot, 1.0 / pd));
+    return (QINF && PINF) ? (float)tot : (float)sqrt(tot);
+}
+
 // GEN: (q, p) not both in {2, inf}: w_i = m_i, sqrt(S_i) (q = 2) or S_i^(1/q),
 // then N = max_i w_i, sqrt(sum_i w_i^2) (p = 2) or (sum_i w_i^p)^(1/p), in fp64.
+// With term_out set, the combination over workers (before the root) goes
+// there in fp64 instead of N to norm_out.
 template <bool QINF, bool PINF, bool LOCAL, bool GEN>
 __global__ __launch_bounds__(kFinThreads) void k_norm_finalize(const double *__restrict__ partials,
                                                                int64_t n, int64_t chunks,
                                                                double *__restrict__ per_worker,
                                                                float *__restrict__ norm_out, int s,
                                                                WorkerParams *__restrict__ params,
-                                                               double qd, double pd)
+                                                               double qd, double pd,
+                                                               double *__restrict__ term_out)
 {
     __shared__ double red[kFinThreads / 64];
     const int t = threadIdx.x, lane64 = t & 63, wave = t >> 6;
@@ -994,11 +1008,20 @@ __global__ __launch_bounds__(kFinThreads) void k_norm_finalize(const double *__r
         double tot = red[0];
         for (int w = 1; w < kFinThreads / 64; ++w)
             tot = combine<PINF>(tot, red[w]);
-        if (GEN)
-            norm_out[0] = PINF ? (float)tot : (float)(p2 ? sqrt(tot) : pow(tot, 1.0 / pd));
+        if (term_out)
+            term_out[0] = tot;
         else
-            norm_out[0] = (QINF && PINF) ? (float)tot : (float)sqrt(tot);
+            norm_out[0] = norm_from_term<QINF, PINF, GEN>(tot, pd);
     }
+}
+
+// N of the whole from the term combined over shards (one thread).
+template <bool QINF, bool PINF, bool GEN>
+__global__ __launch_bounds__(64) void k_norm_from_term(const double *__restrict__ term, double pd,
+                                                       float *__restrict__ norm_out)
+{
+    if (threadIdx.x == 0)
+        norm_out[0] = norm_from_term<QINF, PINF, GEN>(term[0], pd);
 }
 
 // ---------------------------------------------------------------------------
@@ -1880,7 +1903,8 @@ int32_t validate_ws(const void *ws, int64_t ws_bytes, int64_t n, int64_t d)
 
 // Enqueue pass 1 (partials + finalize).  Arguments already validated.
 int32_t launch_norm(const void *x, int32_t dtype, int64_t n, int64_t d, float q, float p,
-                    bool local, float *norm_out, void *ws, int s, hipStream_t st)
+                    bool local, float *norm_out, void *ws, int s, hipStream_t st,
+                    double *term_out = nullptr)
 {
     const NormGeom g = norm_geom(n, d);
     const OneShotGeom o = oneshot_geom(n, d, dtype == GQ_IN_F32 ? 4 : 2);
@@ -1932,7 +1956,7 @@ int32_t launch_norm(const void *x, int32_t dtype, int64_t n, int64_t d, float q,
     }
     const dim3 one(1), block(kFinThreads);
 #define GQ_FIN(QI, PI, LO, GE) \
-    k_norm_finalize<QI, PI, LO, GE><<<one, block, 0, st>>>(fin_in, n, fin_chunks, per_worker, norm_out, s, params, qd, pd)
+    k_norm_finalize<QI, PI, LO, GE><<<one, block, 0, st>>>(fin_in, n, fin_chunks, per_worker, norm_out, s, params, qd, pd, term_out)
     if (local)
         GQ_FIN(false, false, true, false);
     else if (gen) {
@@ -2036,6 +2060,38 @@ int32_t gq_global_norm(const void *x, int32_t dtype, int64_t n, int64_t d, float
         return fail(GQ_ERR_UNSUPPORTED, "q and p must be reals >= 1 or +inf");
     GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
     return launch_norm(x, dtype, n, d, q, p, false, norm_dev, workspace, 0, (hipStream_t)stream);
+}
+
+int32_t gq_norm_term(const void *x, int32_t dtype, int64_t n, int64_t d, float q, float p,
+                     double *term_dev, void *workspace, int64_t workspace_bytes, void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    if (!term_dev)
+        return fail(GQ_ERR_NULL, "term_dev is NULL");
+    if (!order_ok(q) || !order_ok(p))
+        return fail(GQ_ERR_UNSUPPORTED, "q and p must be reals >= 1 or +inf");
+    GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
+    return launch_norm(x, dtype, n, d, q, p, false, nullptr, workspace, 0, (hipStream_t)stream,
+                       term_dev);
+}
+
+int32_t gq_norm_from_term(const double *term_dev, float q, float p, float *norm_dev, void *stream)
+{
+    if (!term_dev || !norm_dev)
+        return fail(GQ_ERR_NULL, "term_dev and norm_dev must not be NULL");
+    if (!order_ok(q) || !order_ok(p))
+        return fail(GQ_ERR_UNSUPPORTED, "q and p must be reals >= 1 or +inf");
+    const bool qinf = is_inf_order(q), pinf = is_inf_order(p);
+    const bool gen = !((qinf || is_two(q)) && (pinf || is_two(p)));
+    const double pd = pinf ? 0.0 : (double)p;
+    hipStream_t st = (hipStream_t)stream;
+#define GQ_FROM(QI, PI, GE) k_norm_from_term<QI, PI, GE><<<dim3(1), dim3(64), 0, st>>>(term_dev, pd, norm_dev)
+    if (gen) {
+        if (pinf) GQ_FROM(false, true, true); else GQ_FROM(false, false, true);
+    } else if (qinf && pinf) GQ_FROM(true, true, false);
+    else GQ_FROM(false, false, false); // the other {2, inf} pairs: fp32(sqrt(term))
+#undef GQ_FROM
+    return check_launch("k_norm_from_term");
 }
 
 int32_t gq_quantize(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s, int32_t scheme,

@@ -104,6 +104,29 @@ int64_t gq_workspace_bytes(int64_t n, int64_t d);
 int32_t gq_global_norm(const void *x, int32_t dtype, int64_t n, int64_t d, float q, float p,
                        float *norm_dev, void *workspace, int64_t workspace_bytes, void *stream);
 
+/* The same norm over workers held in shards, e.g. one per device (Sec. 2
+ * notation; Sec. 6 places the norm before the quantized Allreduce).
+ * gq_norm_term writes to term_dev[0] (one double, device) the combination
+ * over its n rows that the norm takes before its root, with S_i, m_i and
+ * w_i as above:
+ *   (2,2): sum_i S_i    (inf,2): sum_i m_i^2    (2,inf): max_i S_i
+ *   (inf,inf): max_i m_i;  other orders: max_i w_i (p = inf),
+ *   sum_i w_i^2 (p = 2), sum_i w_i^p (other p).
+ * Terms of disjoint shards combine by SUM for finite p and by MAX for
+ * p = inf (one all-reduce of a double).  gq_norm_from_term then writes N
+ * of the combined term to norm_dev[0]: fp32 of it for (inf,inf) and for
+ * p = inf with other orders, of its square root for the other {2, inf}
+ * pairs and for p = 2, of its 1/p-th power otherwise.
+ * One shard holding every row reproduces gq_global_norm's N bit for bit.
+ * Over several shards N agrees within 1e-6 relative (exactly for
+ * q = p = inf): each shard's fp64 sums follow its own reduction tree,
+ * fixed by its (n, d), and a SUM over shards adds in its own order.
+ * Errors as gq_global_norm; gq_norm_from_term needs no workspace.         */
+int32_t gq_norm_term(const void *x, int32_t dtype, int64_t n, int64_t d, float q, float p,
+                     double *term_dev, void *workspace, int64_t workspace_bytes, void *stream);
+int32_t gq_norm_from_term(const double *term_dev, float q, float p, float *norm_dev,
+                          void *stream);
+
 /* Quantization (Sec. 3, Global-Q with the L or E levels), given the global
  * norm N in norm_dev[0]:
  *   pre = 2^64 if N < 2^-64 else 1 (exact);  L: sigma = fp32(s / (N pre)),

@@ -83,6 +83,29 @@ def test_global_norm_rejects(args, expect):
 
 
 @pytest.mark.parametrize("args,expect", [
+    ((NUL, 0, 4, 1000, 2.0, 2.0, A, A, WS, NUL), 1),      # x NULL
+    ((A, 0, 4, 1000, 2.0, 2.0, NUL, A, WS, NUL), 1),      # term NULL
+    ((A, 5, 4, 1000, 2.0, 2.0, A, A, WS, NUL), 2),        # dtype
+    ((A, 0, 0, 1000, 2.0, 2.0, A, A, WS, NUL), 2),        # n = 0
+    ((A, 0, 4, 1000, 0.5, 2.0, A, A, WS, NUL), 3),        # q < 1
+    ((A, 0, 4, 1000, 2.0, math.nan, A, A, WS, NUL), 3),   # p NaN
+    ((U, 0, 4, 1000, 2.0, 2.0, A, A, WS, NUL), 6),        # x misaligned
+    ((A, 0, 4, 1000, 2.0, 2.0, A, A, WS - 1, NUL), 5),    # workspace too small
+])
+def test_norm_term_rejects(args, expect):
+    assert gq.lib().gq_norm_term(*args) == expect
+    assert gq.lib().gq_last_error().decode() != ""
+
+
+def test_norm_from_term_rejects():
+    L = gq.lib()
+    assert L.gq_norm_from_term(NUL, 2.0, 2.0, A, NUL) == 1
+    assert L.gq_norm_from_term(A, 2.0, 2.0, NUL, NUL) == 1
+    assert L.gq_norm_from_term(A, 0.5, 2.0, A, NUL) == 3
+    assert L.gq_norm_from_term(A, 2.0, -math.inf, A, NUL) == 3
+
+
+@pytest.mark.parametrize("args,expect", [
     ((A, 0, 4, 100, 0, 0, A, 1, 0, 8, A, NUL), 2),        # s = 0
     ((A, 0, 4, 100, 7, 2, A, 1, 0, 8, A, NUL), 2),        # scheme 2
     ((A, 0, 4, 100, 32, 1, A, 1, 0, 32, A, NUL), 2),      # E with s = 32
