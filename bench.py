@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
     ap.add_argument("--unfused", action="store_true", help="also time the four-call unfused path")
+    ap.add_argument("--bucket", action="store_true",
+                    help="also time one device's share of a data-parallel gradient bucket "
+                         "(1, 25 and 100 MB of worker 0's row)")
     ap.add_argument("--e8", action="store_true",
                     help="also measure the 8-bit exponential format: its pair reduction against "
                          "fp32/uint8 sums (omega) and the fused tree path on this workload")
@@ -180,6 +183,52 @@ def e8_report(gq, torch, w, xd, stream, steps, ws):
         }
         out["unfused"] = {k: round(_time_us(torch, stream, f, steps), 3) for k, f in parts.items()}
         del codes, root
+    return out
+
+
+def bucket_report(gq, torch, w, xd, stream, steps):
+    """One device's share of a data-parallel gradient bucket, device 0 of
+    n = w.n workers: the fp64 norm term of its bucket, N from the term (after
+    what would be an all-reduce of that double), its codes at its worker
+    index in the width that holds a sum of n codes, and the mean from the
+    summed code row (after what would be the integer all-reduce; here the
+    device's own row stands in for the sum).  The two all-reduces are not
+    run: this build uses one GPU.  Buckets are the leading 1, 25 and 100 MB
+    of worker 0's row, timed as graph replays of the five launches."""
+    out = {}
+    W = gq.gq_min_code_bits(w.n, w.s, w.scheme)
+    for label, nbytes in (("1MB", 1 << 20), ("25MB", 25 << 20), ("100MB", 100 << 20)):
+        db = min(nbytes // w.elem_bytes, w.d)
+        b = xd[0, :db].clone().view(1, db)
+        ws = torch.empty(gq.gq_workspace_bytes(1, db), dtype=torch.uint8, device=xd.device)
+        term = torch.empty(1, dtype=torch.float64, device=xd.device)
+        norm = torch.empty(1, dtype=torch.float32, device=xd.device)
+        codes = torch.empty((1, gq.gq_code_row_bytes(db, W)), dtype=torch.uint8, device=xd.device)
+        mean = torch.empty(db, dtype=torch.float32, device=xd.device)
+        parts = {
+            "norm_term_us": lambda st: gq.gq_norm_term(b, w.q, w.p, term=term, workspace=ws,
+                                                       stream=st),
+            "norm_from_term_us": lambda st: gq.gq_norm_from_term(term, w.q, w.p, norm=norm,
+                                                                 stream=st),
+            "quantize_us": lambda st: gq.gq_quantize(b, w.s, w.scheme, norm, w.seed, W,
+                                                     worker_base=0, codes=codes, stream=st),
+            "dequantize_us": lambda st: gq.gq_dequantize(codes[0], w.n, db, w.s, w.scheme, W,
+                                                         norm, mean=mean, stream=st),
+        }
+
+        def share(st):
+            for f in parts.values():
+                f(st)
+        t = _time_us(torch, stream, share, steps)
+        row_bytes = gq.gq_code_row_bytes(db, W)
+        # algorithmic bytes: the bucket read twice, codes written and read, the mean written
+        alg = 2 * db * w.elem_bytes + 2 * row_bytes + 4 * db
+        out[label] = {"elements": db, "code_bits": W, "us": round(t, 3),
+                      "bucket_GBs": round(db * w.elem_bytes / (t * 1e-6) / 1e9, 3),
+                      "alg_GBs": round(alg / (t * 1e-6) / 1e9, 3),
+                      "code_bytes": row_bytes,
+                      **{k: round(_time_us(torch, stream, f, steps), 3) for k, f in parts.items()}}
+        del b, ws, codes, mean
     return out
 
 
@@ -361,6 +410,8 @@ def main():
         if wmin != w.code_bits:
             # the same pipeline with codes packed to the minimal width
             out["unfused_min_width"] = unfused_at(wmin, args.steps)
+    if args.bucket:
+        out["bucket"] = bucket_report(gq, torch, w, xd, stream, min(args.steps, 100))
     if args.e8:
         out["e8"] = e8_report(gq, torch, w, xd, stream, min(args.steps, 50), ws)
     if args.ablation or w.key == 5:
