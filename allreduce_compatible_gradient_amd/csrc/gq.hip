@@ -1483,6 +1483,20 @@ __device__ __forceinline__ void e8_half_hi4(uint32_t w, uint32_t *hi)
         hi[b] = ((1022u - ((g4 >> (8 * b)) & 0xFFu)) << 20) | ((w << (24 - 8 * b)) & 0x80000000u);
 }
 
+// The same half values for all 256 code bytes, one LDS entry per thread of
+// a 256-thread block (1 KB), then a block barrier.  Decoding a byte through
+// this table takes one address computation instead of the byte-parallel
+// arithmetic above (~90 of ~255 VALU instructions of an 8-coordinate
+// combine); LDS issue is far below the VALU time it replaces.
+__device__ __forceinline__ void e8_fill_half_table(uint32_t *tab)
+{
+    static_assert(kThreads == 256, "one table entry per thread");
+    uint32_t hi[4];
+    e8_half_hi4(threadIdx.x, hi);
+    tab[threadIdx.x] = hi[0];
+    __syncthreads();
+}
+
 // Main-path rounding of one coordinate to a code.  X holds the biased
 // exponent of the value in bits 16 and up and the top 16 fraction bits
 // (F >> 16) below; base - exponent is the index of the lower level.  Adding
@@ -1566,17 +1580,18 @@ __device__ __forceinline__ uint2 pack_bytes(const uint32_t (&c)[kPer])
 // with the same draws and lazy second draw as the quantization.  Main path:
 // the parent's fp64 high word gives X (exponent and top fraction bits; for
 // +-2^-127, between the level 0 and 2^-126, F >> 16 = 2^15 is set in).
-__device__ __forceinline__ uint2 e8_combine(const uint2 &a, const uint2 &b, uint32_t blo,
-                                            uint32_t bhi, uint32_t node, uint32_t level,
-                                            uint32_t k0, uint32_t k1)
+__device__ __forceinline__ uint2 e8_combine(const uint32_t *tab, const uint2 &a, const uint2 &b,
+                                            uint32_t blo, uint32_t bhi, uint32_t node,
+                                            uint32_t level, uint32_t k0, uint32_t k1)
 {
     const uint4 A = philox10(make_uint4(blo, bhi, node, 2u * level), k0, k1);
     const uint32_t Ac[kPer / 2] = {~A.x, ~A.y, ~A.z, ~A.w};
     uint32_t ha[kPer], hb[kPer];
-    e8_half_hi4(a.x, ha);
-    e8_half_hi4(a.y, ha + 4);
-    e8_half_hi4(b.x, hb);
-    e8_half_hi4(b.y, hb + 4);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        ha[k] = tab[byte_of(a, k)];
+        hb[k] = tab[byte_of(b, k)];
+    }
     double v[kPer];
     uint32_t c[kPer];
     bool tie = false;
@@ -1605,8 +1620,9 @@ __device__ __forceinline__ uint2 e8_combine(const uint2 &a, const uint2 &b, uint
 // Binary-counter tree: leaf i enters; while bit l of i is set, it is combined
 // with the stored left sibling at level l into their parent (level l + 1,
 // node i >> (l + 1)).  The same pairs as the level-by-level tree.
-__device__ __forceinline__ uint2 e8_push(uint2 (&st)[kE8MaxLevels + 1], uint2 cur, int64_t i,
-                                         uint32_t blo, uint32_t bhi, uint32_t k0, uint32_t k1)
+__device__ __forceinline__ uint2 e8_push(const uint32_t *tab, uint2 (&st)[kE8MaxLevels + 1],
+                                         uint2 cur, int64_t i, uint32_t blo, uint32_t bhi,
+                                         uint32_t k0, uint32_t k1)
 {
     // constant trip count (no early exit) so the stack stays in registers;
     // i is wave-uniform, so every branch here is uniform
@@ -1615,8 +1631,8 @@ __device__ __forceinline__ uint2 e8_push(uint2 (&st)[kE8MaxLevels + 1], uint2 cu
     for (int l = 0; l <= kE8MaxLevels; ++l) {
         if (carrying) {
             if ((i >> l) & 1) {
-                cur = e8_combine(st[l], cur, blo, bhi, (uint32_t)(i >> (l + 1)), (uint32_t)(l + 1),
-                                 k0, k1);
+                cur = e8_combine(tab, st[l], cur, blo, bhi, (uint32_t)(i >> (l + 1)),
+                                 (uint32_t)(l + 1), k0, k1);
             } else {
                 st[l] = cur;
                 carrying = false;
@@ -1753,12 +1769,14 @@ __global__ __launch_bounds__(kThreads) void k_e8_pair(const uint8_t *__restrict_
                                                       uint64_t seed, uint32_t level, uint32_t node,
                                                       uint8_t *__restrict__ out)
 {
+    __shared__ uint32_t tab[256];
+    e8_fill_half_table(tab);
     const int64_t j0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
     if (j0 >= d)
         return;
     const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
-    const uint2 r = e8_combine(load_codes8(a, j0, d), load_codes8(b, j0, d), blo, bhi, node, level,
-                               (uint32_t)seed, (uint32_t)(seed >> 32));
+    const uint2 r = e8_combine(tab, load_codes8(a, j0, d), load_codes8(b, j0, d), blo, bhi, node,
+                               level, (uint32_t)seed, (uint32_t)(seed >> 32));
     store_codes8(out, j0, d, r);
 }
 
@@ -1766,6 +1784,8 @@ __global__ __launch_bounds__(kThreads) void k_e8_tree(const uint8_t *__restrict_
                                                       int64_t d, int64_t rbytes, uint64_t seed,
                                                       uint8_t *__restrict__ root)
 {
+    __shared__ uint32_t tab[256];
+    e8_fill_half_table(tab);
     const int64_t j0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
     if (j0 >= d)
         return;
@@ -1774,7 +1794,7 @@ __global__ __launch_bounds__(kThreads) void k_e8_tree(const uint8_t *__restrict_
     uint2 st[kE8MaxLevels + 1];
     uint2 cur = make_uint2(0, 0);
     for (int64_t i = 0; i < n; ++i)
-        cur = e8_push(st, load_codes8(codes + i * rbytes, j0, d), i, blo, bhi, k0, k1);
+        cur = e8_push(tab, st, load_codes8(codes + i * rbytes, j0, d), i, blo, bhi, k0, k1);
     store_codes8(root, j0, d, cur);
 }
 
@@ -1804,6 +1824,8 @@ __global__ __launch_bounds__(kThreads) void k_e8_compress_mean(const void *__res
                                                                float *__restrict__ mean,
                                                                uint8_t *__restrict__ root)
 {
+    __shared__ uint32_t tab[256];
+    e8_fill_half_table(tab);
     const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;
     const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
     if (j0 >= d)
@@ -1820,7 +1842,7 @@ __global__ __launch_bounds__(kThreads) void k_e8_compress_mean(const void *__res
             const uint2 leaf = q.prescale
                 ? e8_quant8<DT, true>(x, i * d, j0, d, vec, q, (uint32_t)i, blo, bhi, k0, k1)
                 : e8_quant8<DT, false>(x, i * d, j0, d, vec, q, (uint32_t)i, blo, bhi, k0, k1);
-            cur = e8_push(st, leaf, i, blo, bhi, k0, k1);
+            cur = e8_push(tab, st, leaf, i, blo, bhi, k0, k1);
         }
     }
     if (root)
