@@ -1483,17 +1483,18 @@ __device__ __forceinline__ void e8_half_hi4(uint32_t w, uint32_t *hi)
         hi[b] = ((1022u - ((g4 >> (8 * b)) & 0xFFu)) << 20) | ((w << (24 - 8 * b)) & 0x80000000u);
 }
 
-// The same half values for all 256 code bytes, one LDS entry per thread of
-// a 256-thread block (1 KB), then a block barrier.  Decoding a byte through
-// this table takes one address computation instead of the byte-parallel
-// arithmetic above (~90 of ~255 VALU instructions of an 8-coordinate
-// combine); LDS issue is far below the VALU time it replaces.
-__device__ __forceinline__ void e8_fill_half_table(uint32_t *tab)
+// The same half values for all 256 code bytes as fp64, one LDS entry per
+// thread of a 256-thread block (2 KB), then a block barrier.  Decoding a
+// byte through this table takes one address computation instead of the
+// byte-parallel arithmetic above (~90 of ~255 VALU instructions of an
+// 8-coordinate combine), and a 64-bit entry loads the zero low word with
+// the value (16 moves fewer); LDS issue stays far below the VALU time.
+__device__ __forceinline__ void e8_fill_half_table(double *tab)
 {
     static_assert(kThreads == 256, "one table entry per thread");
     uint32_t hi[4];
     e8_half_hi4(threadIdx.x, hi);
-    tab[threadIdx.x] = hi[0];
+    tab[threadIdx.x] = __hiloint2double((int)hi[0], 0);
     __syncthreads();
 }
 
@@ -1580,30 +1581,28 @@ __device__ __forceinline__ uint2 pack_bytes(const uint32_t (&c)[kPer])
 // with the same draws and lazy second draw as the quantization.  Main path:
 // the parent's fp64 high word gives X (exponent and top fraction bits; for
 // +-2^-127, between the level 0 and 2^-126, F >> 16 = 2^15 is set in).
-__device__ __forceinline__ uint2 e8_combine(const uint32_t *tab, const uint2 &a, const uint2 &b,
+__device__ __forceinline__ uint2 e8_combine(const double *tab, const uint2 &a, const uint2 &b,
                                             uint32_t blo, uint32_t bhi, uint32_t node,
                                             uint32_t level, uint32_t k0, uint32_t k1)
 {
     const uint4 A = philox10(make_uint4(blo, bhi, node, 2u * level), k0, k1);
     const uint32_t Ac[kPer / 2] = {~A.x, ~A.y, ~A.z, ~A.w};
-    uint32_t ha[kPer], hb[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        ha[k] = tab[byte_of(a, k)];
-        hb[k] = tab[byte_of(b, k)];
-    }
     double v[kPer];
-    uint32_t c[kPer];
-    bool tie = false;
+    uint32_t c[kPer], S[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-        v[k] = __hiloint2double((int)ha[k], 0) + __hiloint2double((int)hb[k], 0);
+        v[k] = tab[byte_of(a, k)] + tab[byte_of(b, k)];
         const uint32_t vh = (uint32_t)__double2hiint(v[k]);
         uint32_t X = (vh >> 4) & 0x7FFFFFFu;
         if (X == (896u << 16))
             X |= 0x8000u;
-        c[k] = e8_round_fields(X, 1024u, comp16(Ac, k), (vh >> 24) & 0x80u, tie);
+        S[k] = (k & 1) ? add_half16<1>(X, Ac[k >> 1]) : add_half16<0>(X, Ac[k >> 1]);
+        const uint32_t idx = 1024u - (S[k] >> 16);
+        c[k] = idx > 127u ? 0u : (((vh >> 24) & 0x80u) | idx);
     }
+    // a tie leaves the low half of its sum at 0xFFFF (as in e8_round_fields)
+    const uint32_t mx = max3_lo16(S[6], S[7], max3_lo16(S[0], S[1], S[2]));
+    const bool tie = ((uint16_t)mx == 0xFFFFu) | ((uint16_t)max3_lo16(S[3], S[4], S[5]) == 0xFFFFu);
     if (tie) {
         const uint4 B = philox10(make_uint4(blo, bhi, node, 2u * level + 1u), k0, k1);
 #pragma unroll
@@ -1620,7 +1619,7 @@ __device__ __forceinline__ uint2 e8_combine(const uint32_t *tab, const uint2 &a,
 // Binary-counter tree: leaf i enters; while bit l of i is set, it is combined
 // with the stored left sibling at level l into their parent (level l + 1,
 // node i >> (l + 1)).  The same pairs as the level-by-level tree.
-__device__ __forceinline__ uint2 e8_push(const uint32_t *tab, uint2 (&st)[kE8MaxLevels + 1],
+__device__ __forceinline__ uint2 e8_push(const double *tab, uint2 (&st)[kE8MaxLevels + 1],
                                          uint2 cur, int64_t i, uint32_t blo, uint32_t bhi,
                                          uint32_t k0, uint32_t k1)
 {
@@ -1769,7 +1768,7 @@ __global__ __launch_bounds__(kThreads) void k_e8_pair(const uint8_t *__restrict_
                                                       uint64_t seed, uint32_t level, uint32_t node,
                                                       uint8_t *__restrict__ out)
 {
-    __shared__ uint32_t tab[256];
+    __shared__ double tab[256];
     e8_fill_half_table(tab);
     const int64_t j0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
     if (j0 >= d)
@@ -1784,7 +1783,7 @@ __global__ __launch_bounds__(kThreads) void k_e8_tree(const uint8_t *__restrict_
                                                       int64_t d, int64_t rbytes, uint64_t seed,
                                                       uint8_t *__restrict__ root)
 {
-    __shared__ uint32_t tab[256];
+    __shared__ double tab[256];
     e8_fill_half_table(tab);
     const int64_t j0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
     if (j0 >= d)
@@ -1824,7 +1823,7 @@ __global__ __launch_bounds__(kThreads) void k_e8_compress_mean(const void *__res
                                                                float *__restrict__ mean,
                                                                uint8_t *__restrict__ root)
 {
-    __shared__ uint32_t tab[256];
+    __shared__ double tab[256];
     e8_fill_half_table(tab);
     const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;
     const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
