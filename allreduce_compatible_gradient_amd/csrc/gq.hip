@@ -1618,26 +1618,24 @@ __device__ __forceinline__ uint2 e8_combine(const double *tab, const uint2 &a, c
 
 // Binary-counter tree: leaf i enters; while bit l of i is set, it is combined
 // with the stored left sibling at level l into their parent (level l + 1,
-// node i >> (l + 1)).  The same pairs as the level-by-level tree.
-__device__ __forceinline__ uint2 e8_push(const double *tab, uint2 (&st)[kE8MaxLevels + 1],
-                                         uint2 cur, int64_t i, uint32_t blo, uint32_t bhi,
-                                         uint32_t k0, uint32_t k1)
+// node i >> (l + 1)).  The same pairs as the level-by-level tree.  The stack
+// lives in LDS, slot l of thread t at stk[l kThreads + t]: each thread reads
+// only what it wrote, so no barrier is needed, and the loop keeps a single
+// copy of the combine (the stack unrolled in registers took 132-136 VGPRs,
+// 3 waves per SIMD).  i is wave-uniform, so the loop is uniform.  Level
+// kE8MaxLevels is reached only by the last leaf of a full tree, whose
+// result is the root itself, so it needs no slot.
+constexpr int kE8StackSlots = kE8MaxLevels * kThreads;
+
+__device__ __forceinline__ uint2 e8_push(const double *tab, uint2 *stk, uint2 cur, int64_t i,
+                                         uint32_t blo, uint32_t bhi, uint32_t k0, uint32_t k1)
 {
-    // constant trip count (no early exit) so the stack stays in registers;
-    // i is wave-uniform, so every branch here is uniform
-    bool carrying = true;
-#pragma unroll
-    for (int l = 0; l <= kE8MaxLevels; ++l) {
-        if (carrying) {
-            if ((i >> l) & 1) {
-                cur = e8_combine(tab, st[l], cur, blo, bhi, (uint32_t)(i >> (l + 1)),
-                                 (uint32_t)(l + 1), k0, k1);
-            } else {
-                st[l] = cur;
-                carrying = false;
-            }
-        }
-    }
+    int l = 0;
+    for (; (i >> l) & 1; ++l)
+        cur = e8_combine(tab, stk[l * kThreads + threadIdx.x], cur, blo, bhi,
+                         (uint32_t)(i >> (l + 1)), (uint32_t)(l + 1), k0, k1);
+    if (l < kE8MaxLevels)
+        stk[l * kThreads + threadIdx.x] = cur;
     return cur;
 }
 
@@ -1784,16 +1782,16 @@ __global__ __launch_bounds__(kThreads) void k_e8_tree(const uint8_t *__restrict_
                                                       uint8_t *__restrict__ root)
 {
     __shared__ double tab[256];
+    __shared__ uint2 stk[kE8StackSlots];
     e8_fill_half_table(tab);
     const int64_t j0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
     if (j0 >= d)
         return;
     const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-    uint2 st[kE8MaxLevels + 1];
     uint2 cur = make_uint2(0, 0);
     for (int64_t i = 0; i < n; ++i)
-        cur = e8_push(tab, st, load_codes8(codes + i * rbytes, j0, d), i, blo, bhi, k0, k1);
+        cur = e8_push(tab, stk, load_codes8(codes + i * rbytes, j0, d), i, blo, bhi, k0, k1);
     store_codes8(root, j0, d, cur);
 }
 
@@ -1824,6 +1822,7 @@ __global__ __launch_bounds__(kThreads) void k_e8_compress_mean(const void *__res
                                                                uint8_t *__restrict__ root)
 {
     __shared__ double tab[256];
+    __shared__ uint2 stk[kE8StackSlots];
     e8_fill_half_table(tab);
     const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;
     const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
@@ -1836,12 +1835,11 @@ __global__ __launch_bounds__(kThreads) void k_e8_compress_mean(const void *__res
         const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
         const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
         const bool vec = (d & 7) == 0;
-        uint2 st[kE8MaxLevels + 1];
         for (int64_t i = 0; i < n; ++i) {
             const uint2 leaf = q.prescale
                 ? e8_quant8<DT, true>(x, i * d, j0, d, vec, q, (uint32_t)i, blo, bhi, k0, k1)
                 : e8_quant8<DT, false>(x, i * d, j0, d, vec, q, (uint32_t)i, blo, bhi, k0, k1);
-            cur = e8_push(tab, st, leaf, i, blo, bhi, k0, k1);
+            cur = e8_push(tab, stk, leaf, i, blo, bhi, k0, k1);
         }
     }
     if (root)
