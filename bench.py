@@ -336,6 +336,24 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
 
+    # ---- the same step with the caches cold: reading 1 GiB before each step
+    # evicts L2 and the 256 MB Infinity Cache, so no step re-reads what the
+    # previous one left there.  The flush only reads, so it leaves no dirty
+    # lines to be written back inside the step; only the step itself lies
+    # between its events.
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    fsum = torch.empty((), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    cpairs = event_pairs(torch, min(args.steps, 20))
+    for a, b in cpairs:
+        torch.sum(flush, 0, out=fsum)
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    cold_ms = float(np.median([a.elapsed_time(b) for a, b in cpairs]))
+    del flush
+
     # ---- the dominant kernel alone, one event pair per launch on the same stream
     kpairs = event_pairs(torch, args.steps)
     npairs = event_pairs(torch, args.steps)
@@ -375,6 +393,9 @@ def main():
                    "n_workers": n, "d": d, "input_dtype": w.dtype, "code_bits": w.code_bits,
                    "min_code_bits": W, "values": w.values},
         "hbm_frac_fused": round(fused_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "cold_cache": {"ms_per_step": round(cold_ms, 6),
+                       "input_GBs": round(in_bytes / (cold_ms * 1e-3) / 1e9, 3),
+                       "steps": len(cpairs), "stat": "median"},
         "kernels_ms": {"norm_pass": round(n_ms, 6), DOMINANT: round(k_ms, 6)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
