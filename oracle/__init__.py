@@ -76,6 +76,12 @@ def lib():
         L.oracle_pack.argtypes = [_vp, _i64, _i64, _int, _vp]
         L.oracle_unpack.argtypes = [_vp, _i64, _i64, _int, _vp]
         L.oracle_sum_codes.argtypes = [_vp, _i64, _i64, _vp]
+        L.oracle_word_fields.argtypes = [_int]
+        L.oracle_word_row_bytes.argtypes = [_i64, _int]
+        L.oracle_word_row_bytes.restype = _i64
+        L.oracle_pack_words.argtypes = [_vp, _i64, _i64, _int, _i64, _vp]
+        L.oracle_sum_words.argtypes = [_vp, _i64, _i64, _vp]
+        L.oracle_unpack_word_sums.argtypes = [_vp, _i64, _i64, _int, _i64, _vp]
         L.oracle_dequantize.argtypes = [_vp, _i64, _i64, _f32, _int, _int, _vp]
         L.oracle_compress_mean_cols.argtypes = [_vp, _int, _i64, _i64, _f32, _int, _int, _u64,
                                                 _vp, _i64, _vp, _vp]
@@ -261,6 +267,45 @@ def sum_codes(codes: np.ndarray) -> np.ndarray:
     n, d = codes.shape
     sums = np.zeros(d, dtype=np.int64)
     lib().oracle_sum_codes(_ptr(codes), n, d, _ptr(sums))
+    return sums
+
+
+def word_fields(W: int) -> int:
+    """Fields per 32-bit word of the word layout: floor(32 / W)."""
+    return int(lib().oracle_word_fields(W))
+
+
+def word_row_bytes(d: int, W: int) -> int:
+    return int(lib().oracle_word_row_bytes(d, W))
+
+
+def pack_words(codes: np.ndarray, W: int, M: int) -> np.ndarray:
+    """Codes [n][d] in the word layout (fields of code + M): uint32 [n][row words]."""
+    codes = np.ascontiguousarray(codes, dtype=np.int32)
+    if codes.ndim == 1:
+        codes = codes.reshape(1, -1)
+    n, d = codes.shape
+    out = np.zeros((n, word_row_bytes(d, W) // 4), dtype=np.uint32)
+    lib().oracle_pack_words(_ptr(codes), n, d, W, M, _ptr(out))
+    return out
+
+
+def sum_words(rows: np.ndarray) -> np.ndarray:
+    """Word-wise uint32 sum of the rows (modulo 2^32), as a native SUM does it."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint32)
+    n, nw = rows.shape
+    out = np.zeros(nw, dtype=np.uint32)
+    lib().oracle_sum_words(_ptr(rows), n, nw, _ptr(out))
+    return out
+
+
+def unpack_word_sums(word_sum: np.ndarray, n: int, d: int, W: int, M: int) -> np.ndarray:
+    """Exact code sums [d] (int64) from a summed row of n rows in the word layout."""
+    word_sum = np.ascontiguousarray(word_sum, dtype=np.uint32)
+    if word_sum.size * 4 != word_row_bytes(d, W):
+        raise ValueError("summed row has the wrong size")
+    sums = np.zeros(d, dtype=np.int64)
+    lib().oracle_unpack_word_sums(_ptr(word_sum), n, d, W, M, _ptr(sums))
     return sums
 
 

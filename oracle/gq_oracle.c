@@ -385,6 +385,62 @@ void oracle_dequantize(const int64_t *sums, int64_t n, int64_t d, float N, int s
         mean[j] = (float)((double)sums[j] * kappa);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Word layout for a native integer all-reduce (Sec. 6: the codes are summed
+ * by the collective's own integer SUM; a collective without a 16-bit integer
+ * type still sums 32-bit words).  Field width W, f = floor(32 / W) fields per
+ * 32-bit word: coordinate j sits in word j / f at bits [W (j % f),
+ * W (j % f) + W) and holds its code plus M, a value in [0, 2M].  Bits above
+ * the last field of a word, fields past d and the row's pad words are 0;
+ * rows are padded to 16 bytes.  Summed over n rows, a field holds
+ * sum_i code_ij + n M <= 2 n M, below 2^W whenever W is at least the
+ * minimal width (2^(W-1) > n M), so the 32-bit sum of the words never
+ * carries out of a field and never wraps.                                  */
+
+int oracle_word_fields(int W) { return 32 / W; }
+
+int64_t oracle_word_row_bytes(int64_t d, int W)
+{
+    int64_t f = 32 / W;
+    int64_t words = (d + f - 1) / f;
+    return ((words + 3) / 4) * 16;
+}
+
+void oracle_pack_words(const int32_t *codes, int64_t n, int64_t d, int W, int64_t M,
+                       uint32_t *out)
+{
+    int64_t f = 32 / W, rw = oracle_word_row_bytes(d, W) / 4;
+    memset(out, 0, (size_t)(n * rw) * sizeof(uint32_t));
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j < d; ++j) {
+            uint32_t biased = (uint32_t)((int64_t)codes[i * d + j] + M);
+            out[i * rw + j / f] |= biased << (W * (int)(j % f));
+        }
+}
+
+/* What the collective computes: the word-wise sum of n rows, modulo 2^32.  */
+void oracle_sum_words(const uint32_t *rows, int64_t n, int64_t nwords, uint32_t *sum)
+{
+    for (int64_t w = 0; w < nwords; ++w) {
+        uint32_t acc = 0;
+        for (int64_t i = 0; i < n; ++i)
+            acc += rows[i * nwords + w];
+        sum[w] = acc;
+    }
+}
+
+/* Field j of a summed row, minus the n biases: the exact code sum.         */
+void oracle_unpack_word_sums(const uint32_t *sum, int64_t n, int64_t d, int W, int64_t M,
+                             int64_t *sums)
+{
+    int64_t f = 32 / W;
+    uint32_t mask = W == 32 ? 0xFFFFFFFFu : ((1u << W) - 1u);
+    for (int64_t j = 0; j < d; ++j) {
+        uint32_t field = (sum[j / f] >> (W * (int)(j % f))) & mask;
+        sums[j] = (int64_t)field - n * M;
+    }
+}
+
 /* Selected columns of the whole pipeline, given the norm: for each listed
  * coordinate j, the exact code sum over the n workers and the mean.        */
 void oracle_compress_mean_cols(const void *x, int dtype, int64_t n, int64_t d, float N,
