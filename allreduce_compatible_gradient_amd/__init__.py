@@ -40,6 +40,11 @@ SIGNATURES = {
     "gq_quantize": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _vp, _u64, _i64, _i32, _vp, _vp]),
     "gq_reduce_codes": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp]),
     "gq_dequantize": (_i32, [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "gq_word_row_bytes": (_i64, [_i64, _i32]),
+    "gq_quantize_words": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _vp, _u64, _i64, _i32, _vp,
+                                 _vp]),
+    "gq_sum_words": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp]),
+    "gq_dequantize_words": (_i32, [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
     "gq_compress_mean_from_norm": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _u64, _vp, _i32,
                                           _vp, _vp, _vp]),
     "gq_compress_mean": (_i32, [_vp, _i32, _i64, _i64, _i32, _f32, _f32, _i32, _u64, _i32, _vp,
@@ -209,6 +214,45 @@ def gq_dequantize(code_sum: torch.Tensor, n: int, d: int, s: int, scheme, code_b
         mean = torch.empty(d, dtype=torch.float32, device=code_sum.device)
     _check(lib().gq_dequantize(_ptr(code_sum), n, d, s, _scheme(scheme), code_bits, _ptr(norm),
                                _ptr(mean), _stream(stream)))
+    return mean
+
+
+def gq_word_row_bytes(d: int, code_bits: int) -> int:
+    return int(lib().gq_word_row_bytes(d, code_bits))
+
+
+def gq_quantize_words(x: torch.Tensor, s: int, scheme, norm: torch.Tensor, seed: int,
+                      code_bits: int, *, worker_base: int = 0, words=None, stream=None):
+    """Codes in the word layout (floor(32/W) fields of code + M per word):
+    the uint32 words held in an int32 tensor [n, gq_word_row_bytes(d, W) / 4]."""
+    dt = _input(x)
+    n, d = x.shape
+    rb = gq_word_row_bytes(d, code_bits)
+    if words is None:
+        words = torch.empty((n, max(rb, 0) // 4), dtype=torch.int32, device=x.device)
+    _check(lib().gq_quantize_words(_ptr(x), dt, n, d, s, _scheme(scheme), _ptr(norm), seed,
+                                   worker_base, code_bits, _ptr(words), _stream(stream)))
+    return words
+
+
+def gq_sum_words(words: torch.Tensor, n: int, d: int, code_bits: int, *, word_sum=None,
+                 stream=None):
+    """Word-wise uint32 sum of the n rows (what a native SUM all-reduce computes),
+    in an int32 tensor of the same bits."""
+    rb = gq_word_row_bytes(d, code_bits)
+    if word_sum is None:
+        word_sum = torch.empty(max(rb, 0) // 4, dtype=torch.int32, device=words.device)
+    _check(lib().gq_sum_words(_ptr(words), n, d, code_bits, _ptr(word_sum), _stream(stream)))
+    return word_sum
+
+
+def gq_dequantize_words(word_sum: torch.Tensor, n: int, d: int, s: int, scheme, code_bits: int,
+                        norm: torch.Tensor, *, mean=None, stream=None):
+    """Mean over the n workers from a summed row in the word layout, float32 [d]."""
+    if mean is None:
+        mean = torch.empty(d, dtype=torch.float32, device=word_sum.device)
+    _check(lib().gq_dequantize_words(_ptr(word_sum), n, d, s, _scheme(scheme), code_bits,
+                                     _ptr(norm), _ptr(mean), _stream(stream)))
     return mean
 
 

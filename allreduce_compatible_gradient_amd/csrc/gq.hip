@@ -43,6 +43,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <type_traits>
+
 #include "gq.h"
 
 namespace {
@@ -1385,6 +1387,168 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t *__restri
     store_mean8<false>(mean, j0, d, m);
 }
 
+// ---------------------------------------------------------------------------
+// Word layout for a native integer all-reduce (Sec. 6: the collective's own
+// integer SUM adds the codes).  FPW = floor(32 / W) fields per 32-bit word;
+// coordinate j sits in word j / FPW at bits W (j % FPW) and holds code + M
+// (0 past d).  A block covers 2048 words of one row, i.e. 2048 FPW
+// coordinates.  Quantization is coalesced per 8-coordinate Philox group:
+// group g of thread t is coordinates g 2048 + 8 t .. + 8 of the block; the
+// biased fields go to LDS (one byte each for W <= 8, two for W <= 16), and
+// after one barrier thread t assembles words 4 t .. 4 t + 3 and
+// 1024 + 4 t .. + 3 and stores each quad with one 16-byte store.  With
+// FPW = 1 (W >= 17) the 8 fields of a thread are its 8 words, no LDS.
+constexpr int kWordsPerBlock = 2048;
+
+__host__ __device__ constexpr int word_fields(int W) { return 32 / W; }
+
+template <int FPW>
+using WordLdsT = typename std::conditional<(FPW >= 4), uint8_t, uint16_t>::type;
+
+template <int DT, int SCH, int FPW>
+__global__ __launch_bounds__(kThreads) void k_quantize_words(const void *__restrict__ x, int64_t n,
+                                                             int64_t d, int s, uint64_t seed,
+                                                             int64_t worker_base,
+                                                             const float *__restrict__ norm_dev,
+                                                             uint32_t *__restrict__ words, int W,
+                                                             uint32_t M, int64_t rwords,
+                                                             int64_t tiles)
+{
+    static_assert(kThreads * kPer == kWordsPerBlock, "one Philox group per thread and word group");
+    using E = WordLdsT<FPW>;
+    __shared__ alignas(16) E lds[FPW > 1 ? kWordsPerBlock * FPW : 1];
+    const int64_t i = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    const int64_t c_base = tile * kWordsPerBlock * FPW; // first coordinate of the block
+    const QParams q = make_qparams(*norm_dev, n, s, SCH);
+    const bool vec = (d & 7) == 0;
+    uint32_t *row = words + i * rwords;
+    if constexpr (FPW == 1) {
+        const int64_t j0 = c_base + (int64_t)threadIdx.x * kPer;
+        int code[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (!q.zero && j0 < d) {
+            float v[kPer];
+            load_group<DT>(x, i * d, j0, d, vec, v);
+            quantize_group_codes<SCH>(v, q, j0, (uint64_t)(worker_base + i), seed, code);
+        }
+        uint32_t w[kPer];
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            w[k] = (j0 + k < d) ? (uint32_t)code[k] + M : 0u;
+        if (j0 < rwords)
+            nt_store((uint8_t *)(row + j0), make_uint4(w[0], w[1], w[2], w[3]));
+        if (j0 + 4 < rwords)
+            nt_store((uint8_t *)(row + j0 + 4), make_uint4(w[4], w[5], w[6], w[7]));
+    } else {
+#pragma unroll
+        for (int g = 0; g < FPW; ++g) {
+            const int rel = g * kWordsPerBlock + (int)threadIdx.x * kPer;
+            const int64_t j0 = c_base + rel;
+            int code[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (!q.zero && j0 < d) {
+                float v[kPer];
+                load_group<DT>(x, i * d, j0, d, vec, v);
+                quantize_group_codes<SCH>(v, q, j0, (uint64_t)(worker_base + i), seed, code);
+            }
+            E b[kPer];
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+                b[k] = (E)((j0 + k < d) ? (uint32_t)code[k] + M : 0u);
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+                lds[rel + k] = b[k];
+        }
+        __syncthreads();
+        const int64_t w_base = tile * kWordsPerBlock;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int wr = h * (kWordsPerBlock / 2) + 4 * (int)threadIdx.x;
+            uint32_t w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint32_t acc = 0;
+#pragma unroll
+                for (int f = 0; f < FPW; ++f)
+                    acc |= (uint32_t)lds[(wr + u) * FPW + f] << (W * f);
+                w[u] = acc;
+            }
+            if (w_base + wr < rwords)
+                nt_store((uint8_t *)(row + w_base + wr), make_uint4(w[0], w[1], w[2], w[3]));
+        }
+    }
+}
+
+// What a native integer SUM over the n rows computes: the word-wise sum
+// modulo 2^32.  Thread = 8 consecutive words, the n rows in order.
+__global__ __launch_bounds__(kThreads) void k_sum_words(const uint32_t *__restrict__ words,
+                                                        int64_t n, int64_t rwords,
+                                                        uint32_t *__restrict__ out)
+{
+    const int64_t w0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
+    if (w0 >= rwords)
+        return;
+    const bool two = w0 + 4 < rwords; // rwords is a multiple of 4
+    uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+    for (int64_t i = 0; i < n; ++i) {
+        const uint32_t *r = words + i * rwords + w0;
+        const uint4 u = *(const uint4 *)r;
+        a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+        if (two) {
+            const uint4 v = *(const uint4 *)(r + 4);
+            b.x += v.x; b.y += v.y; b.z += v.z; b.w += v.w;
+        }
+    }
+    nt_store((uint8_t *)(out + w0), a);
+    if (two)
+        nt_store((uint8_t *)(out + w0 + 4), b);
+}
+
+// Dequantization of a summed row in the word layout: field - n M, times
+// kappa (fp64 product, one rounding).  Thread = 8 consecutive coordinates,
+// as in k_dequantize, so the mean stores of a wave are contiguous; each
+// coordinate reads its own word (neighbours share words through the cache).
+// One 64-bit division per thread finds the first word and field; the 8
+// offsets from there are small constant divisions.
+template <int SCH, int FPW>
+__global__ __launch_bounds__(kThreads) void k_dequantize_words(const uint32_t *__restrict__ wsum,
+                                                               int64_t n, int64_t d, int s, int W,
+                                                               uint32_t M,
+                                                               const float *__restrict__ norm_dev,
+                                                               float *__restrict__ mean)
+{
+    const int64_t j0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
+    if (j0 >= d)
+        return;
+    const QParams q = make_qparams(*norm_dev, n, s, SCH);
+    const uint32_t mask = W == 32 ? 0xFFFFFFFFu : ((1u << W) - 1u);
+    // n M < 2^31 (the width rule), so field - n M is an int32 and converts
+    // to fp64 in one instruction (an int64 conversion is a long sequence)
+    const uint32_t bias = (uint32_t)(n * (int64_t)M);
+    const int64_t w0 = j0 / FPW;
+    const uint32_t r0 = (uint32_t)(j0 - w0 * FPW); // field of coordinate j0, < FPW
+    const uint32_t *row = wsum + w0;
+    // all loads first, unconditional inside the row (loads each behind its
+    // own branch were issued one round trip at a time: 37 vs 27 us on
+    // 25.6M coordinates); fields past d read 0 and are not stored
+    uint32_t wv[kPer];
+    if (j0 + kPer <= d) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            wv[k] = row[(r0 + (uint32_t)k) / FPW];
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            wv[k] = (j0 + k < d) ? row[(r0 + (uint32_t)k) / FPW] : 0u;
+    }
+    float m[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const uint32_t r = r0 + (uint32_t)k, f = r - (r / FPW) * FPW;
+        const int32_t v = (int32_t)(((wv[k] >> (W * f)) & mask) - bias);
+        m[k] = (float)((double)v * q.kappa);
+    }
+    store_mean8<false>(mean, j0, d, m);
+}
+
 // Ablation: local-norm QSGD.  Worker i uses its own scalars; the mean is an
 // fp64 sum in worker order.  Optional per-worker packed codes.
 template <int DT>
@@ -2214,6 +2378,128 @@ int32_t gq_dequantize(const void *code_sum, int64_t n, int64_t d, int32_t s, int
     else
         k_dequantize<GQ_SCHEME_E><<<grid, block, 0, st>>>((const uint8_t *)code_sum, n, d, s, code_bits, norm_dev, mean);
     return check_launch("k_dequantize");
+}
+
+int64_t gq_word_row_bytes(int64_t d, int32_t code_bits)
+{
+    if (d < 0 || code_bits < 2 || code_bits > 32 || d > INT64_MAX / 64)
+        return -1;
+    const int64_t f = word_fields(code_bits), nw = (d + f - 1) / f;
+    return ((nw + 3) / 4) * 16;
+}
+
+// One launch of a kernel templated on the fields per word, for every value
+// floor(32 / W) takes with W in [2, 32].
+#define GQ_FPW_SWITCH(FPW_RUNTIME, LAUNCH)   \
+    switch (FPW_RUNTIME) {                   \
+    case 16: LAUNCH(16); break;              \
+    case 10: LAUNCH(10); break;              \
+    case 8: LAUNCH(8); break;                \
+    case 6: LAUNCH(6); break;                \
+    case 5: LAUNCH(5); break;                \
+    case 4: LAUNCH(4); break;                \
+    case 3: LAUNCH(3); break;                \
+    case 2: LAUNCH(2); break;                \
+    default: LAUNCH(1); break;               \
+    }
+
+int32_t gq_quantize_words(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                          int32_t scheme, const float *norm_dev, uint64_t seed,
+                          int64_t worker_base, int32_t code_bits, void *words, void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    GQ_TRY(validate_scheme(s, scheme));
+    if (!norm_dev || (!words && d > 0))
+        return fail(GQ_ERR_NULL, "norm_dev or words is NULL");
+    if (worker_base < 0 || worker_base + n > ((int64_t)1 << 32))
+        return fail(GQ_ERR_ARG, "worker indices must lie in [0, 2^32)");
+    GQ_TRY(validate_width(n, s, scheme, code_bits));
+    if (!aligned16(words))
+        return fail(GQ_ERR_ALIGN, "words is not 16-byte aligned");
+    const int64_t rwords = gq_word_row_bytes(d, code_bits) / 4;
+    const int64_t tiles = (rwords + kWordsPerBlock - 1) / kWordsPerBlock;
+    if (tiles == 0)
+        return ok();
+    if (tiles * n > kMaxGrid)
+        return fail(GQ_ERR_UNSUPPORTED, "n * tiles exceeds the launch limit");
+    const uint32_t M = (uint32_t)top_code(s, scheme);
+    const dim3 grid((unsigned)(tiles * n)), block(kThreads);
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t *wd = (uint32_t *)words;
+#define GQ_QW(F)                                                                               \
+    do {                                                                                       \
+        if (dtype == GQ_IN_F32 && scheme == GQ_SCHEME_L)                                       \
+            k_quantize_words<GQ_IN_F32, GQ_SCHEME_L, F><<<grid, block, 0, st>>>(               \
+                x, n, d, s, seed, worker_base, norm_dev, wd, code_bits, M, rwords, tiles);     \
+        else if (dtype == GQ_IN_F32)                                                           \
+            k_quantize_words<GQ_IN_F32, GQ_SCHEME_E, F><<<grid, block, 0, st>>>(               \
+                x, n, d, s, seed, worker_base, norm_dev, wd, code_bits, M, rwords, tiles);     \
+        else if (scheme == GQ_SCHEME_L)                                                        \
+            k_quantize_words<GQ_IN_BF16, GQ_SCHEME_L, F><<<grid, block, 0, st>>>(              \
+                x, n, d, s, seed, worker_base, norm_dev, wd, code_bits, M, rwords, tiles);     \
+        else                                                                                   \
+            k_quantize_words<GQ_IN_BF16, GQ_SCHEME_E, F><<<grid, block, 0, st>>>(              \
+                x, n, d, s, seed, worker_base, norm_dev, wd, code_bits, M, rwords, tiles);     \
+    } while (0)
+    GQ_FPW_SWITCH(word_fields(code_bits), GQ_QW)
+#undef GQ_QW
+    return check_launch("k_quantize_words");
+}
+
+int32_t gq_sum_words(const void *words, int64_t n, int64_t d, int32_t code_bits, void *word_sum,
+                     void *stream)
+{
+    if (n < 1 || n > 0x7FFFFFFF || d < 0)
+        return fail(GQ_ERR_ARG, "n must be >= 1 and d >= 0");
+    if ((!words || !word_sum) && d > 0)
+        return fail(GQ_ERR_NULL, "words or word_sum is NULL");
+    if (code_bits < 2 || code_bits > 32)
+        return fail(GQ_ERR_CODE_WIDTH, "code_bits %d outside [2, 32]", code_bits);
+    if (!aligned16(words) || !aligned16(word_sum))
+        return fail(GQ_ERR_ALIGN, "words or word_sum is not 16-byte aligned");
+    const int64_t rwords = gq_word_row_bytes(d, code_bits) / 4;
+    const int64_t blocks = (rwords + kWordsPerBlock - 1) / kWordsPerBlock;
+    if (blocks == 0)
+        return ok();
+    if (blocks > kMaxGrid)
+        return fail(GQ_ERR_UNSUPPORTED, "d exceeds the launch limit");
+    k_sum_words<<<dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream>>>(
+        (const uint32_t *)words, n, rwords, (uint32_t *)word_sum);
+    return check_launch("k_sum_words");
+}
+
+int32_t gq_dequantize_words(const void *word_sum, int64_t n, int64_t d, int32_t s, int32_t scheme,
+                            int32_t code_bits, const float *norm_dev, float *mean, void *stream)
+{
+    if (!norm_dev || ((!word_sum || !mean) && d > 0))
+        return fail(GQ_ERR_NULL, "word_sum, norm_dev or mean is NULL");
+    if (n < 1 || n > 0x7FFFFFFF || d < 0)
+        return fail(GQ_ERR_ARG, "n must be >= 1 and d >= 0");
+    GQ_TRY(validate_scheme(s, scheme));
+    GQ_TRY(validate_width(n, s, scheme, code_bits));
+    if (!aligned16(word_sum) || !aligned16(mean))
+        return fail(GQ_ERR_ALIGN, "word_sum or mean is not 16-byte aligned");
+    const int64_t blocks = (d + kTile - 1) / kTile;
+    if (blocks == 0)
+        return ok();
+    if (blocks > kMaxGrid)
+        return fail(GQ_ERR_UNSUPPORTED, "d exceeds the launch limit");
+    const uint32_t M = (uint32_t)top_code(s, scheme);
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    hipStream_t st = (hipStream_t)stream;
+    const uint32_t *ws = (const uint32_t *)word_sum;
+#define GQ_DW(F)                                                                                \
+    do {                                                                                        \
+        if (scheme == GQ_SCHEME_L)                                                              \
+            k_dequantize_words<GQ_SCHEME_L, F><<<grid, block, 0, st>>>(ws, n, d, s, code_bits,  \
+                                                                       M, norm_dev, mean);      \
+        else                                                                                    \
+            k_dequantize_words<GQ_SCHEME_E, F><<<grid, block, 0, st>>>(ws, n, d, s, code_bits,  \
+                                                                       M, norm_dev, mean);      \
+    } while (0)
+    GQ_FPW_SWITCH(word_fields(code_bits), GQ_DW)
+#undef GQ_DW
+    return check_launch("k_dequantize_words");
 }
 
 int32_t gq_compress_mean_from_norm(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,

@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
     ap.add_argument("--unfused", action="store_true", help="also time the four-call unfused path")
+    ap.add_argument("--words", action="store_true",
+                    help="also time the word layout for a native uint32 SUM all-reduce")
     ap.add_argument("--bucket", action="store_true",
                     help="also time one device's share of a data-parallel gradient bucket "
                          "(1, 25 and 100 MB of worker 0's row)")
@@ -229,6 +231,37 @@ def bucket_report(gq, torch, w, xd, stream, steps):
                       "code_bytes": row_bytes,
                       **{k: round(_time_us(torch, stream, f, steps), 3) for k, f in parts.items()}}
         del b, ws, codes, mean
+    return out
+
+
+def words_report(gq, torch, w, xd, stream, steps, norm, mean):
+    """The word layout at the minimal width: floor(32 / W) biased fields per
+    32-bit word, so that a native uint32 SUM all-reduce adds the codes.
+    Times the codes of all n rows, the word-wise sum over the rows (the
+    all-reduce's arithmetic, on one device) and the dequantization, with
+    bits on the wire per coordinate against an int32 container."""
+    n, d = w.n, w.d
+    W = gq.gq_min_code_bits(n, w.s, w.scheme)
+    rb = gq.gq_word_row_bytes(d, W)
+    words = torch.empty((n, rb // 4), dtype=torch.int32, device=xd.device)
+    wsum = torch.empty(rb // 4, dtype=torch.int32, device=xd.device)
+    parts = {
+        "quantize_words_us": lambda st: gq.gq_quantize_words(xd, w.s, w.scheme, norm, w.seed, W,
+                                                             words=words, stream=st),
+        "sum_words_us": lambda st: gq.gq_sum_words(words, n, d, W, word_sum=wsum, stream=st),
+        "dequantize_words_us": lambda st: gq.gq_dequantize_words(wsum, n, d, w.s, w.scheme, W,
+                                                                 norm, mean=mean, stream=st),
+    }
+    out = {"code_bits": W, "fields_per_word": 32 // W, "bits_on_wire": 8.0 * rb / d,
+           "row_bytes": rb}
+    in_bytes = n * d * w.elem_bytes
+    alg = {"quantize_words_us": in_bytes + n * rb, "sum_words_us": (n + 1) * rb,
+           "dequantize_words_us": rb + 4 * d}
+    for k, f in parts.items():
+        t = _time_us(torch, stream, f, steps)
+        out[k] = round(t, 3)
+        out[k.replace("_us", "_alg_GBs")] = round(alg[k] / (t * 1e-6) / 1e9, 1)
+    del words, wsum
     return out
 
 
@@ -431,6 +464,9 @@ def main():
         if wmin != w.code_bits:
             # the same pipeline with codes packed to the minimal width
             out["unfused_min_width"] = unfused_at(wmin, args.steps)
+    if args.words:
+        gq.gq_global_norm(xd, w.q, w.p, norm=norm, workspace=ws, stream=stream)
+        out["words"] = words_report(gq, torch, w, xd, stream, min(args.steps, 50), norm, mean)
     if args.bucket:
         out["bucket"] = bucket_report(gq, torch, w, xd, stream, min(args.steps, 100))
     if args.e8:

@@ -157,6 +157,44 @@ int32_t gq_reduce_codes(const void *codes, int64_t n, int64_t d, int32_t code_bi
 int32_t gq_dequantize(const void *code_sum, int64_t n, int64_t d, int32_t s, int32_t scheme,
                       int32_t code_bits, const float *norm_dev, float *mean, void *stream);
 
+/* ---- Word layout for a native integer all-reduce ----
+ * Sec. 6 reduces the codes with the collective's own integer SUM.  A
+ * collective without a 16-bit integer type still sums 32-bit words, so this
+ * layout packs f = floor(32 / W) fields per 32-bit word: coordinate j sits
+ * in word j / f at bits [W (j % f), W (j % f) + W) and holds its code plus
+ * M (a value in [0, 2M]).  Bits above the last field of a word, fields past
+ * d and pad words are 0.  Rows are gq_word_row_bytes(d, W) bytes (16-byte
+ * multiples) apart.  A field summed over n rows holds sum_i code_ij + n M
+ * <= 2 n M < 2^W whenever W >= gq_min_code_bits(n, s, scheme), so the
+ * word-wise uint32 sum of the rows -- in any order, as any all-reduce
+ * algorithm adds them -- never carries out of a field.  Bits on the wire
+ * per coordinate: 32 / f (16 for W = 11..16, 10.7 for W = 9, 10, 8 for
+ * W = 7, 8), against 32 for an int32 container.                          */
+
+/* 16 * ceil(ceil(d / floor(32 / W)) / 4); -1 for d < 0 or W outside [2, 32]. */
+int64_t gq_word_row_bytes(int64_t d, int32_t code_bits);
+
+/* gq_quantize's codes (same rules, same draws, worker index worker_base + i
+ * for row i) written in the word layout.  W must hold a sum of the codes
+ * of every worker whose rows will be summed: with shards, choose W for the
+ * total number of workers (this call checks it against its own n).
+ * words: n rows of gq_word_row_bytes(d, W) bytes, 16-byte aligned.        */
+int32_t gq_quantize_words(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                          int32_t scheme, const float *norm_dev, uint64_t seed,
+                          int64_t worker_base, int32_t code_bits, void *words, void *stream);
+
+/* What a native uint32 SUM all-reduce computes, on one device: word_sum[w]
+ * = sum_i words[i][w] modulo 2^32 over the n rows.                         */
+int32_t gq_sum_words(const void *words, int64_t n, int64_t d, int32_t code_bits, void *word_sum,
+                     void *stream);
+
+/* Dequantization of a summed row in the word layout, n = the number of
+ * rows summed: mean[j] = fp32((field_j - n M) kappa), kappa = fp64(N / (n M)),
+ * product in fp64 -- the same bits as gq_dequantize of the same sums.
+ * W must satisfy the width rule for n.  mean: d floats, 16-byte aligned.  */
+int32_t gq_dequantize_words(const void *word_sum, int64_t n, int64_t d, int32_t s, int32_t scheme,
+                            int32_t code_bits, const float *norm_dev, float *mean, void *stream);
+
 /* Fused quantize + exact integer sum + dequantize in one streaming pass,
  * given N in norm_dev[0]: equals gq_quantize, gq_reduce_codes and
  * gq_dequantize in sequence, without materializing the codes.  If

@@ -148,3 +148,34 @@ def test_binding_fails_loudly_without_a_gpu():
         pytest.skip("a GPU is present")
     with pytest.raises(ValueError):
         gq.gq_global_norm(torch.zeros(2, 8), 2, 2)
+
+
+def test_word_layout_sizes_match_the_oracle():
+    for d in (0, 1, 7, 8, 97, 65536, 25_557_032):
+        for W in (2, 3, 5, 6, 8, 9, 11, 13, 16, 17, 32):
+            assert gq.gq_word_row_bytes(d, W) == oracle.word_row_bytes(d, W)
+    assert gq.gq_word_row_bytes(10, 1) == -1
+    assert gq.gq_word_row_bytes(10, 33) == -1
+    assert gq.gq_word_row_bytes(-1, 8) == -1
+
+
+def test_word_layout_entry_points_reject():
+    L = gq.lib()
+    q = L.gq_quantize_words
+    assert q(A, 0, 4, 100, 7, 0, A, 1, 0, 5, A, NUL) == 4      # W below W_min = 6
+    assert q(A, 0, 4, 100, 7, 0, A, 1, 0, 33, A, NUL) == 4     # W above 32
+    assert q(A, 0, 4, 100, 7, 0, NUL, 1, 0, 8, A, NUL) == 1    # norm NULL
+    assert q(A, 0, 4, 100, 7, 0, A, 1, 0, 8, NUL, NUL) == 1    # words NULL
+    assert q(A, 0, 4, 100, 7, 0, A, 1, 0, 8, U, NUL) == 6      # words misaligned
+    assert q(U, 0, 4, 100, 7, 0, A, 1, 0, 8, A, NUL) == 6      # x misaligned
+    assert q(A, 0, 4, 100, 7, 0, A, 1, -1, 8, A, NUL) == 2     # worker_base < 0
+    assert q(A, 2, 4, 100, 7, 0, A, 1, 0, 8, A, NUL) == 2      # dtype
+    assert L.gq_sum_words(NUL, 4, 100, 8, A, NUL) == 1
+    assert L.gq_sum_words(A, 0, 100, 8, A, NUL) == 2
+    assert L.gq_sum_words(A, 4, 100, 1, A, NUL) == 4
+    assert L.gq_sum_words(A, 4, 100, 8, U, NUL) == 6
+    dq = L.gq_dequantize_words
+    assert dq(A, 4, 100, 7, 0, 5, A, A, NUL) == 4
+    assert dq(A, 4, 100, 7, 0, 8, NUL, A, NUL) == 1
+    assert dq(A, 4, 100, 7, 0, 8, A, U, NUL) == 6
+    assert dq(A, 4, 100, 7, 3, 8, A, A, NUL) == 2
