@@ -192,11 +192,12 @@ def bucket_report(gq, torch, w, xd, stream, steps):
     """One device's share of a data-parallel gradient bucket, device 0 of
     n = w.n workers: the fp64 norm term of its bucket, N from the term (after
     what would be an all-reduce of that double), its codes at its worker
-    index in the width that holds a sum of n codes, and the mean from the
-    summed code row (after what would be the integer all-reduce; here the
-    device's own row stands in for the sum).  The two all-reduces are not
-    run: this build uses one GPU.  Buckets are the leading 1, 25 and 100 MB
-    of worker 0's row, timed as graph replays of the five launches."""
+    index in the word layout of the width that holds a sum of n codes (what
+    a native uint32 SUM all-reduce adds), and the mean from the summed words
+    (after what would be that all-reduce; here the device's own row stands
+    in for the sum).  The two all-reduces are not run: this build uses one
+    GPU.  Buckets are the leading 1, 25 and 100 MB of worker 0's row, timed
+    as graph replays of the four launches."""
     out = {}
     W = gq.gq_min_code_bits(w.n, w.s, w.scheme)
     for label, nbytes in (("1MB", 1 << 20), ("25MB", 25 << 20), ("100MB", 100 << 20)):
@@ -205,63 +206,34 @@ def bucket_report(gq, torch, w, xd, stream, steps):
         ws = torch.empty(gq.gq_workspace_bytes(1, db), dtype=torch.uint8, device=xd.device)
         term = torch.empty(1, dtype=torch.float64, device=xd.device)
         norm = torch.empty(1, dtype=torch.float32, device=xd.device)
-        codes = torch.empty((1, gq.gq_code_row_bytes(db, W)), dtype=torch.uint8, device=xd.device)
+        rb = gq.gq_word_row_bytes(db, W)
+        words = torch.empty((1, rb // 4), dtype=torch.int32, device=xd.device)
         mean = torch.empty(db, dtype=torch.float32, device=xd.device)
         parts = {
             "norm_term_us": lambda st: gq.gq_norm_term(b, w.q, w.p, term=term, workspace=ws,
                                                        stream=st),
             "norm_from_term_us": lambda st: gq.gq_norm_from_term(term, w.q, w.p, norm=norm,
                                                                  stream=st),
-            "quantize_us": lambda st: gq.gq_quantize(b, w.s, w.scheme, norm, w.seed, W,
-                                                     worker_base=0, codes=codes, stream=st),
-            "dequantize_us": lambda st: gq.gq_dequantize(codes[0], w.n, db, w.s, w.scheme, W,
-                                                         norm, mean=mean, stream=st),
+            "quantize_words_us": lambda st: gq.gq_quantize_words(b, w.s, w.scheme, norm, w.seed,
+                                                                 W, worker_base=0, words=words,
+                                                                 stream=st),
+            "dequantize_words_us": lambda st: gq.gq_dequantize_words(words[0], w.n, db, w.s,
+                                                                     w.scheme, W, norm,
+                                                                     mean=mean, stream=st),
         }
 
         def share(st):
             for f in parts.values():
                 f(st)
         t = _time_us(torch, stream, share, steps)
-        row_bytes = gq.gq_code_row_bytes(db, W)
-        # algorithmic bytes: the bucket read twice, codes written and read, the mean written
-        alg = 2 * db * w.elem_bytes + 2 * row_bytes + 4 * db
+        # algorithmic bytes: the bucket read twice, the word row written and read, the mean
+        alg = 2 * db * w.elem_bytes + 2 * rb + 4 * db
         out[label] = {"elements": db, "code_bits": W, "us": round(t, 3),
                       "bucket_GBs": round(db * w.elem_bytes / (t * 1e-6) / 1e9, 3),
                       "alg_GBs": round(alg / (t * 1e-6) / 1e9, 3),
-                      "code_bytes": row_bytes,
+                      "wire_bytes": rb, "bits_on_wire": round(8.0 * rb / db, 3),
                       **{k: round(_time_us(torch, stream, f, steps), 3) for k, f in parts.items()}}
-        del b, ws, codes, mean
-    return out
-
-
-def words_report(gq, torch, w, xd, stream, steps, norm, mean):
-    """The word layout at the minimal width: floor(32 / W) biased fields per
-    32-bit word, so that a native uint32 SUM all-reduce adds the codes.
-    Times the codes of all n rows, the word-wise sum over the rows (the
-    all-reduce's arithmetic, on one device) and the dequantization, with
-    bits on the wire per coordinate against an int32 container."""
-    n, d = w.n, w.d
-    W = gq.gq_min_code_bits(n, w.s, w.scheme)
-    rb = gq.gq_word_row_bytes(d, W)
-    words = torch.empty((n, rb // 4), dtype=torch.int32, device=xd.device)
-    wsum = torch.empty(rb // 4, dtype=torch.int32, device=xd.device)
-    parts = {
-        "quantize_words_us": lambda st: gq.gq_quantize_words(xd, w.s, w.scheme, norm, w.seed, W,
-                                                             words=words, stream=st),
-        "sum_words_us": lambda st: gq.gq_sum_words(words, n, d, W, word_sum=wsum, stream=st),
-        "dequantize_words_us": lambda st: gq.gq_dequantize_words(wsum, n, d, w.s, w.scheme, W,
-                                                                 norm, mean=mean, stream=st),
-    }
-    out = {"code_bits": W, "fields_per_word": 32 // W, "bits_on_wire": 8.0 * rb / d,
-           "row_bytes": rb}
-    in_bytes = n * d * w.elem_bytes
-    alg = {"quantize_words_us": in_bytes + n * rb, "sum_words_us": (n + 1) * rb,
-           "dequantize_words_us": rb + 4 * d}
-    for k, f in parts.items():
-        t = _time_us(torch, stream, f, steps)
-        out[k] = round(t, 3)
-        out[k.replace("_us", "_alg_GBs")] = round(alg[k] / (t * 1e-6) / 1e9, 1)
-    del words, wsum
+        del b, ws, words, mean
     return out
 
 
