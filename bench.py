@@ -359,6 +359,12 @@ def main():
     cold_ms = float(np.median([a.elapsed_time(b) for a, b in cpairs]))
     del flush
 
+    # ---- the same step as graph replays: device time without host launch
+    # overhead (what bounds the small workload is the launches themselves)
+    graph_us = _time_us(torch, stream, lambda st: gq.gq_compress_mean(
+        xd, w.s, w.q, w.p, w.scheme, w.seed, mean=mean, norm=norm, workspace=ws, stream=st),
+        min(args.steps, 50))
+
     # ---- the dominant kernel alone, one event pair per launch on the same stream
     kpairs = event_pairs(torch, args.steps)
     npairs = event_pairs(torch, args.steps)
@@ -398,6 +404,8 @@ def main():
                    "n_workers": n, "d": d, "input_dtype": w.dtype, "code_bits": w.code_bits,
                    "min_code_bits": W, "values": w.values},
         "hbm_frac_fused": round(fused_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "graph_replay": {"ms_per_step": round(graph_us * 1e-3, 6),
+                         "input_GBs": round(in_bytes / (graph_us * 1e-6) / 1e9, 3)},
         "cold_cache": {"ms_per_step": round(cold_ms, 6),
                        "input_GBs": round(in_bytes / (cold_ms * 1e-3) / 1e9, 3),
                        "steps": len(cpairs), "stat": "median"},

@@ -44,6 +44,10 @@ def test_graph_replays_match_eager(n, d, s, q, p, scheme, W):
     codes = torch.empty((n, gq.gq_code_row_bytes(d, W)), dtype=torch.uint8, device=DEV)
     csum2 = torch.empty_like(csum)
     mean2 = torch.empty_like(mean)
+    rw = gq.gq_word_row_bytes(d, W) // 4
+    words = torch.empty((n, rw), dtype=torch.int32, device=DEV)
+    wsum = torch.empty(rw, dtype=torch.int32, device=DEV)
+    mean3 = torch.empty_like(mean)
     seed = 1234
 
     def fused(st):
@@ -54,15 +58,19 @@ def test_graph_replays_match_eager(n, d, s, q, p, scheme, W):
         gq.gq_quantize(xd, s, scheme, norm, seed, W, codes=codes, stream=st)
         gq.gq_reduce_codes(codes, n, d, W, code_sum=csum2, stream=st)
         gq.gq_dequantize(csum2, n, d, s, scheme, W, norm, mean=mean2, stream=st)
+        gq.gq_quantize_words(xd, s, scheme, norm, seed, W, words=words, stream=st)
+        gq.gq_sum_words(words, n, d, W, word_sum=wsum, stream=st)
+        gq.gq_dequantize_words(wsum, n, d, s, scheme, W, norm, mean=mean3, stream=st)
 
     cur = torch.cuda.current_stream()
     fused(cur)
     unfused(cur)
-    ref = [host(t).copy() for t in (mean, norm, csum, codes, csum2, mean2)]
+    ref = [host(t).copy() for t in (mean, norm, csum, codes, csum2, mean2, words, wsum, mean3)]
     N, sums, omean = oracle.compress_mean(x, s, q, p, oracle.SCHEME_L if scheme == "L" else oracle.SCHEME_E,
                                           seed)
     assert np.float32(ref[1][0]) == N
     assert np.array_equal(ref[0], omean)
+    assert np.array_equal(ref[8], omean)  # the word path gives the same mean
 
     side = torch.cuda.Stream()
     side.wait_stream(cur)
@@ -76,11 +84,11 @@ def test_graph_replays_match_eager(n, d, s, q, p, scheme, W):
         fused(side)
         unfused(side)
     for rep in range(3):
-        for t in (mean, norm, csum, codes, csum2, mean2):
+        for t in (mean, norm, csum, codes, csum2, mean2, words, wsum, mean3):
             t.zero_()  # eager work between replays
         torch.cuda.synchronize()
         graph.replay()
-        got = [host(t) for t in (mean, norm, csum, codes, csum2, mean2)]
+        got = [host(t) for t in (mean, norm, csum, codes, csum2, mean2, words, wsum, mean3)]
         for a, b in zip(ref, got):
             assert np.array_equal(a, b), rep
         fused(cur)  # eager call between replays
