@@ -195,8 +195,8 @@ def bucket_report(gq, torch, w, xd, stream, steps):
     index in the word layout of the width that holds a sum of n codes (what
     a native uint32 SUM all-reduce adds), and the mean from the summed words
     (after what would be that all-reduce; here the device's own row stands
-    in for the sum).  The two all-reduces are not run: this build uses one
-    GPU.  Buckets are the leading 1, 25 and 100 MB of worker 0's row, timed
+    in for the sum).  The two all-reduces are not run: the library works on
+    one device.  Buckets are the leading 1, 25 and 100 MB of worker 0's row, timed
     as graph replays of the four launches."""
     out = {}
     W = gq.gq_min_code_bits(w.n, w.s, w.scheme)
@@ -287,7 +287,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the n workers are "
-              "simulated as rows of one device buffer and no collective is part of this build",
+              "simulated as rows of one device buffer and the library has no collective",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
