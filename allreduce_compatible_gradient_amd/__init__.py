@@ -43,6 +43,8 @@ SIGNATURES = {
     "gq_word_row_bytes": (_i64, [_i64, _i32]),
     "gq_quantize_words": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _vp, _u64, _i64, _i32, _vp,
                                  _vp]),
+    "gq_compress_words_from_norm": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _vp, _u64, _i64,
+                                           _i32, _vp, _vp]),
     "gq_sum_words": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp]),
     "gq_dequantize_words": (_i32, [_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
     "gq_compress_mean_from_norm": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _u64, _vp, _i32,
@@ -233,6 +235,22 @@ def gq_quantize_words(x: torch.Tensor, s: int, scheme, norm: torch.Tensor, seed:
     _check(lib().gq_quantize_words(_ptr(x), dt, n, d, s, _scheme(scheme), _ptr(norm), seed,
                                    worker_base, code_bits, _ptr(words), _stream(stream)))
     return words
+
+
+def gq_compress_words_from_norm(x: torch.Tensor, s: int, scheme, norm: torch.Tensor, seed: int,
+                                code_bits: int, *, worker_base: int = 0, word_sum=None,
+                                stream=None):
+    """The n rows' codes summed into one word row (fields of sum_i (code + M)),
+    in an int32 tensor of the uint32 bits [gq_word_row_bytes(d, W) / 4]."""
+    dt = _input(x)
+    n, d = x.shape
+    rb = gq_word_row_bytes(d, code_bits)
+    if word_sum is None:
+        word_sum = torch.empty(max(rb, 0) // 4, dtype=torch.int32, device=x.device)
+    _check(lib().gq_compress_words_from_norm(_ptr(x), dt, n, d, s, _scheme(scheme), _ptr(norm),
+                                             seed, worker_base, code_bits, _ptr(word_sum),
+                                             _stream(stream)))
+    return word_sum
 
 
 def gq_sum_words(words: torch.Tensor, n: int, d: int, code_bits: int, *, word_sum=None,

@@ -1477,6 +1477,80 @@ __global__ __launch_bounds__(kThreads) void k_quantize_words(const void *__restr
     }
 }
 
+// A device's own rows summed before the all-reduce: the word row whose
+// fields hold sum_i (code_ij + M) over its n rows, as gq_sum_words of the
+// rows of k_quantize_words, in one pass with the sum in registers.  Block =
+// 2048 words (2048 FPW coordinates); for each of its FPW groups a thread
+// walks the n rows for 8 coordinates, one Philox call per row, then the
+// biased sums go to LDS and are assembled into word quads as in
+// k_quantize_words.
+template <int DT, int SCH, int FPW>
+__global__ __launch_bounds__(kThreads) void k_compress_words(const void *__restrict__ x, int64_t n,
+                                                             int64_t d, int s, uint64_t seed,
+                                                             int64_t worker_base,
+                                                             const float *__restrict__ norm_dev,
+                                                             uint32_t *__restrict__ out, int W,
+                                                             uint32_t bias, int64_t rwords)
+{
+    using E = WordLdsT<FPW>;
+    __shared__ alignas(16) E lds[FPW > 1 ? kWordsPerBlock * FPW : 1];
+    const int64_t tile = blockIdx.x;
+    const int64_t c_base = tile * kWordsPerBlock * FPW;
+    const QParams q = make_qparams(*norm_dev, n, s, SCH);
+    const bool vec = (d & 7) == 0;
+    uint32_t w1[kPer]; // FPW == 1: the thread's 8 words
+#pragma unroll
+    for (int g = 0; g < FPW; ++g) {
+        const int rel = g * kWordsPerBlock + (int)threadIdx.x * kPer;
+        const int64_t j0 = c_base + rel;
+        int acc[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (!q.zero && j0 < d) {
+            for (int64_t i = 0; i < n; ++i) {
+                float v[kPer];
+                int code[kPer];
+                load_group<DT>(x, i * d, j0, d, vec, v);
+                quantize_group_codes<SCH>(v, q, j0, (uint64_t)(worker_base + i), seed, code);
+#pragma unroll
+                for (int k = 0; k < kPer; ++k)
+                    acc[k] += code[k];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const uint32_t b = (j0 + k < d) ? (uint32_t)acc[k] + bias : 0u;
+            if constexpr (FPW == 1)
+                w1[k] = b;
+            else
+                lds[rel + k] = (E)b;
+        }
+    }
+    if constexpr (FPW == 1) {
+        const int64_t w0 = c_base + (int64_t)threadIdx.x * kPer;
+        if (w0 < rwords)
+            nt_store((uint8_t *)(out + w0), make_uint4(w1[0], w1[1], w1[2], w1[3]));
+        if (w0 + 4 < rwords)
+            nt_store((uint8_t *)(out + w0 + 4), make_uint4(w1[4], w1[5], w1[6], w1[7]));
+    } else {
+        __syncthreads();
+        const int64_t w_base = tile * kWordsPerBlock;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int wr = h * (kWordsPerBlock / 2) + 4 * (int)threadIdx.x;
+            uint32_t w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint32_t a = 0;
+#pragma unroll
+                for (int f = 0; f < FPW; ++f)
+                    a |= (uint32_t)lds[(wr + u) * FPW + f] << (W * f);
+                w[u] = a;
+            }
+            if (w_base + wr < rwords)
+                nt_store((uint8_t *)(out + w_base + wr), make_uint4(w[0], w[1], w[2], w[3]));
+        }
+    }
+}
+
 // What a native integer SUM over the n rows computes: the word-wise sum
 // modulo 2^32.  Thread = 8 consecutive words, the n rows in order.
 __global__ __launch_bounds__(kThreads) void k_sum_words(const uint32_t *__restrict__ words,
@@ -2444,6 +2518,50 @@ int32_t gq_quantize_words(const void *x, int32_t dtype, int64_t n, int64_t d, in
     GQ_FPW_SWITCH(word_fields(code_bits), GQ_QW)
 #undef GQ_QW
     return check_launch("k_quantize_words");
+}
+
+int32_t gq_compress_words_from_norm(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                                   int32_t scheme, const float *norm_dev, uint64_t seed,
+                                   int64_t worker_base, int32_t code_bits, void *word_sum,
+                                   void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    GQ_TRY(validate_scheme(s, scheme));
+    if (!norm_dev || (!word_sum && d > 0))
+        return fail(GQ_ERR_NULL, "norm_dev or word_sum is NULL");
+    if (worker_base < 0 || worker_base + n > ((int64_t)1 << 32))
+        return fail(GQ_ERR_ARG, "worker indices must lie in [0, 2^32)");
+    GQ_TRY(validate_width(n, s, scheme, code_bits));
+    if (!aligned16(word_sum))
+        return fail(GQ_ERR_ALIGN, "word_sum is not 16-byte aligned");
+    const int64_t rwords = gq_word_row_bytes(d, code_bits) / 4;
+    const int64_t tiles = (rwords + kWordsPerBlock - 1) / kWordsPerBlock;
+    if (tiles == 0)
+        return ok();
+    if (tiles > kMaxGrid)
+        return fail(GQ_ERR_UNSUPPORTED, "d exceeds the launch limit");
+    const uint32_t bias = (uint32_t)(n * top_code(s, scheme)); // < 2^31 by the width rule
+    const dim3 grid((unsigned)tiles), block(kThreads);
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t *out = (uint32_t *)word_sum;
+#define GQ_CW(F)                                                                               \
+    do {                                                                                       \
+        if (dtype == GQ_IN_F32 && scheme == GQ_SCHEME_L)                                       \
+            k_compress_words<GQ_IN_F32, GQ_SCHEME_L, F><<<grid, block, 0, st>>>(               \
+                x, n, d, s, seed, worker_base, norm_dev, out, code_bits, bias, rwords);        \
+        else if (dtype == GQ_IN_F32)                                                           \
+            k_compress_words<GQ_IN_F32, GQ_SCHEME_E, F><<<grid, block, 0, st>>>(               \
+                x, n, d, s, seed, worker_base, norm_dev, out, code_bits, bias, rwords);        \
+        else if (scheme == GQ_SCHEME_L)                                                        \
+            k_compress_words<GQ_IN_BF16, GQ_SCHEME_L, F><<<grid, block, 0, st>>>(              \
+                x, n, d, s, seed, worker_base, norm_dev, out, code_bits, bias, rwords);        \
+        else                                                                                   \
+            k_compress_words<GQ_IN_BF16, GQ_SCHEME_E, F><<<grid, block, 0, st>>>(              \
+                x, n, d, s, seed, worker_base, norm_dev, out, code_bits, bias, rwords);        \
+    } while (0)
+    GQ_FPW_SWITCH(word_fields(code_bits), GQ_CW)
+#undef GQ_CW
+    return check_launch("k_compress_words");
 }
 
 int32_t gq_sum_words(const void *words, int64_t n, int64_t d, int32_t code_bits, void *word_sum,

@@ -237,6 +237,41 @@ def bucket_report(gq, torch, w, xd, stream, steps):
     return out
 
 
+def words_report(gq, torch, w, xd, stream, steps, norm, mean):
+    """The word layout at the minimal width: floor(32 / W) biased fields per
+    32-bit word, so that a native uint32 SUM all-reduce adds the codes.
+    Times the codes of all n rows, the word-wise sum over the rows (the
+    all-reduce's arithmetic, on one device), the same summed row in one pass
+    (what a device holding the n rows sends), and the dequantization, with
+    bits on the wire per coordinate against an int32 container."""
+    n, d = w.n, w.d
+    W = gq.gq_min_code_bits(n, w.s, w.scheme)
+    rb = gq.gq_word_row_bytes(d, W)
+    words = torch.empty((n, rb // 4), dtype=torch.int32, device=xd.device)
+    wsum = torch.empty(rb // 4, dtype=torch.int32, device=xd.device)
+    parts = {
+        "quantize_words_us": lambda st: gq.gq_quantize_words(xd, w.s, w.scheme, norm, w.seed, W,
+                                                             words=words, stream=st),
+        "sum_words_us": lambda st: gq.gq_sum_words(words, n, d, W, word_sum=wsum, stream=st),
+        "compress_words_us": lambda st: gq.gq_compress_words_from_norm(
+            xd, w.s, w.scheme, norm, w.seed, W, word_sum=wsum, stream=st),
+        "dequantize_words_us": lambda st: gq.gq_dequantize_words(wsum, n, d, w.s, w.scheme, W,
+                                                                 norm, mean=mean, stream=st),
+    }
+    out = {"code_bits": W, "fields_per_word": 32 // W, "bits_on_wire": 8.0 * rb / d,
+           "row_bytes": rb}
+    in_bytes = n * d * w.elem_bytes
+    alg = {"quantize_words_us": in_bytes + n * rb, "sum_words_us": (n + 1) * rb,
+           "compress_words_us": in_bytes + rb,
+           "dequantize_words_us": rb + 4 * d}
+    for k, f in parts.items():
+        t = _time_us(torch, stream, f, steps)
+        out[k] = round(t, 3)
+        out[k.replace("_us", "_alg_GBs")] = round(alg[k] / (t * 1e-6) / 1e9, 1)
+    del words, wsum
+    return out
+
+
 def ablation(gq, torch, w, xd, stream, steps, global_ms, gmean, gnorm, ws):
     """Global-L_s against per-worker local-norm QSGD on the same input: time,
     bits sent per element, and the relative error of the dequantized mean."""

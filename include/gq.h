@@ -183,6 +183,19 @@ int32_t gq_quantize_words(const void *x, int32_t dtype, int64_t n, int64_t d, in
                           int32_t scheme, const float *norm_dev, uint64_t seed,
                           int64_t worker_base, int32_t code_bits, void *words, void *stream);
 
+/* A device's own n rows summed before the all-reduce, in one pass: the
+ * word row whose fields hold sum_i (code_ij + M) over its rows -- the same
+ * bits as gq_sum_words of gq_quantize_words' rows, with the codes summed in
+ * registers and never written.  Rows use worker indices worker_base + i.
+ * Summed word-wise over every device and decoded by gq_dequantize_words
+ * with n = the total number of workers, it gives the mean over all of
+ * them; W must hold that total (this call checks it against its own n).
+ * word_sum: gq_word_row_bytes(d, W) bytes, 16-byte aligned.               */
+int32_t gq_compress_words_from_norm(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                                   int32_t scheme, const float *norm_dev, uint64_t seed,
+                                   int64_t worker_base, int32_t code_bits, void *word_sum,
+                                   void *stream);
+
 /* What a native uint32 SUM all-reduce computes, on one device: word_sum[w]
  * = sum_i words[i][w] modulo 2^32 over the n rows.                         */
 int32_t gq_sum_words(const void *words, int64_t n, int64_t d, int32_t code_bits, void *word_sum,

@@ -170,6 +170,12 @@ def test_word_layout_entry_points_reject():
     assert q(U, 0, 4, 100, 7, 0, A, 1, 0, 8, A, NUL) == 6      # x misaligned
     assert q(A, 0, 4, 100, 7, 0, A, 1, -1, 8, A, NUL) == 2     # worker_base < 0
     assert q(A, 2, 4, 100, 7, 0, A, 1, 0, 8, A, NUL) == 2      # dtype
+    c = L.gq_compress_words_from_norm
+    assert c(A, 0, 4, 100, 7, 0, A, 1, 0, 5, A, NUL) == 4      # W below W_min = 6
+    assert c(A, 0, 4, 100, 7, 0, NUL, 1, 0, 8, A, NUL) == 1    # norm NULL
+    assert c(A, 0, 4, 100, 7, 0, A, 1, 0, 8, NUL, NUL) == 1    # word_sum NULL
+    assert c(A, 0, 4, 100, 7, 0, A, 1, 0, 8, U, NUL) == 6      # word_sum misaligned
+    assert c(A, 0, 4, 100, 7, 0, A, 1, -1, 8, A, NUL) == 2     # worker_base < 0
     assert L.gq_sum_words(NUL, 4, 100, 8, A, NUL) == 1
     assert L.gq_sum_words(A, 0, 100, 8, A, NUL) == 2
     assert L.gq_sum_words(A, 4, 100, 1, A, NUL) == 4

@@ -105,6 +105,45 @@ def test_words_match_oracle(n0, s, scheme, W, dtype):
         assert np.array_equal(host(gmean), oracle.dequantize(sums, n, N, s, SCH[scheme])), (n, d)
 
 
+@pytest.mark.parametrize("n0,s,scheme,W", [c for c in _cases() if c[0] > 1 or c[3] <= 4])
+def test_compress_words_equals_the_summed_rows(n0, s, scheme, W):
+    """One pass over a device's rows: the word-wise sum of its rows' words,
+    bit-exact against the oracle, for every fields-per-word count."""
+    for n, d in SHAPES:
+        n = min(n, n0)
+        seed = 11 * n + d + W
+        x = wl.random_rows(n, d, seed=seed, scale=0.3)
+        xd = to_dev(x)
+        norm = gq.gq_global_norm(xd, 2.0, 2.0)
+        N = np.float32(host(norm)[0])
+        M = M_of(s, scheme)
+        ocodes = oracle.quantize(x, N, s, SCH[scheme], seed)
+        expect = oracle.sum_words(oracle.pack_words(ocodes, W, M))
+        got = gq.gq_compress_words_from_norm(xd, s, scheme, norm, seed, W)
+        assert np.array_equal(words_host(got), expect), (n, d)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_device_sums_add_up_to_the_whole(dtype):
+    """Three devices' summed rows (their workers at their global offsets),
+    added word-wise as the all-reduce would, give the sum over all workers,
+    and gq_dequantize_words of it the fused path's mean."""
+    n, d, s, scheme = 9, 40_003, 15, "L"
+    W = gq.gq_min_code_bits(n, s, scheme)
+    x = wl.random_rows(n, d, seed=123, dtype=dtype, scale=0.2)
+    xd = to_dev(x)
+    norm = gq.gq_global_norm(xd, 2.0, 2.0)
+    parts = [words_host(gq.gq_compress_words_from_norm(xd[a:b].clone(), s, scheme, norm, 8, W,
+                                                       worker_base=a))
+             for a, b in ((0, 4), (4, 5), (5, 9))]
+    total = (parts[0].astype(np.uint64) + parts[1] + parts[2]).astype(np.uint32)  # mod 2^32
+    whole = words_host(gq.gq_compress_words_from_norm(xd, s, scheme, norm, 8, W))
+    assert np.array_equal(total, whole)
+    mean = gq.gq_dequantize_words(u32(total), n, d, s, scheme, W, norm)
+    fmean, _, _ = gq.gq_compress_mean(xd, s, 2.0, 2.0, scheme, 8)
+    assert np.array_equal(host(mean), host(fmean))
+
+
 def test_zero_norm_gives_the_bias_only():
     """N = 0: every code is 0, so each field holds M and the mean is 0."""
     n, d, s, W = 3, 5000, 7, 6
@@ -160,6 +199,8 @@ def test_workload_full_size(key):
     words = gq.gq_quantize_words(xd, w.s, w.scheme, norm, w.seed, W)
     wsum = gq.gq_sum_words(words, w.n, w.d, W)
     mean = gq.gq_dequantize_words(wsum, w.n, w.d, w.s, w.scheme, W, norm)
+    csum = gq.gq_compress_words_from_norm(xd, w.s, w.scheme, norm, w.seed, W)
+    assert torch.equal(csum, wsum)
     log("unpacking")
     sums = oracle.unpack_word_sums(words_host(wsum), w.n, w.d, W, M)
     assert np.array_equal(sums, host(fsum).view(np.int32)[: w.d].astype(np.int64))
