@@ -143,11 +143,40 @@ def gq_workspace_bytes(n: int, d: int) -> int:
     return int(lib().gq_workspace_bytes(n, d))
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _buf(t, nbytes: int, name: str, device, dtype=None):
+    """A caller-given device buffer: on the input's device, contiguous, of the
+    given dtype (raw byte buffers: any), and at least nbytes long.  The C ABI
+    takes plain pointers and cannot check sizes, so the binding does."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != torch.device(device):
+        raise ValueError(f"{name} is on {t.device}, the input on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if _nbytes(t) < nbytes:
+        raise ValueError(f"{name} holds {_nbytes(t)} bytes, {nbytes} are needed")
+    return t
+
+
+def _norm_in(norm, device):
+    if norm is None:
+        raise ValueError("norm is required (a 1-element float32 device tensor)")
+    return _buf(norm, 4, "norm", device, torch.float32)
+
+
 def _workspace(ws, n, d, device):
     need = gq_workspace_bytes(n, d)
     if ws is None:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
-    return ws
+    return _buf(ws, need, "workspace", device)
 
 
 # ---------------------------------------------------------------------------
@@ -157,10 +186,11 @@ def gq_global_norm(x: torch.Tensor, q=2.0, p=2.0, *, norm=None, workspace=None, 
     """Global (q,p)-norm of the rows of x; returns a 1-element float32 device tensor."""
     dt = _input(x)
     n, d = x.shape
-    norm = torch.empty(1, dtype=torch.float32, device=x.device) if norm is None else norm
+    norm = (torch.empty(1, dtype=torch.float32, device=x.device) if norm is None
+            else _buf(norm, 4, "norm", x.device, torch.float32))
     ws = _workspace(workspace, n, d, x.device)
     _check(lib().gq_global_norm(_ptr(x), dt, n, d, _order(q), _order(p), _ptr(norm), _ptr(ws),
-                                ws.numel(), _stream(stream)))
+                                _nbytes(ws), _stream(stream)))
     return norm
 
 
@@ -170,10 +200,11 @@ def gq_norm_term(x: torch.Tensor, q=2.0, p=2.0, *, term=None, workspace=None, st
     by sum (finite p) or max (p = inf)."""
     dt = _input(x)
     n, d = x.shape
-    term = torch.empty(1, dtype=torch.float64, device=x.device) if term is None else term
+    term = (torch.empty(1, dtype=torch.float64, device=x.device) if term is None
+            else _buf(term, 8, "term", x.device, torch.float64))
     ws = _workspace(workspace, n, d, x.device)
     _check(lib().gq_norm_term(_ptr(x), dt, n, d, _order(q), _order(p), _ptr(term), _ptr(ws),
-                              ws.numel(), _stream(stream)))
+                              _nbytes(ws), _stream(stream)))
     return term
 
 
@@ -181,7 +212,8 @@ def gq_norm_from_term(term: torch.Tensor, q=2.0, p=2.0, *, norm=None, stream=Non
     """The norm N from a term combined over shards; 1-element float32 device tensor."""
     if term.dtype != torch.float64 or term.numel() < 1 or not term.is_cuda:
         raise ValueError("term must be a float64 device tensor")
-    norm = torch.empty(1, dtype=torch.float32, device=term.device) if norm is None else norm
+    norm = (torch.empty(1, dtype=torch.float32, device=term.device) if norm is None
+            else _buf(norm, 4, "norm", term.device, torch.float32))
     _check(lib().gq_norm_from_term(_ptr(term), _order(q), _order(p), _ptr(norm), _stream(stream)))
     return norm
 
@@ -192,8 +224,10 @@ def gq_quantize(x: torch.Tensor, s: int, scheme, norm: torch.Tensor, seed: int, 
     dt = _input(x)
     n, d = x.shape
     rb = gq_code_row_bytes(d, code_bits)
+    _norm_in(norm, x.device)
     if codes is None:
         codes = torch.empty((n, max(rb, 0)), dtype=torch.uint8, device=x.device)
+    _buf(codes, n * max(rb, 0), "codes", x.device)
     _check(lib().gq_quantize(_ptr(x), dt, n, d, s, _scheme(scheme), _ptr(norm), seed, worker_base,
                              code_bits, _ptr(codes), _stream(stream)))
     return codes
@@ -202,9 +236,11 @@ def gq_quantize(x: torch.Tensor, s: int, scheme, norm: torch.Tensor, seed: int, 
 def gq_reduce_codes(codes: torch.Tensor, n: int, d: int, code_bits: int, *, code_sum=None,
                     stream=None):
     """Exact sum over the n packed rows; one packed row, uint8 [row_bytes]."""
-    rb = gq_code_row_bytes(d, code_bits)
+    rb = max(gq_code_row_bytes(d, code_bits), 0)
+    _buf(codes, n * rb, "codes", None)
     if code_sum is None:
-        code_sum = torch.empty(max(rb, 0), dtype=torch.uint8, device=codes.device)
+        code_sum = torch.empty(rb, dtype=torch.uint8, device=codes.device)
+    _buf(code_sum, rb, "code_sum", codes.device)
     _check(lib().gq_reduce_codes(_ptr(codes), n, d, code_bits, _ptr(code_sum), _stream(stream)))
     return code_sum
 
@@ -212,8 +248,11 @@ def gq_reduce_codes(codes: torch.Tensor, n: int, d: int, code_bits: int, *, code
 def gq_dequantize(code_sum: torch.Tensor, n: int, d: int, s: int, scheme, code_bits: int,
                   norm: torch.Tensor, *, mean=None, stream=None):
     """Mean over the n workers from the packed code sums, float32 [d]."""
+    _buf(code_sum, max(gq_code_row_bytes(d, code_bits), 0), "code_sum", None)
+    _norm_in(norm, code_sum.device)
     if mean is None:
         mean = torch.empty(d, dtype=torch.float32, device=code_sum.device)
+    _buf(mean, 4 * d, "mean", code_sum.device, torch.float32)
     _check(lib().gq_dequantize(_ptr(code_sum), n, d, s, _scheme(scheme), code_bits, _ptr(norm),
                                _ptr(mean), _stream(stream)))
     return mean
@@ -229,9 +268,11 @@ def gq_quantize_words(x: torch.Tensor, s: int, scheme, norm: torch.Tensor, seed:
     the uint32 words held in an int32 tensor [n, gq_word_row_bytes(d, W) / 4]."""
     dt = _input(x)
     n, d = x.shape
-    rb = gq_word_row_bytes(d, code_bits)
+    rb = max(gq_word_row_bytes(d, code_bits), 0)
+    _norm_in(norm, x.device)
     if words is None:
-        words = torch.empty((n, max(rb, 0) // 4), dtype=torch.int32, device=x.device)
+        words = torch.empty((n, rb // 4), dtype=torch.int32, device=x.device)
+    _buf(words, n * rb, "words", x.device)
     _check(lib().gq_quantize_words(_ptr(x), dt, n, d, s, _scheme(scheme), _ptr(norm), seed,
                                    worker_base, code_bits, _ptr(words), _stream(stream)))
     return words
@@ -244,9 +285,11 @@ def gq_compress_words_from_norm(x: torch.Tensor, s: int, scheme, norm: torch.Ten
     in an int32 tensor of the uint32 bits [gq_word_row_bytes(d, W) / 4]."""
     dt = _input(x)
     n, d = x.shape
-    rb = gq_word_row_bytes(d, code_bits)
+    rb = max(gq_word_row_bytes(d, code_bits), 0)
+    _norm_in(norm, x.device)
     if word_sum is None:
-        word_sum = torch.empty(max(rb, 0) // 4, dtype=torch.int32, device=x.device)
+        word_sum = torch.empty(rb // 4, dtype=torch.int32, device=x.device)
+    _buf(word_sum, rb, "word_sum", x.device)
     _check(lib().gq_compress_words_from_norm(_ptr(x), dt, n, d, s, _scheme(scheme), _ptr(norm),
                                              seed, worker_base, code_bits, _ptr(word_sum),
                                              _stream(stream)))
@@ -257,9 +300,11 @@ def gq_sum_words(words: torch.Tensor, n: int, d: int, code_bits: int, *, word_su
                  stream=None):
     """Word-wise uint32 sum of the n rows (what a native SUM all-reduce computes),
     in an int32 tensor of the same bits."""
-    rb = gq_word_row_bytes(d, code_bits)
+    rb = max(gq_word_row_bytes(d, code_bits), 0)
+    _buf(words, n * rb, "words", None)
     if word_sum is None:
-        word_sum = torch.empty(max(rb, 0) // 4, dtype=torch.int32, device=words.device)
+        word_sum = torch.empty(rb // 4, dtype=torch.int32, device=words.device)
+    _buf(word_sum, rb, "word_sum", words.device)
     _check(lib().gq_sum_words(_ptr(words), n, d, code_bits, _ptr(word_sum), _stream(stream)))
     return word_sum
 
@@ -267,8 +312,11 @@ def gq_sum_words(words: torch.Tensor, n: int, d: int, code_bits: int, *, word_su
 def gq_dequantize_words(word_sum: torch.Tensor, n: int, d: int, s: int, scheme, code_bits: int,
                         norm: torch.Tensor, *, mean=None, stream=None):
     """Mean over the n workers from a summed row in the word layout, float32 [d]."""
+    _buf(word_sum, max(gq_word_row_bytes(d, code_bits), 0), "word_sum", None)
+    _norm_in(norm, word_sum.device)
     if mean is None:
         mean = torch.empty(d, dtype=torch.float32, device=word_sum.device)
+    _buf(mean, 4 * d, "mean", word_sum.device, torch.float32)
     _check(lib().gq_dequantize_words(_ptr(word_sum), n, d, s, _scheme(scheme), code_bits,
                                      _ptr(norm), _ptr(mean), _stream(stream)))
     return mean
@@ -280,11 +328,14 @@ def gq_compress_mean_from_norm(x: torch.Tensor, s: int, scheme, seed: int, norm:
     """Fused quantize + integer sum + dequantize given the norm: (mean, code_sum or None)."""
     dt = _input(x)
     n, d = x.shape
+    _norm_in(norm, x.device)
     if mean is None:
         mean = torch.empty(d, dtype=torch.float32, device=x.device)
+    _buf(mean, 4 * d, "mean", x.device, torch.float32)
     if want_code_sum and code_sum is None:
         code_sum = torch.empty(max(gq_code_row_bytes(d, code_bits), 0), dtype=torch.uint8,
                                device=x.device)
+    _buf(code_sum, max(gq_code_row_bytes(d, code_bits), 0), "code_sum", x.device)
     _check(lib().gq_compress_mean_from_norm(_ptr(x), dt, n, d, s, _scheme(scheme), seed,
                                             _ptr(norm), code_bits, _ptr(mean), _ptr(code_sum),
                                             _stream(stream)))
@@ -304,10 +355,13 @@ def gq_compress_mean(x: torch.Tensor, s: int, q, p, scheme, seed: int, *, code_b
     if want_code_sum and code_sum is None:
         code_sum = torch.empty(max(gq_code_row_bytes(d, code_bits), 0), dtype=torch.uint8,
                                device=x.device)
+    _buf(mean, 4 * d, "mean", x.device, torch.float32)
+    _buf(norm, 4, "norm", x.device, torch.float32)
+    _buf(code_sum, max(gq_code_row_bytes(d, code_bits), 0), "code_sum", x.device)
     ws = _workspace(workspace, n, d, x.device)
     _check(lib().gq_compress_mean(_ptr(x), dt, n, d, s, _order(q), _order(p), _scheme(scheme), seed,
                                   code_bits, _ptr(mean), _ptr(norm), _ptr(code_sum), _ptr(ws),
-                                  ws.numel(), _stream(stream)))
+                                  _nbytes(ws), _stream(stream)))
     return mean, norm, code_sum
 
 
@@ -324,9 +378,12 @@ def gq_qsgd_local_mean(x: torch.Tensor, s: int, seed: int, *, code_bits: int = 0
     if want_codes and codes is None:
         codes = torch.empty((n, max(gq_code_row_bytes(d, code_bits), 0)), dtype=torch.uint8,
                             device=x.device)
+    _buf(mean, 4 * d, "mean", x.device, torch.float32)
+    _buf(norms, 4 * n, "norms", x.device, torch.float32)
+    _buf(codes, n * max(gq_code_row_bytes(d, code_bits), 0), "codes", x.device)
     ws = _workspace(workspace, n, d, x.device)
     _check(lib().gq_qsgd_local_mean(_ptr(x), dt, n, d, s, seed, _ptr(mean), _ptr(norms),
-                                    _ptr(codes), code_bits, _ptr(ws), ws.numel(),
+                                    _ptr(codes), code_bits, _ptr(ws), _nbytes(ws),
                                     _stream(stream)))
     return mean, norms, codes
 
@@ -343,8 +400,10 @@ def gq_e8_quantize(x: torch.Tensor, norm: torch.Tensor, seed: int, *, worker_bas
     """8-bit codes, uint8 [n, gq_e8_row_bytes(d)]."""
     dt = _input(x)
     n, d = x.shape
+    _norm_in(norm, x.device)
     if codes is None:
         codes = torch.empty((n, gq_e8_row_bytes(d)), dtype=torch.uint8, device=x.device)
+    _buf(codes, n * gq_e8_row_bytes(d), "codes", x.device)
     _check(lib().gq_e8_quantize(_ptr(x), dt, n, d, _ptr(norm), seed, worker_base, _ptr(codes),
                                 _stream(stream)))
     return codes
@@ -352,23 +411,33 @@ def gq_e8_quantize(x: torch.Tensor, norm: torch.Tensor, seed: int, *, worker_bas
 
 def gq_e8_reduce_pair(a: torch.Tensor, b: torch.Tensor, d: int, seed: int, level: int, node: int,
                       *, out=None, stream=None):
+    rb = max(gq_e8_row_bytes(d), 0)
+    _buf(a, rb, "a", None)
+    _buf(b, rb, "b", a.device)
     if out is None:
-        out = torch.empty(gq_e8_row_bytes(d), dtype=torch.uint8, device=a.device)
+        out = torch.empty(rb, dtype=torch.uint8, device=a.device)
+    _buf(out, rb, "out", a.device)
     _check(lib().gq_e8_reduce_pair(_ptr(a), _ptr(b), d, seed, level, node, _ptr(out),
                                    _stream(stream)))
     return out
 
 
 def gq_e8_tree(codes: torch.Tensor, n: int, d: int, seed: int, *, root=None, stream=None):
+    rb = max(gq_e8_row_bytes(d), 0)
+    _buf(codes, n * rb, "codes", None)
     if root is None:
-        root = torch.empty(gq_e8_row_bytes(d), dtype=torch.uint8, device=codes.device)
+        root = torch.empty(rb, dtype=torch.uint8, device=codes.device)
+    _buf(root, rb, "root", codes.device)
     _check(lib().gq_e8_tree(_ptr(codes), n, d, seed, _ptr(root), _stream(stream)))
     return root
 
 
 def gq_e8_dequantize(root: torch.Tensor, d: int, norm: torch.Tensor, *, mean=None, stream=None):
+    _buf(root, max(gq_e8_row_bytes(d), 0), "root", None)
+    _norm_in(norm, root.device)
     if mean is None:
         mean = torch.empty(d, dtype=torch.float32, device=root.device)
+    _buf(mean, 4 * d, "mean", root.device, torch.float32)
     _check(lib().gq_e8_dequantize(_ptr(root), d, _ptr(norm), _ptr(mean), _stream(stream)))
     return mean
 
@@ -384,8 +453,11 @@ def gq_e8_compress_mean(x: torch.Tensor, q, p, seed: int, *, want_root: bool = F
         norm = torch.empty(1, dtype=torch.float32, device=x.device)
     if want_root and root is None:
         root = torch.empty(gq_e8_row_bytes(d), dtype=torch.uint8, device=x.device)
+    _buf(mean, 4 * d, "mean", x.device, torch.float32)
+    _buf(norm, 4, "norm", x.device, torch.float32)
+    _buf(root, max(gq_e8_row_bytes(d), 0), "root", x.device)
     ws = _workspace(workspace, n, d, x.device)
     _check(lib().gq_e8_compress_mean(_ptr(x), dt, n, d, _order(q), _order(p), seed, _ptr(mean),
-                                     _ptr(norm), _ptr(root), _ptr(ws), ws.numel(),
+                                     _ptr(norm), _ptr(root), _ptr(ws), _nbytes(ws),
                                      _stream(stream)))
     return mean, norm, root
