@@ -57,6 +57,7 @@ SIGNATURES = {
     "gq_e8_quantize": (_i32, [_vp, _i32, _i64, _i64, _vp, _u64, _i64, _vp, _vp]),
     "gq_e8_reduce_pair": (_i32, [_vp, _vp, _i64, _u64, _i32, _i64, _vp, _vp]),
     "gq_e8_tree": (_i32, [_vp, _i64, _i64, _u64, _vp, _vp]),
+    "gq_e8_subtree": (_i32, [_vp, _i64, _i64, _u64, _i64, _vp, _vp]),
     "gq_e8_dequantize": (_i32, [_vp, _i64, _vp, _vp, _vp]),
     "gq_e8_compress_mean": (_i32, [_vp, _i32, _i64, _i64, _f32, _f32, _u64, _vp, _vp, _vp, _vp,
                                    _i64, _vp]),
@@ -429,6 +430,19 @@ def gq_e8_tree(codes: torch.Tensor, n: int, d: int, seed: int, *, root=None, str
         root = torch.empty(rb, dtype=torch.uint8, device=codes.device)
     _buf(root, rb, "root", codes.device)
     _check(lib().gq_e8_tree(_ptr(codes), n, d, seed, _ptr(root), _stream(stream)))
+    return root
+
+
+def gq_e8_subtree(codes: torch.Tensor, n: int, d: int, seed: int, worker_base: int, *, root=None,
+                  stream=None):
+    """Root of the subtree over workers worker_base .. worker_base + n - 1, with
+    the whole tree's node indices (worker_base a multiple of n)."""
+    rb = max(gq_e8_row_bytes(d), 0)
+    _buf(codes, n * rb, "codes", None)
+    if root is None:
+        root = torch.empty(rb, dtype=torch.uint8, device=codes.device)
+    _buf(root, rb, "root", codes.device)
+    _check(lib().gq_e8_subtree(_ptr(codes), n, d, seed, worker_base, _ptr(root), _stream(stream)))
     return root
 
 

@@ -1865,13 +1865,18 @@ __device__ __forceinline__ uint2 e8_combine(const double *tab, const uint2 &a, c
 // result is the root itself, so it needs no slot.
 constexpr int kE8StackSlots = kE8MaxLevels * kThreads;
 
+// wb is the global index of leaf 0 (0, or a multiple of the subtree's leaf
+// count): the parent at level l + 1 is node (wb + i) >> (l + 1) of the
+// whole tree, so a subtree held by one device draws what the whole tree
+// draws there.
 __device__ __forceinline__ uint2 e8_push(const double *tab, uint2 *stk, uint2 cur, int64_t i,
-                                         uint32_t blo, uint32_t bhi, uint32_t k0, uint32_t k1)
+                                         int64_t wb, uint32_t blo, uint32_t bhi, uint32_t k0,
+                                         uint32_t k1)
 {
     int l = 0;
     for (; (i >> l) & 1; ++l)
         cur = e8_combine(tab, stk[l * kThreads + threadIdx.x], cur, blo, bhi,
-                         (uint32_t)(i >> (l + 1)), (uint32_t)(l + 1), k0, k1);
+                         (uint32_t)((wb + i) >> (l + 1)), (uint32_t)(l + 1), k0, k1);
     if (l < kE8MaxLevels)
         stk[l * kThreads + threadIdx.x] = cur;
     return cur;
@@ -2017,7 +2022,7 @@ __global__ __launch_bounds__(kThreads) void k_e8_pair(const uint8_t *__restrict_
 
 __global__ __launch_bounds__(kThreads) void k_e8_tree(const uint8_t *__restrict__ codes, int64_t n,
                                                       int64_t d, int64_t rbytes, uint64_t seed,
-                                                      uint8_t *__restrict__ root)
+                                                      int64_t wb, uint8_t *__restrict__ root)
 {
     __shared__ double tab[256];
     __shared__ uint2 stk[kE8StackSlots];
@@ -2029,7 +2034,7 @@ __global__ __launch_bounds__(kThreads) void k_e8_tree(const uint8_t *__restrict_
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     uint2 cur = make_uint2(0, 0);
     for (int64_t i = 0; i < n; ++i)
-        cur = e8_push(tab, stk, load_codes8(codes + i * rbytes, j0, d), i, blo, bhi, k0, k1);
+        cur = e8_push(tab, stk, load_codes8(codes + i * rbytes, j0, d), i, wb, blo, bhi, k0, k1);
     store_codes8(root, j0, d, cur);
 }
 
@@ -2077,7 +2082,7 @@ __global__ __launch_bounds__(kThreads) void k_e8_compress_mean(const void *__res
             const uint2 leaf = q.prescale
                 ? e8_quant8<DT, true>(x, i * d, j0, d, vec, q, (uint32_t)i, blo, bhi, k0, k1)
                 : e8_quant8<DT, false>(x, i * d, j0, d, vec, q, (uint32_t)i, blo, bhi, k0, k1);
-            cur = e8_push(tab, stk, leaf, i, blo, bhi, k0, k1);
+            cur = e8_push(tab, stk, leaf, i, 0, blo, bhi, k0, k1);
         }
     }
     if (root)
@@ -2763,11 +2768,15 @@ int32_t gq_e8_reduce_pair(const void *a, const void *b, int64_t d, uint64_t seed
     return check_launch("k_e8_pair");
 }
 
-int32_t gq_e8_tree(const void *codes, int64_t n, int64_t d, uint64_t seed, void *root, void *stream)
+int32_t gq_e8_subtree(const void *codes, int64_t n, int64_t d, uint64_t seed, int64_t worker_base,
+                      void *root, void *stream)
 {
     GQ_TRY(e8_check_n(n));
     if (d < 0)
         return fail(GQ_ERR_ARG, "d is negative");
+    if (worker_base < 0 || worker_base % n != 0 || worker_base + n > ((int64_t)1 << 32))
+        return fail(GQ_ERR_ARG, "worker_base = %lld must be a multiple of n = %lld in [0, 2^32)",
+                    (long long)worker_base, (long long)n);
     if ((!codes || !root) && d > 0)
         return fail(GQ_ERR_NULL, "codes or root is NULL");
     if (!aligned16(codes) || !aligned16(root))
@@ -2778,8 +2787,13 @@ int32_t gq_e8_tree(const void *codes, int64_t n, int64_t d, uint64_t seed, void 
     if (blocks > kMaxGrid)
         return fail(GQ_ERR_UNSUPPORTED, "d exceeds the launch limit");
     k_e8_tree<<<dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream>>>(
-        (const uint8_t *)codes, n, d, gq_e8_row_bytes(d), seed, (uint8_t *)root);
+        (const uint8_t *)codes, n, d, gq_e8_row_bytes(d), seed, worker_base, (uint8_t *)root);
     return check_launch("k_e8_tree");
+}
+
+int32_t gq_e8_tree(const void *codes, int64_t n, int64_t d, uint64_t seed, void *root, void *stream)
+{
+    return gq_e8_subtree(codes, n, d, seed, 0, root, stream);
 }
 
 int32_t gq_e8_dequantize(const void *root, int64_t d, const float *norm_dev, float *mean,

@@ -271,6 +271,17 @@ int32_t gq_e8_reduce_pair(const void *a, const void *b, int64_t d, uint64_t seed
 int32_t gq_e8_tree(const void *codes, int64_t n, int64_t d, uint64_t seed, void *root,
                    void *stream);
 
+/* The subtree over n rows of workers worker_base .. worker_base + n - 1
+ * (worker_base a multiple of n): the tree's nodes there, drawn with their
+ * node indices in the whole tree, so that a device holding an aligned block
+ * of workers computes its subtree root and the levels above it
+ * (gq_e8_reduce_pair with level log2(n) + 1 ... and the whole tree's node
+ * index) reproduce gq_e8_tree over all workers bit for bit.  The codes must
+ * come from gq_e8_quantize with the same worker_base.  gq_e8_tree is this
+ * call with worker_base = 0.                                               */
+int32_t gq_e8_subtree(const void *codes, int64_t n, int64_t d, uint64_t seed, int64_t worker_base,
+                      void *root, void *stream);
+
 /* mean[j] = fp32(N value(root[j])), product in fp64.                        */
 int32_t gq_e8_dequantize(const void *root, int64_t d, const float *norm_dev, float *mean,
                          void *stream);

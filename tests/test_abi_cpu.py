@@ -185,3 +185,12 @@ def test_word_layout_entry_points_reject():
     assert dq(A, 4, 100, 7, 0, 8, NUL, A, NUL) == 1
     assert dq(A, 4, 100, 7, 0, 8, A, U, NUL) == 6
     assert dq(A, 4, 100, 7, 3, 8, A, A, NUL) == 2
+
+
+def test_e8_subtree_rejects():
+    L = gq.lib()
+    assert L.gq_e8_subtree(A, 4, 100, 1, 2, A, NUL) == 2      # worker_base not a multiple of n
+    assert L.gq_e8_subtree(A, 4, 100, 1, -4, A, NUL) == 2     # negative worker_base
+    assert L.gq_e8_subtree(A, 3, 100, 1, 0, A, NUL) == 3      # n not a power of two
+    assert L.gq_e8_subtree(NUL, 4, 100, 1, 4, A, NUL) == 1
+    assert L.gq_e8_subtree(A, 4, 100, 1, 4, U, NUL) == 6

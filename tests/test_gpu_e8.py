@@ -191,3 +191,32 @@ def test_e8_full_size_sampled(key):
     del xd, x
     torch.cuda.empty_cache()
     log(f"workload {key} ok")
+
+
+@pytest.mark.parametrize("n,k", [(16, 4), (8, 2), (8, 1), (4, 4), (32, 8)])
+@pytest.mark.parametrize("d", [17, 10_007])
+def test_device_subtrees_and_pairs_reproduce_the_whole_tree(n, k, d):
+    """n workers on n / k devices of k each: every device quantizes its rows
+    at its worker offset and reduces its subtree with the whole tree's node
+    indices; the levels above, pair by pair with their global (level, node),
+    give the root of the whole tree -- the oracle's, bit for bit."""
+    seed = 77 + n + k + d
+    x = wl.random_rows(n, d, seed=seed, scale=0.2)
+    xd = to_dev(x)
+    norm = gq.gq_global_norm(xd, 2.0, 2.0)
+    N = np.float32(host(norm)[0])
+    roots = []
+    for r in range(n // k):
+        part = xd[r * k:(r + 1) * k].clone()
+        codes = gq.gq_e8_quantize(part, norm, seed, worker_base=r * k)
+        roots.append(gq.gq_e8_subtree(codes, k, d, seed, r * k))
+    level = k.bit_length()  # log2(k) + 1: the first level above the devices
+    while len(roots) > 1:
+        roots = [gq.gq_e8_reduce_pair(roots[2 * m], roots[2 * m + 1], d, seed, level, m)
+                 for m in range(len(roots) // 2)]
+        level += 1
+    whole = gq.gq_e8_tree(gq.gq_e8_quantize(xd, norm, seed), n, d, seed)
+    ocodes = oracle.e8_quantize(x, N, seed)
+    expect = oracle.e8_tree(ocodes, seed)
+    assert np.array_equal(host(roots[0])[:d], expect)
+    assert np.array_equal(host(whole)[:d], expect)
