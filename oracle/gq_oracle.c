@@ -20,7 +20,10 @@
  *     levels (s-i)/s, and exponential dithering Global-E_s with levels
  *     {0} and the powers of two 2^-k, k = 0..s-1.
  *   - Sec. 6 (implementation): quantize, integer Allreduce (here: an exact
- *     sum over the n simulated workers), dequantize once.
+ *     sum over the n simulated workers), dequantize once; the word layout
+ *     whose plain 32-bit word sum adds the codes (a collective's own
+ *     integer SUM) and the re-rounding tree of the 8-bit exponential format
+ *     (Sec. 4 worked example, Sec. 5-6 custom reduction).
  * Philox4x32-10 follows Salmon, Moraes, Dror, Shaw, "Parallel Random
  * Numbers: As Easy as 1, 2, 3" (SC'11), Sec. on the Philox family.
  *
