@@ -13,6 +13,7 @@ means are compared with the oracle evaluated at the device's norm, since
 every code is a function of the norm's bits.
 """
 import math
+import os
 import sys
 import time
 
@@ -30,7 +31,8 @@ INF = math.inf
 DEV = "cuda:0"
 SCH = {"L": oracle.SCHEME_L, "E": oracle.SCHEME_E}
 ORDERS = [1.0, 1.5, 2.0, 2.0, 3.0, INF, INF]
-N_CASES = 60
+# 60 cases by default; GQ_SWEEP_CASES widens the sweep for a longer run
+N_CASES = int(os.environ.get("GQ_SWEEP_CASES", "60"))
 
 
 def log(msg):
