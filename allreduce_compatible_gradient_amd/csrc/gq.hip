@@ -1034,22 +1034,23 @@ __global__ __launch_bounds__(64) void k_norm_from_term(const double *__restrict_
 // integer of magnitude <= n M <= 2^24; the sign is applied by an fma with
 // +-1.  Otherwise int32.  (Prefetching the next worker's inputs into
 // registers was measured to give nothing for fp32 and to cost 3% for bf16.)
+// wb: Philox worker index of row 0 (rows held by one device of several).
 template <int DT, int SCH, bool PRE, bool FACC>
 __device__ __forceinline__ void accumulate_workers(const void *__restrict__ x, int64_t n, int64_t d,
                                                    int64_t j0, bool vec, const QParams &q,
                                                    uint32_t k0, uint32_t k1, float (&accf)[kPer],
-                                                   int (&acci)[kPer])
+                                                   int (&acci)[kPer], uint32_t wb = 0)
 {
     const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
     for (int64_t i = 0; i < n; ++i) {
         float v[kPer];
         load_group<DT>(x, i * d, j0, d, vec, v);
-        const uint4 A = philox10(make_uint4(blo, bhi, (uint32_t)i, 0u), k0, k1);
+        const uint4 A = philox10(make_uint4(blo, bhi, wb + (uint32_t)i, 0u), k0, k1);
         float m[kPer];
         bool tie = false;
         quant_group<SCH, PRE, false>(v, A, q, m, tie);
         if (tie) {
-            const uint4 B = philox10(make_uint4(blo, bhi, (uint32_t)i, 1u), k0, k1);
+            const uint4 B = philox10(make_uint4(blo, bhi, wb + (uint32_t)i, 1u), k0, k1);
             settle_ties<SCH, PRE>(v, A, B, q, m);
         }
 #pragma unroll
@@ -1086,7 +1087,8 @@ template <int DT, bool PRE>
 __device__ __forceinline__ void accumulate_workers_pk16(const void *__restrict__ x, int64_t n,
                                                         int64_t d, int64_t j0, bool vec,
                                                         const QParams &q, uint32_t k0,
-                                                        uint32_t k1, int (&acc)[kPer])
+                                                        uint32_t k1, int (&acc)[kPer],
+                                                        uint32_t wb = 0)
 {
     const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
     const float sigma16 = q.sigma * 0x1p16f, top16 = q.top * 0x1p16f;
@@ -1115,7 +1117,7 @@ __device__ __forceinline__ void accumulate_workers_pk16(const void *__restrict__
             v[2 * k] = __uint_as_float(rw[k] << 16);
             v[2 * k + 1] = __uint_as_float(rw[k] & 0xFFFF0000u);
         }
-        const uint4 A = philox10(make_uint4(blo, bhi, (uint32_t)i, 0u), k0, k1);
+        const uint4 A = philox10(make_uint4(blo, bhi, wb + (uint32_t)i, 0u), k0, k1);
         const uint32_t Aw[kPer / 2] = {A.x, A.y, A.z, A.w};
         uint32_t T[kPer];
 #pragma unroll
@@ -1141,7 +1143,7 @@ __device__ __forceinline__ void accumulate_workers_pk16(const void *__restrict__
         const uint32_t mx = max3_lo16(S[6], S[7], max3_lo16(S[0], S[1], S[2]));
         const bool tie = ((uint16_t)mx == 0xFFFFu) | ((uint16_t)max3_lo16(S[3], S[4], S[5]) == 0xFFFFu);
         if (tie) {
-            const uint4 B = philox10(make_uint4(blo, bhi, (uint32_t)i, 1u), k0, k1);
+            const uint4 B = philox10(make_uint4(blo, bhi, wb + (uint32_t)i, 1u), k0, k1);
 #pragma unroll
             for (int k = 0; k < kPer; ++k) {
                 if ((S[k] & 0xFFFFu) == 0xFFFFu) { // tie: h == F >> 16
@@ -1481,10 +1483,11 @@ __global__ __launch_bounds__(kThreads) void k_quantize_words(const void *__restr
 // fields hold sum_i (code_ij + M) over its n rows, as gq_sum_words of the
 // rows of k_quantize_words, in one pass with the sum in registers.  Block =
 // 2048 words (2048 FPW coordinates); for each of its FPW groups a thread
-// walks the n rows for 8 coordinates, one Philox call per row, then the
-// biased sums go to LDS and are assembled into word quads as in
-// k_quantize_words.
-template <int DT, int SCH, int FPW>
+// walks the n rows for 8 coordinates with the fused pass's accumulators
+// (ACC as in k_compress_mean: fp32 sums, int32, or packed 16-bit pairs for
+// bf16 standard dithering), then the biased sums go to LDS and are
+// assembled into word quads as in k_quantize_words.
+template <int DT, int SCH, int FPW, int ACC>
 __global__ __launch_bounds__(kThreads) void k_compress_words(const void *__restrict__ x, int64_t n,
                                                              int64_t d, int s, uint64_t seed,
                                                              int64_t worker_base,
@@ -1498,6 +1501,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_words(const void *__restr
     const int64_t c_base = tile * kWordsPerBlock * FPW;
     const QParams q = make_qparams(*norm_dev, n, s, SCH);
     const bool vec = (d & 7) == 0;
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32), wb = (uint32_t)worker_base;
     uint32_t w1[kPer]; // FPW == 1: the thread's 8 words
 #pragma unroll
     for (int g = 0; g < FPW; ++g) {
@@ -1505,14 +1509,24 @@ __global__ __launch_bounds__(kThreads) void k_compress_words(const void *__restr
         const int64_t j0 = c_base + rel;
         int acc[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (!q.zero && j0 < d) {
-            for (int64_t i = 0; i < n; ++i) {
-                float v[kPer];
-                int code[kPer];
-                load_group<DT>(x, i * d, j0, d, vec, v);
-                quantize_group_codes<SCH>(v, q, j0, (uint64_t)(worker_base + i), seed, code);
+            if constexpr (ACC == kAccPk16) {
+                if (q.prescale)
+                    accumulate_workers_pk16<DT, true>(x, n, d, j0, vec, q, k0, k1, acc, wb);
+                else
+                    accumulate_workers_pk16<DT, false>(x, n, d, j0, vec, q, k0, k1, acc, wb);
+            } else {
+                float accf[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+                if (q.prescale)
+                    accumulate_workers<DT, SCH, true, ACC == kAccF32>(x, n, d, j0, vec, q, k0, k1,
+                                                                      accf, acc, wb);
+                else
+                    accumulate_workers<DT, SCH, false, ACC == kAccF32>(x, n, d, j0, vec, q, k0,
+                                                                       k1, accf, acc, wb);
+                if (ACC == kAccF32) {
 #pragma unroll
-                for (int k = 0; k < kPer; ++k)
-                    acc[k] += code[k];
+                    for (int k = 0; k < kPer; ++k)
+                        acc[k] = (int)accf[k];
+                }
             }
         }
 #pragma unroll
@@ -1548,6 +1562,36 @@ __global__ __launch_bounds__(kThreads) void k_compress_words(const void *__restr
             if (w_base + wr < rwords)
                 nt_store((uint8_t *)(out + w_base + wr), make_uint4(w[0], w[1], w[2], w[3]));
         }
+    }
+}
+
+// The accumulator of k_compress_words for one fields-per-word count: packed
+// 16-bit pairs for bf16 standard dithering with n M < 2^15, else fp32 sums
+// while n M <= 2^24 (always true for W <= 16), else int32.
+template <int DT, int SCH, int F>
+void launch_compress_words(dim3 grid, hipStream_t st, bool pk16, bool facc, const void *x,
+                           int64_t n, int64_t d, int s, uint64_t seed, int64_t worker_base,
+                           const float *norm_dev, uint32_t *out, int W, uint32_t bias,
+                           int64_t rwords)
+{
+    const dim3 block(kThreads);
+    if constexpr (DT == GQ_IN_BF16 && SCH == GQ_SCHEME_L && F > 1) {
+        if (pk16) {
+            k_compress_words<DT, SCH, F, kAccPk16><<<grid, block, 0, st>>>(
+                x, n, d, s, seed, worker_base, norm_dev, out, W, bias, rwords);
+            return;
+        }
+    }
+    if constexpr (F > 1) {
+        k_compress_words<DT, SCH, F, kAccF32><<<grid, block, 0, st>>>(
+            x, n, d, s, seed, worker_base, norm_dev, out, W, bias, rwords);
+    } else {
+        if (facc)
+            k_compress_words<DT, SCH, F, kAccF32><<<grid, block, 0, st>>>(
+                x, n, d, s, seed, worker_base, norm_dev, out, W, bias, rwords);
+        else
+            k_compress_words<DT, SCH, F, kAccInt><<<grid, block, 0, st>>>(
+                x, n, d, s, seed, worker_base, norm_dev, out, W, bias, rwords);
     }
 }
 
@@ -2546,23 +2590,26 @@ int32_t gq_compress_words_from_norm(const void *x, int32_t dtype, int64_t n, int
     if (tiles > kMaxGrid)
         return fail(GQ_ERR_UNSUPPORTED, "d exceeds the launch limit");
     const uint32_t bias = (uint32_t)(n * top_code(s, scheme)); // < 2^31 by the width rule
-    const dim3 grid((unsigned)tiles), block(kThreads);
+    const dim3 grid((unsigned)tiles);
     hipStream_t st = (hipStream_t)stream;
     uint32_t *out = (uint32_t *)word_sum;
+    const int64_t nm = n * top_code(s, scheme);
+    const bool facc = nm <= ((int64_t)1 << 24);
+    const bool pk16 = dtype == GQ_IN_BF16 && scheme == GQ_SCHEME_L && nm < ((int64_t)1 << 15);
 #define GQ_CW(F)                                                                               \
     do {                                                                                       \
         if (dtype == GQ_IN_F32 && scheme == GQ_SCHEME_L)                                       \
-            k_compress_words<GQ_IN_F32, GQ_SCHEME_L, F><<<grid, block, 0, st>>>(               \
-                x, n, d, s, seed, worker_base, norm_dev, out, code_bits, bias, rwords);        \
+            launch_compress_words<GQ_IN_F32, GQ_SCHEME_L, F>(grid, st, pk16, facc, x, n, d, s, \
+                seed, worker_base, norm_dev, out, code_bits, bias, rwords);                   \
         else if (dtype == GQ_IN_F32)                                                           \
-            k_compress_words<GQ_IN_F32, GQ_SCHEME_E, F><<<grid, block, 0, st>>>(               \
-                x, n, d, s, seed, worker_base, norm_dev, out, code_bits, bias, rwords);        \
+            launch_compress_words<GQ_IN_F32, GQ_SCHEME_E, F>(grid, st, pk16, facc, x, n, d, s, \
+                seed, worker_base, norm_dev, out, code_bits, bias, rwords);                   \
         else if (scheme == GQ_SCHEME_L)                                                        \
-            k_compress_words<GQ_IN_BF16, GQ_SCHEME_L, F><<<grid, block, 0, st>>>(              \
-                x, n, d, s, seed, worker_base, norm_dev, out, code_bits, bias, rwords);        \
+            launch_compress_words<GQ_IN_BF16, GQ_SCHEME_L, F>(grid, st, pk16, facc, x, n, d,  \
+                s, seed, worker_base, norm_dev, out, code_bits, bias, rwords);                \
         else                                                                                   \
-            k_compress_words<GQ_IN_BF16, GQ_SCHEME_E, F><<<grid, block, 0, st>>>(              \
-                x, n, d, s, seed, worker_base, norm_dev, out, code_bits, bias, rwords);        \
+            launch_compress_words<GQ_IN_BF16, GQ_SCHEME_E, F>(grid, st, pk16, facc, x, n, d,  \
+                s, seed, worker_base, norm_dev, out, code_bits, bias, rwords);                \
     } while (0)
     GQ_FPW_SWITCH(word_fields(code_bits), GQ_CW)
 #undef GQ_CW
