@@ -29,13 +29,23 @@
 //                    with n s < 2^15 (vector-ALU bound), the rounding is one
 //                    integer add per coordinate and pairs of coordinates are
 //                    signed and summed in packed int16 lanes.
+//   k_norm_oneshot / k_norm_mid: pass 1 for fp32 inputs above 1 GiB, 16 KB
+//                    one-shot blocks, then a fixed-order middle reduction.
 //   k_quantize / k_reduce_codes / k_dequantize: the same steps unfused, with
 //                    W-bit codes packed through LDS into coalesced words.
+//   k_quantize_words / k_compress_words / k_sum_words / k_dequantize_words:
+//                    floor(32/W) biased fields per 32-bit word, the layout a
+//                    native uint32 SUM all-reduce adds exactly (Sec. 6).
 //   k_local_mean     ablation: per-worker norms (QSGD), fp64 mean.
 //   k_e8_*           the pages' 8-bit exponential format (sign + 7-bit level
 //                    index): quantization, the re-rounding pair step, the
-//                    whole averaging tree as a binary counter in registers,
-//                    dequantization, and the fused norm-to-mean path.
+//                    averaging tree as a binary counter with its stack in
+//                    LDS, dequantization, and the fused norm-to-mean path.
+//
+// Sections below: constants and host-side geometry; device helpers (Philox,
+// bracketing, loads, stores, packing); the norm kernels; the fused and
+// unfused code kernels with the ablation; the word layout; the 8-bit format;
+// launch helpers; the C ABI.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
