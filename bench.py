@@ -97,7 +97,20 @@ def cpu_baseline(w, target_s: float):
     gbs = w.n * d1 * w.elem_bytes / dt / 1e9
     return {"value": round(gbs, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first {d1} of {w.d} coordinates of all {w.n} workers "
-                      f"({w.n * d1} elements, {dt:.1f} s)"}
+                      f"({w.n * d1} elements, {dt:.1f} s)",
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    """The host CPU's model name (Linux), for the CPU baseline's record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def eq8_threshold(rho: float, omega: float) -> float:
