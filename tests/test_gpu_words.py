@@ -181,12 +181,12 @@ def _sample_cols(d, rng, k=20000):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("key", [2, 5])
+@pytest.mark.parametrize("key", [2, 3, 4, 5])
 def test_workload_full_size(key):
-    """Full-size workloads at the minimal width (11 bits, 2 fields per word;
-    9 bits, 3 per word): the word path's sums and mean equal the fused
-    path's at every coordinate, and sampled columns equal the oracle's at
-    the device's norm."""
+    """Full-size workloads at the minimal width (11 and 13 bits, 2 fields per
+    word; 8 bits from bf16 input, 4 per word; 9 bits, 3 per word): the word
+    path's sums and mean equal the fused path's at every coordinate, and
+    sampled columns equal the oracle's at the device's norm."""
     w = wl.WORKLOADS[key]
     threads = min(16, os.cpu_count() or 1)
     log(f"workload {key} {w.name}: generating {w.input_bytes / 1e9:.2f} GB")
