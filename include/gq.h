@@ -286,8 +286,9 @@ int32_t gq_e8_subtree(const void *codes, int64_t n, int64_t d, uint64_t seed, in
 int32_t gq_e8_dequantize(const void *root, int64_t d, const float *norm_dev, float *mean,
                          void *stream);
 
-/* Norm, quantization, tree and dequantization in one call (the tree runs in
- * registers, no codes are materialized); root_or_null receives the root.   */
+/* Norm, quantization, tree and dequantization in one call (the tree runs on
+ * chip, in registers and LDS; no codes are written to memory);
+ * root_or_null receives the root.                                          */
 int32_t gq_e8_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, float q, float p,
                             uint64_t seed, float *mean, float *norm_dev, void *root_or_null,
                             void *workspace, int64_t workspace_bytes, void *stream);
