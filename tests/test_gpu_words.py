@@ -144,6 +144,67 @@ def test_device_sums_add_up_to_the_whole(dtype):
     assert np.array_equal(host(mean), host(fmean))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_subnormal_inputs_take_the_exact_prescale(dtype):
+    """N < 2^-64: |x| and N are scaled by 2^64 first; the word path's words,
+    one-pass row and mean are the oracle's bit for bit."""
+    rng = np.random.default_rng(31)
+    # subnormal values (bf16 keeps 7 fraction bits, so a larger scale)
+    scale = 1e-41 if dtype == "f32" else 1e-39
+    x = (rng.standard_normal((3, 3001)) * scale).astype(np.float32)
+    if dtype == "bf16":
+        x = wl.f32_to_bf16_bits(x)
+    xd = to_dev(x)
+    for scheme, s in (("L", 7), ("E", 9)):
+        W = gq.gq_min_code_bits(3, s, scheme)
+        M = M_of(s, scheme)
+        norm = gq.gq_global_norm(xd, 2.0, 2.0)
+        N = np.float32(host(norm)[0])
+        assert N < 2.0 ** -64
+        ocodes = oracle.quantize(x, N, s, SCH[scheme], 4)
+        assert np.any(ocodes != 0)
+        owords = oracle.pack_words(ocodes, W, M)
+        assert np.array_equal(words_host(gq.gq_quantize_words(xd, s, scheme, norm, 4, W)), owords)
+        osum = oracle.sum_words(owords)
+        assert np.array_equal(words_host(gq.gq_compress_words_from_norm(xd, s, scheme, norm, 4, W)),
+                              osum)
+        mean = gq.gq_dequantize_words(u32(osum), 3, 3001, s, scheme, W, norm)
+        sums = oracle.unpack_word_sums(osum, 3, 3001, W, M)
+        assert np.array_equal(host(mean), oracle.dequantize(sums, 3, N, s, SCH[scheme]))
+
+
+def test_non_finite_inputs_stay_in_their_fields():
+    """NaN and +-inf inputs give codes in [-M, M], so every field stays in
+    [0, 2M] and no field carries into its neighbour."""
+    x = wl.random_rows(4, 4096, seed=9)
+    x[0, 5] = np.nan
+    x[1, 100] = np.inf
+    x[2, 2000] = -np.inf
+    xd = to_dev(x)
+    norm = gq.gq_global_norm(xd, INF, INF)
+    for scheme, s in (("L", 7), ("E", 6)):
+        W = gq.gq_min_code_bits(4, s, scheme)
+        M = M_of(s, scheme)
+        f = oracle.word_fields(W)
+        rows = words_host(gq.gq_quantize_words(xd, s, scheme, norm, 1, W))
+        for r in rows:
+            fields = (r[:, None] >> (W * np.arange(f, dtype=np.uint32))) & ((1 << W) - 1)
+            assert fields.max() <= 2 * M
+        total = words_host(gq.gq_compress_words_from_norm(xd, s, scheme, norm, 1, W))
+        sums = oracle.unpack_word_sums(total, 4, 4096, W, M)
+        assert np.abs(sums).max() <= 4 * M
+
+
+def test_empty_rows_launch_nothing():
+    xd = torch.zeros((3, 0), dtype=torch.float32, device=DEV)
+    norm = torch.zeros(1, dtype=torch.float32, device=DEV)
+    assert gq.gq_quantize_words(xd, 7, "L", norm, 1, 6).numel() == 0
+    assert gq.gq_compress_words_from_norm(xd, 7, "L", norm, 1, 6).numel() == 0
+    assert gq.gq_dequantize_words(torch.zeros(0, dtype=torch.int32, device=DEV), 3, 0, 7, "L", 6,
+                                  norm).numel() == 0
+    torch.cuda.synchronize()
+
+
 def test_zero_norm_gives_the_bias_only():
     """N = 0: every code is 0, so each field holds M and the mean is 0."""
     n, d, s, W = 3, 5000, 7, 6
