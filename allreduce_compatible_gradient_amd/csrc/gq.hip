@@ -1489,6 +1489,56 @@ __global__ __launch_bounds__(kThreads) void k_quantize_words(const void *__restr
     }
 }
 
+// The same for 3, 5, 6 or 10 fields per word, where a thread's 8
+// coordinates straddle unaligned words: a block covers 2048 words
+// (2048 FPW coordinates); thread t loads words 8 t .. 8 t + 7 with two
+// 16-byte loads, decodes their 8 FPW values into LDS, and after one barrier
+// the block stores the mean with 16-byte stores, 4 KB per instruction.
+template <int SCH, int FPW>
+__global__ __launch_bounds__(kThreads) void k_dequantize_words_lds(
+    const uint32_t *__restrict__ wsum, int64_t n, int64_t d, int s, int W, uint32_t M,
+    int64_t rwords, const float *__restrict__ norm_dev, float *__restrict__ mean)
+{
+    static_assert(FPW == 3 || FPW == 5 || FPW == 6 || FPW == 10,
+                  "field counts whose words do not align with 8 coordinates");
+    constexpr int kCoords = kWordsPerBlock * FPW; // coordinates per block
+    __shared__ alignas(16) float lds[kCoords];
+    const int64_t c_base = (int64_t)blockIdx.x * kCoords;
+    const int64_t w0 = (int64_t)blockIdx.x * kWordsPerBlock + (int64_t)threadIdx.x * kPer;
+    const QParams q = make_qparams(*norm_dev, n, s, SCH);
+    const uint32_t mask = (1u << W) - 1u; // W <= 10 here
+    const uint32_t bias = (uint32_t)(n * (int64_t)M);
+    uint32_t w[kPer];
+    {
+        const uint4 a = (w0 < rwords) ? *(const uint4 *)(wsum + w0) : make_uint4(0, 0, 0, 0);
+        const uint4 b = (w0 + 4 < rwords) ? *(const uint4 *)(wsum + w0 + 4) : make_uint4(0, 0, 0, 0);
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+#pragma unroll
+        for (int f = 0; f < FPW; ++f) {
+            const int32_t v = (int32_t)(((w[u] >> (W * f)) & mask) - bias);
+            lds[((int)threadIdx.x * kPer + u) * FPW + f] = (float)((double)v * q.kappa);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kCoords / (4 * kThreads); ++r) {
+        const int c = (r * kThreads + (int)threadIdx.x) * 4;
+        const int64_t j = c_base + c;
+        if (j + 4 <= d) {
+            *(float4 *)(mean + j) = *(const float4 *)(lds + c);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (j + k < d)
+                    mean[j + k] = lds[c + k];
+        }
+    }
+}
+
 // A device's own rows summed before the all-reduce: the word row whose
 // fields hold sum_i (code_ij + M) over its n rows, as gq_sum_words of the
 // rows of k_quantize_words, in one pass with the sum in registers.  Block =
@@ -2668,6 +2718,30 @@ int32_t gq_dequantize_words(const void *word_sum, int64_t n, int64_t d, int32_t 
     const dim3 grid((unsigned)blocks), block(kThreads);
     hipStream_t st = (hipStream_t)stream;
     const uint32_t *ws = (const uint32_t *)word_sum;
+    const int fpw = word_fields(code_bits);
+    if (fpw == 3 || fpw == 5 || fpw == 6 || fpw == 10) {
+        // 3, 5, 6 or 10 fields per word: whole words per thread, stores staged in LDS
+        const int64_t rwords = gq_word_row_bytes(d, code_bits) / 4;
+        const int64_t nw = (d + fpw - 1) / fpw;
+        const dim3 g2((unsigned)((nw + kWordsPerBlock - 1) / kWordsPerBlock));
+#define GQ_DWL(F)                                                                               \
+    do {                                                                                        \
+        if (scheme == GQ_SCHEME_L)                                                              \
+            k_dequantize_words_lds<GQ_SCHEME_L, F><<<g2, block, 0, st>>>(                       \
+                ws, n, d, s, code_bits, M, rwords, norm_dev, mean);                             \
+        else                                                                                    \
+            k_dequantize_words_lds<GQ_SCHEME_E, F><<<g2, block, 0, st>>>(                       \
+                ws, n, d, s, code_bits, M, rwords, norm_dev, mean);                             \
+    } while (0)
+        switch (fpw) {
+        case 10: GQ_DWL(10); break;
+        case 6: GQ_DWL(6); break;
+        case 5: GQ_DWL(5); break;
+        case 3: GQ_DWL(3); break;
+        }
+#undef GQ_DWL
+        return check_launch("k_dequantize_words_lds");
+    }
 #define GQ_DW(F)                                                                                \
     do {                                                                                        \
         if (scheme == GQ_SCHEME_L)                                                              \
@@ -2677,7 +2751,13 @@ int32_t gq_dequantize_words(const void *word_sum, int64_t n, int64_t d, int32_t 
             k_dequantize_words<GQ_SCHEME_E, F><<<grid, block, 0, st>>>(ws, n, d, s, code_bits,  \
                                                                        M, norm_dev, mean);      \
     } while (0)
-    GQ_FPW_SWITCH(word_fields(code_bits), GQ_DW)
+    switch (fpw) {
+    case 16: GQ_DW(16); break;
+    case 8: GQ_DW(8); break;
+    case 4: GQ_DW(4); break;
+    case 2: GQ_DW(2); break;
+    default: GQ_DW(1); break;
+    }
 #undef GQ_DW
     return check_launch("k_dequantize_words");
 }
