@@ -194,3 +194,40 @@ def test_e8_subtree_rejects():
     assert L.gq_e8_subtree(A, 3, 100, 1, 0, A, NUL) == 3      # n not a power of two
     assert L.gq_e8_subtree(NUL, 4, 100, 1, 4, A, NUL) == 1
     assert L.gq_e8_subtree(A, 4, 100, 1, 4, U, NUL) == 6
+
+
+def test_header_serves_a_plain_c_caller(tmp_path):
+    """include/gq.h compiles as C99 and C++11, and a C program linked against
+    libgq.so gets sizes, status names and argument errors without a GPU."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "caller.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include <string.h>
+#include "gq.h"
+int main(void)
+{
+    if (gq_min_code_bits(8, 127, GQ_SCHEME_L) != 11) return 1;
+    if (gq_code_row_bytes(25557032, 11) != 35140928) return 2; /* 16 ceil(d 11 / 128) */
+    if (gq_word_row_bytes(64, 9) != 96) return 3;
+    if (strcmp(gq_status_str(GQ_ERR_ALIGN), "GQ_ERR_ALIGN") != 0) return 4;
+    float norm;
+    if (gq_global_norm(NULL, GQ_IN_F32, 4, 100, 2.0f, 2.0f, &norm, NULL, 0, NULL) != GQ_ERR_NULL)
+        return 5;
+    if (gq_last_error()[0] == '\0') return 6;
+    puts("ok");
+    return 0;
+}
+""")
+    lib_dir = os.path.join(ROOT, "allreduce_compatible_gradient_amd")
+    exe = tmp_path / "caller"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-L", lib_dir, "-lgq",
+                    f"-Wl,-rpath,{lib_dir}", "-o", str(exe)], check=True, timeout=120)
+    subprocess.run(["g++", "-std=c++11", "-Wall", "-Werror", "-fsyntax-only", "-x", "c++",
+                    "-I", os.path.join(ROOT, "include"), str(src)], check=True, timeout=120)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
