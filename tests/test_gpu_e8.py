@@ -195,13 +195,14 @@ def test_e8_full_size_sampled(key):
 
 @pytest.mark.parametrize("n,k", [(16, 4), (8, 2), (8, 1), (4, 4), (32, 8)])
 @pytest.mark.parametrize("d", [17, 10_007])
-def test_device_subtrees_and_pairs_reproduce_the_whole_tree(n, k, d):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_device_subtrees_and_pairs_reproduce_the_whole_tree(n, k, d, dtype):
     """n workers on n / k devices of k each: every device quantizes its rows
     at its worker offset and reduces its subtree with the whole tree's node
     indices; the levels above, pair by pair with their global (level, node),
     give the root of the whole tree -- the oracle's, bit for bit."""
     seed = 77 + n + k + d
-    x = wl.random_rows(n, d, seed=seed, scale=0.2)
+    x = wl.random_rows(n, d, seed=seed, dtype=dtype, scale=0.2)
     xd = to_dev(x)
     norm = gq.gq_global_norm(xd, 2.0, 2.0)
     N = np.float32(host(norm)[0])

@@ -106,13 +106,15 @@ def test_words_match_oracle(n0, s, scheme, W, dtype):
 
 
 @pytest.mark.parametrize("n0,s,scheme,W", [c for c in _cases() if c[0] > 1 or c[3] <= 4])
-def test_compress_words_equals_the_summed_rows(n0, s, scheme, W):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_compress_words_equals_the_summed_rows(n0, s, scheme, W, dtype):
     """One pass over a device's rows: the word-wise sum of its rows' words,
-    bit-exact against the oracle, for every fields-per-word count."""
+    bit-exact against the oracle, for every fields-per-word count (bf16
+    standard dithering takes the packed 16-bit accumulators)."""
     for n, d in SHAPES:
         n = min(n, n0)
         seed = 11 * n + d + W
-        x = wl.random_rows(n, d, seed=seed, scale=0.3)
+        x = wl.random_rows(n, d, seed=seed, dtype=dtype, scale=0.3)
         xd = to_dev(x)
         norm = gq.gq_global_norm(xd, 2.0, 2.0)
         N = np.float32(host(norm)[0])
