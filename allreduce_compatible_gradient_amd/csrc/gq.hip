@@ -1417,7 +1417,9 @@ __host__ __device__ constexpr int word_fields(int W) { return 32 / W; }
 template <int FPW>
 using WordLdsT = typename std::conditional<(FPW >= 4), uint8_t, uint16_t>::type;
 
-template <int DT, int SCH, int FPW>
+// PK: bf16 standard dithering, codes formed by the fused pass's packed
+// 16-bit loop over one row (the row's codes are its one-row sum).
+template <int DT, int SCH, int FPW, bool PK = false>
 __global__ __launch_bounds__(kThreads) void k_quantize_words(const void *__restrict__ x, int64_t n,
                                                              int64_t d, int s, uint64_t seed,
                                                              int64_t worker_base,
@@ -1457,9 +1459,20 @@ __global__ __launch_bounds__(kThreads) void k_quantize_words(const void *__restr
             const int64_t j0 = c_base + rel;
             int code[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
             if (!q.zero && j0 < d) {
-                float v[kPer];
-                load_group<DT>(x, i * d, j0, d, vec, v);
-                quantize_group_codes<SCH>(v, q, j0, (uint64_t)(worker_base + i), seed, code);
+                if constexpr (PK) {
+                    const void *xrow = (const uint16_t *)x + i * d;
+                    const uint32_t wk = (uint32_t)(worker_base + i);
+                    if (q.prescale)
+                        accumulate_workers_pk16<DT, true>(xrow, 1, d, j0, vec, q, (uint32_t)seed,
+                                                          (uint32_t)(seed >> 32), code, wk);
+                    else
+                        accumulate_workers_pk16<DT, false>(xrow, 1, d, j0, vec, q, (uint32_t)seed,
+                                                           (uint32_t)(seed >> 32), code, wk);
+                } else {
+                    float v[kPer];
+                    load_group<DT>(x, i * d, j0, d, vec, v);
+                    quantize_group_codes<SCH>(v, q, j0, (uint64_t)(worker_base + i), seed, code);
+                }
             }
             E b[kPer];
 #pragma unroll
@@ -2616,6 +2629,9 @@ int32_t gq_quantize_words(const void *x, int32_t dtype, int64_t n, int64_t d, in
                 x, n, d, s, seed, worker_base, norm_dev, wd, code_bits, M, rwords, tiles);     \
         else if (dtype == GQ_IN_F32)                                                           \
             k_quantize_words<GQ_IN_F32, GQ_SCHEME_E, F><<<grid, block, 0, st>>>(               \
+                x, n, d, s, seed, worker_base, norm_dev, wd, code_bits, M, rwords, tiles);     \
+        else if (scheme == GQ_SCHEME_L && F > 1)                                               \
+            k_quantize_words<GQ_IN_BF16, GQ_SCHEME_L, F, (F > 1)><<<grid, block, 0, st>>>(     \
                 x, n, d, s, seed, worker_base, norm_dev, wd, code_bits, M, rwords, tiles);     \
         else if (scheme == GQ_SCHEME_L)                                                        \
             k_quantize_words<GQ_IN_BF16, GQ_SCHEME_L, F><<<grid, block, 0, st>>>(              \
