@@ -125,6 +125,18 @@ def test_random_case(k):
     part = gq.gq_quantize(xd[n - 1:n].clone(), s, c["scheme"], norm, c["seed"], W,
                           worker_base=n - 1)
     assert np.array_equal(host(part)[0], oracle.pack(codes, W)[n - 1])
+    # the word layout for a native uint32 SUM: rows, their sum, the one-pass
+    # row and the mean from it
+    M = oracle.top_code(s, SCH[c["scheme"]])
+    owords = oracle.pack_words(codes, W, M)
+    words = gq.gq_quantize_words(xd, s, c["scheme"], norm, c["seed"], W)
+    assert np.array_equal(host(words).view(np.uint32), owords)
+    wsum = gq.gq_sum_words(words, n, d, W)
+    assert np.array_equal(host(wsum).view(np.uint32), oracle.sum_words(owords))
+    one = gq.gq_compress_words_from_norm(xd, s, c["scheme"], norm, c["seed"], W)
+    assert np.array_equal(host(one), host(wsum))
+    wmean = gq.gq_dequantize_words(wsum, n, d, s, c["scheme"], W, norm)
+    assert np.array_equal(host(wmean), mean)
 
 
 @pytest.mark.parametrize("k", range(0, N_CASES, 3))
