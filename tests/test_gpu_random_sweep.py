@@ -167,3 +167,12 @@ def test_random_case_local_and_e8(k):
         emean = oracle.e8_dequantize(root, gN)
     assert np.array_equal(host(groot)[:d], root)
     assert np.array_equal(host(gmean), emean)
+    if m >= 2:
+        # two devices of m / 2 workers: subtrees at their offsets, then the top pair
+        h = m // 2
+        xmd = to_dev(xm)
+        roots = [gq.gq_e8_subtree(gq.gq_e8_quantize(xmd[r * h:(r + 1) * h].clone(), gnorm, seed,
+                                                    worker_base=r * h), h, d, seed, r * h)
+                 for r in range(2)]
+        top = gq.gq_e8_reduce_pair(roots[0], roots[1], d, seed, h.bit_length(), 0)
+        assert np.array_equal(host(top)[:d], root)
