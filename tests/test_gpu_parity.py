@@ -160,6 +160,46 @@ def test_many_workers(n, d, scheme, s, q, p):
         assert np.array_equal(host(gl), lmean)
 
 
+@pytest.mark.parametrize("scheme,s,n", [("E", 28, 3), ("L", 1 << 23, 4), ("E", 26, 9),
+                                         ("L", 5_000_000, 7)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_int32_accumulator_above_2_24(scheme, s, n, dtype):
+    """Sums of magnitude up to n M > 2^24 are no longer exact in fp32, so the
+    fused pass and the one-pass word row (one field per word at these widths)
+    accumulate in int32: every entry point that takes that branch, at the
+    minimal width and at 32 bits, against the oracle."""
+    d = 6151
+    M = M_of(s, scheme)
+    assert n * M > 1 << 24
+    x = wl.random_rows(n, d, seed=s + n, dtype="f32", scale=0.5)
+    x[:, :64] = 4.0  # t at the top level in every row: sums of +-n M
+    x[1, :32] = -4.0
+    if dtype == "bf16":
+        x = wl.f32_to_bf16_bits(x)
+    seed = 0x0123456789ABCDEF + n
+    N, sums, mean = oracle.compress_mean(x, s, INF, INF, SCH[scheme], seed)
+    assert np.abs(sums).max() > 1 << 24
+    codes = oracle.quantize(x, N, s, SCH[scheme], seed)
+    Wmin = gq.gq_min_code_bits(n, s, scheme)
+    xd = to_dev(x)
+    for W in sorted({Wmin, 32}):
+        gmean, gnorm, gsum = gq.gq_compress_mean(xd, s, INF, INF, scheme, seed, code_bits=W,
+                                                 want_code_sum=True)
+        check_norm(host(gnorm)[0], N)
+        assert np.array_equal(host(gsum), oracle.pack(sums.astype(np.int32), W)[0]), W
+        assert np.array_equal(host(gmean), mean), W
+        fmean, fsum = gq.gq_compress_mean_from_norm(xd, s, scheme, seed, gnorm, code_bits=W,
+                                                    want_code_sum=True)
+        assert np.array_equal(host(fsum), host(gsum)) and np.array_equal(host(fmean), mean), W
+        owords = oracle.pack_words(codes, W, M)
+        one = gq.gq_compress_words_from_norm(xd, s, scheme, gnorm, seed, W)
+        assert np.array_equal(host(one).view(np.uint32), oracle.sum_words(owords)), W
+        words = gq.gq_quantize_words(xd, s, scheme, gnorm, seed, W)
+        assert np.array_equal(host(words).view(np.uint32), owords), W
+        wmean = gq.gq_dequantize_words(one, n, d, s, scheme, W, gnorm)
+        assert np.array_equal(host(wmean), mean), W
+
+
 def test_worker_base_shards_reproduce_the_whole():
     n, d, s = 6, 3000, 9
     x = wl.random_rows(n, d, seed=5)
@@ -368,7 +408,7 @@ def test_large_input_norm(n, d, dtype, q, p):
 
 # ---------------------------------------------------------------------------
 # General real orders (fp64 pow): the norm within 1e-6 relative; codes and
-# means bit-exact whenever the fp32 norm agrees to the bit
+# means bit-exact against the oracle at the device's norm
 
 @pytest.mark.parametrize("q,p", [(1.0, 1.0), (1.5, 3.0), (3.0, INF), (INF, 1.5), (2.0, 4.0),
                                  (7.25, 2.0)])
@@ -382,9 +422,13 @@ def test_general_orders(q, p, dtype):
                                              want_code_sum=True)
     gN = np.float32(host(gnorm)[0])
     assert abs(float(gN) - float(N)) <= 1e-6 * float(N)
-    # fp64 pow differs between the device library and the host libm by at most
-    # an ulp, so the fp32 norm agrees to the bit unless it sits on a rounding
-    # boundary; every code depends on those bits
-    assert gN == N, f"fp32 norm differs in the last bit ({gN!r} vs {N!r})"
+    if gN != N:
+        # fp64 pow of the device library and of the host libm may differ by
+        # an ulp, which can move the fp32 norm by its last bit; every code is
+        # a function of the norm's bits, so compare at the device's norm
+        log(f"q={q} p={p} {dtype}: norm differs in the last bit ({gN!r} vs {N!r})")
+        ocodes = oracle.quantize(x, gN, s, oracle.SCHEME_L, 8)
+        sums = oracle.sum_codes(ocodes)
+        mean = oracle.dequantize(sums, n, gN, s, oracle.SCHEME_L)
     assert np.array_equal(host(gsum), oracle.pack(sums.astype(np.int32), W)[0])
     assert np.array_equal(host(gmean), mean)
