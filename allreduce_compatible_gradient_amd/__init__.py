@@ -51,6 +51,8 @@ SIGNATURES = {
                                           _vp, _vp, _vp]),
     "gq_compress_mean": (_i32, [_vp, _i32, _i64, _i64, _i32, _f32, _f32, _i32, _u64, _i32, _vp,
                                 _vp, _vp, _vp, _i64, _vp]),
+    "gq_compress_mean_noalloc": (_i32, [_vp, _i32, _i64, _i64, _i32, _f32, _f32, _i32, _u64,
+                                        _i32, _vp, _vp, _vp, _vp]),
     "gq_qsgd_local_mean": (_i32, [_vp, _i32, _i64, _i64, _i32, _u64, _vp, _vp, _vp, _i32, _vp,
                                   _i64, _vp]),
     "gq_e8_row_bytes": (_i64, [_i64]),
@@ -363,6 +365,26 @@ def gq_compress_mean(x: torch.Tensor, s: int, q, p, scheme, seed: int, *, code_b
     _check(lib().gq_compress_mean(_ptr(x), dt, n, d, s, _order(q), _order(p), _scheme(scheme), seed,
                                   code_bits, _ptr(mean), _ptr(norm), _ptr(code_sum), _ptr(ws),
                                   _nbytes(ws), _stream(stream)))
+    return mean, norm, code_sum
+
+
+# bytes of the device array behind gq_compress_mean_noalloc (GQ_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def gq_compress_mean_noalloc(x: torch.Tensor, s: int, q, p, scheme, seed: int, *, mean,
+                             norm, code_bits: int = 0, code_sum=None, stream=None):
+    """gq_compress_mean with the library's own scratch instead of a workspace:
+    the caller passes every output (nothing is allocated on this path).
+    Returns (mean, norm, code_sum)."""
+    dt = _input(x)
+    n, d = x.shape
+    _buf(mean, 4 * d, "mean", x.device, torch.float32)
+    _buf(norm, 4, "norm", x.device, torch.float32)
+    _buf(code_sum, max(gq_code_row_bytes(d, code_bits), 0), "code_sum", x.device)
+    _check(lib().gq_compress_mean_noalloc(_ptr(x), dt, n, d, s, _order(q), _order(p),
+                                          _scheme(scheme), seed, code_bits, _ptr(mean),
+                                          _ptr(norm), _ptr(code_sum), _stream(stream)))
     return mean, norm, code_sum
 
 

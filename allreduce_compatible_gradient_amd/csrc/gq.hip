@@ -53,9 +53,17 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "gq.h"
+
+// Library-owned scratch of gq_compress_mean_noalloc: the norm pass's
+// partial sums for callers that cannot allocate.  Each device holds its own
+// copy; host code never uses this name as an address (in host code it is a
+// stand-in, not device memory) -- the device address comes from
+// hipGetSymbolAddress, once per device, below.
+static __device__ __align__(256) uint8_t scratch[GQ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -2389,6 +2397,43 @@ int32_t launch_compress(const void *x, int32_t dtype, int64_t n, int64_t d, int3
     return check_launch("k_compress_mean");
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices]; // address of `scratch` on each device, once looked up
+
+// Device address of the current device's copy of `scratch`, looked up on
+// the first call on that device.  stream, if not NULL, must belong to it.
+int32_t noalloc_scratch(hipStream_t stream, void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(GQ_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(GQ_ERR_UNSUPPORTED, "device %d beyond the %d the library tracks", dev,
+                    kMaxDevices);
+    if (stream) {
+        int sdev = -1;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess)
+            return fail(GQ_ERR_DEVICE, "hipStreamGetDevice: %s", hipGetErrorString(e));
+        if (sdev != dev)
+            return fail(GQ_ERR_ARG, "stream belongs to device %d, the current device is %d",
+                        sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(GQ_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return GQ_OK;
+}
+
 } // namespace
 
 // ---------------------------------------------------------------------------
@@ -2823,6 +2868,41 @@ int32_t gq_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int
     GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
     hipStream_t st = (hipStream_t)stream;
     GQ_TRY(launch_norm(x, dtype, n, d, q, p, false, norm_dev, workspace, 0, st));
+    return launch_compress(x, dtype, n, d, s, scheme, seed, norm_dev, code_bits, mean,
+                           code_sum_or_null, st);
+}
+
+int32_t gq_compress_mean_noalloc(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                                 float q, float p, int32_t scheme, uint64_t seed,
+                                 int32_t code_bits, float *mean, float *norm_dev,
+                                 void *code_sum_or_null, void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    GQ_TRY(validate_scheme(s, scheme));
+    if (!norm_dev || (!mean && d > 0))
+        return fail(GQ_ERR_NULL, "norm_dev or mean is NULL");
+    if (!order_ok(q) || !order_ok(p))
+        return fail(GQ_ERR_UNSUPPORTED, "q and p must be reals >= 1 or +inf");
+    if (min_bits(n, s, scheme) > 32)
+        return fail(GQ_ERR_CODE_WIDTH, "sums of %lld codes do not fit 32 bits", (long long)n);
+    if (code_sum_or_null) {
+        GQ_TRY(validate_width(n, s, scheme, code_bits));
+        if (!aligned16(code_sum_or_null))
+            return fail(GQ_ERR_ALIGN, "code_sum is not 16-byte aligned");
+    }
+    if (!aligned16(mean))
+        return fail(GQ_ERR_ALIGN, "mean is not 16-byte aligned");
+    const int64_t need = ws_layout(n, d).total;
+    if (need > GQ_NOALLOC_SCRATCH_BYTES)
+        return fail(GQ_ERR_WORKSPACE,
+                    "n = %lld, d = %lld needs %lld bytes of scratch, beyond the %lld the "
+                    "no-allocation entry point holds (use gq_compress_mean with a workspace)",
+                    (long long)n, (long long)d, (long long)need,
+                    (long long)GQ_NOALLOC_SCRATCH_BYTES);
+    hipStream_t st = (hipStream_t)stream;
+    void *ws = nullptr;
+    GQ_TRY(noalloc_scratch(st, &ws));
+    GQ_TRY(launch_norm(x, dtype, n, d, q, p, false, norm_dev, ws, 0, st));
     return launch_compress(x, dtype, n, d, s, scheme, seed, norm_dev, code_bits, mean,
                            code_sum_or_null, st);
 }

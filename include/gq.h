@@ -40,7 +40,8 @@
  *   - Memory: every pointer is a DEVICE pointer owned by the caller.  x,
  *     mean and packed code buffers must be 16-byte aligned.  With d == 0
  *     the per-coordinate buffers (x, codes, sums, mean) may be NULL.  The library
- *     allocates nothing and keeps no state between calls.
+ *     allocates nothing and keeps no state between calls, except the
+ *     device array behind gq_compress_mean_noalloc (below).
  *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Calls only
  *     enqueue kernels and never synchronize; results are ready when the
  *     stream reaches them.  Scalars computed on the device (the norm) stay
@@ -224,6 +225,34 @@ int32_t gq_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int
                          float p, int32_t scheme, uint64_t seed, int32_t code_bits, float *mean,
                          float *norm_dev, void *code_sum_or_null, void *workspace,
                          int64_t workspace_bytes, void *stream);
+
+/* gq_compress_mean without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * gq_compress_mean, bit for bit, except that the norm pass keeps its
+ * partial sums in a library-owned device array of GQ_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) instead of a workspace; every GPU the library runs on holds its
+ * own copy of that array until the process ends.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine).
+ *   - Size limit: inputs with gq_workspace_bytes(n, d) >
+ *     GQ_NOALLOC_SCRATCH_BYTES are rejected with GQ_ERR_WORKSPACE before
+ *     any HIP call (fp32 inputs up to about 32 GiB fit; the per-worker
+ *     values cap n at about 500k).
+ *   - Device: the array used is the current device's; a non-NULL stream
+ *     must belong to the current device (GQ_ERR_ARG otherwise).  The first
+ *     call on a device looks up its copy's address (hipGetSymbolAddress);
+ *     a failure there returns GQ_ERR_DEVICE.
+ *   - Concurrency: every call on one GPU shares that GPU's array.  Calls
+ *     that may overlap on one GPU (different streams, or host threads
+ *     without ordering) race on it and give undefined results; serialize
+ *     them, or use gq_compress_mean with separate workspaces.  No value
+ *     carries between calls: each call writes every scratch word it reads
+ *     before reading it, so nothing needs clearing.                       */
+#define GQ_NOALLOC_SCRATCH_BYTES (16LL << 20)
+int32_t gq_compress_mean_noalloc(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                                 float q, float p, int32_t scheme, uint64_t seed,
+                                 int32_t code_bits, float *mean, float *norm_dev,
+                                 void *code_sum_or_null, void *stream);
 
 /* Ablation: QSGD with LOCAL norms, the scheme Global-QSGD replaces (Sec. 3:
  * each worker normalizes by its own norm).  Worker i uses

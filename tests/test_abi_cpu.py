@@ -142,6 +142,25 @@ def test_other_entry_points_reject():
     assert L.gq_qsgd_local_mean(A, 0, 4, 100, 3, 1, NUL, A, NUL, 0, A, ws, NUL) == 1
 
 
+def test_noalloc_entry_point_rejects():
+    """The no-allocation entry point checks every argument, and the scratch
+    it would need, before any HIP call (so these run without a GPU)."""
+    L = gq.lib()
+    cap = gq.NOALLOC_SCRATCH_BYTES
+    assert L.gq_compress_mean_noalloc(NUL, 0, 4, 100, 7, 2.0, 2.0, 0, 1, 8, A, A, NUL, NUL) == 1
+    assert L.gq_compress_mean_noalloc(A, 0, 4, 100, 7, 2.0, 0.0, 0, 1, 8, A, A, NUL, NUL) == 3
+    assert L.gq_compress_mean_noalloc(A, 0, 4, 100, 7, 2.0, 2.0, 0, 1, 5, A, A, A, NUL) == 4
+    assert L.gq_compress_mean_noalloc(A, 0, 4, 100, 7, 2.0, 2.0, 0, 1, 8, U, A, NUL, NUL) == 6
+    assert L.gq_compress_mean_noalloc(A, 0, 4, 100, 7, 2.0, 2.0, 0, 1, 8, A, NUL, NUL, NUL) == 1
+    # sizes whose norm-pass scratch exceeds the array: rejected, with the size named
+    for n, d in ((1 << 20, 1), (600_000, 4096), (4, 9_000_000_000)):
+        assert gq.gq_workspace_bytes(n, d) > cap
+        assert L.gq_compress_mean_noalloc(A, 0, n, d, 7, 2.0, 2.0, 0, 1, 0, A, A, NUL, NUL) == 5
+        assert str(cap) in L.gq_last_error().decode()
+    # the largest workload's scratch fits (16 GB of fp32 input)
+    assert gq.gq_workspace_bytes(64, 64_000_000) <= cap
+
+
 def test_binding_fails_loudly_without_a_gpu():
     torch = pytest.importorskip("torch")
     if torch.cuda.is_available():
