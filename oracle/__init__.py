@@ -341,6 +341,131 @@ def compress_mean_cols(x: np.ndarray, N, s: int, scheme: int, seed: int, cols) -
     return sums, mean
 
 
+# ---------------------------------------------------------------------------
+# Whole rows in parallel host threads: the same oracle calls over blocks of
+# columns (or rows), gathered in place.  Threads only split the work; each
+# block is one call of the function above it, so the results are those of a
+# single call over every column.
+
+def _threads(threads: int | None) -> int:
+    if threads:
+        return max(1, int(threads))
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return max(1, min(16, avail))
+
+
+def col_blocks(d: int, threads: int | None = None, align: int = 128):
+    """[a, b) column ranges covering [0, d): starts are multiples of align
+    (so that W-bit packed rows split at whole bytes), about 4 per thread."""
+    t = _threads(threads)
+    want = max(1, 4 * t)
+    step = max(align, -(-d // want))
+    step = -(-step // align) * align
+    return [(a, min(d, a + step)) for a in range(0, d, step)]
+
+
+def run_blocks(fn, blocks, threads: int | None = None):
+    """fn(a, b) over every block, in a pool of host threads (ctypes calls
+    release the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+    t = _threads(threads)
+    if t == 1 or len(blocks) <= 1:
+        for a, b in blocks:
+            fn(a, b)
+        return
+    with ThreadPoolExecutor(max_workers=t) as ex:
+        for f in [ex.submit(fn, a, b) for a, b in blocks]:
+            f.result()
+
+
+def compress_mean_all(x: np.ndarray, N, s: int, scheme: int, seed: int,
+                      threads: int | None = None, d_end: int | None = None):
+    """compress_mean_cols over every column in [0, d_end) (default d), split
+    into column blocks run in host threads: (sums int64, mean float32)."""
+    x = _rows(x)
+    n, d = x.shape
+    d_end = d if d_end is None else d_end
+    sums = np.zeros(d_end, dtype=np.int64)
+    mean = np.zeros(d_end, dtype=np.float32)
+    dt = _x_dtype(x)
+
+    def one(a, b):
+        cols = np.arange(a, b, dtype=np.int64)
+        lib().oracle_compress_mean_cols(_ptr(x), dt, n, d, float(N), s, scheme, seed,
+                                        _ptr(cols), b - a, _ptr(sums[a:b]), _ptr(mean[a:b]))
+
+    run_blocks(one, col_blocks(d_end, threads), threads)
+    return sums, mean
+
+
+def e8_compress_all(x: np.ndarray, N, seed: int, threads: int | None = None):
+    """e8_compress_cols over every column, in column blocks: (root, mean)."""
+    x = _rows(x)
+    n, d = x.shape
+    if n & (n - 1):
+        raise ValueError("the tree needs a power-of-two number of rows")
+    root = np.zeros(d, dtype=np.uint8)
+    mean = np.zeros(d, dtype=np.float32)
+    dt = _x_dtype(x)
+
+    def one(a, b):
+        cols = np.arange(a, b, dtype=np.int64)
+        lib().oracle_e8_compress_cols(_ptr(x), dt, n, d, float(N), seed, _ptr(cols), b - a,
+                                      _ptr(root[a:b]), _ptr(mean[a:b]))
+
+    run_blocks(one, col_blocks(d, threads), threads)
+    return root, mean
+
+
+def qsgd_local_all(x: np.ndarray, norms: np.ndarray, s: int, seed: int,
+                   threads: int | None = None):
+    """The ablation's mean at every column given the norms, in column blocks."""
+    x = _rows(x)
+    n, d = x.shape
+    norms = np.ascontiguousarray(norms, dtype=np.float32)
+    mean = np.zeros(d, dtype=np.float32)
+    dt = _x_dtype(x)
+
+    def one(a, b):
+        cols = np.arange(a, b, dtype=np.int64)
+        lib().oracle_qsgd_local_cols(_ptr(x), dt, n, d, s, seed, _ptr(norms), _ptr(cols), b - a,
+                                     None, _ptr(mean[a:b]))
+
+    run_blocks(one, col_blocks(d, threads), threads)
+    return mean
+
+
+def pack_row(values: np.ndarray, W: int, threads: int | None = None) -> np.ndarray:
+    """pack of one row of d values, in 128-column blocks (each block's W-bit
+    fields fill whole 16-byte units, so the blocks' bytes concatenate)."""
+    values = np.ascontiguousarray(values, dtype=np.int32).reshape(-1)
+    d = values.size
+    out = np.zeros(row_bytes(d, W), dtype=np.uint8)
+
+    def one(a, b):
+        part = pack(values[a:b], W)[0]
+        out[a * W // 8: a * W // 8 + part.size] = part
+
+    run_blocks(one, col_blocks(d, threads), threads)
+    return out
+
+
+def sum_words_all(rows: np.ndarray, threads: int | None = None) -> np.ndarray:
+    """sum_words over blocks of words, in host threads."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint32)
+    n, nw = rows.shape
+    out = np.zeros(nw, dtype=np.uint32)
+
+    def one(a, b):
+        out[a:b] = sum_words(np.ascontiguousarray(rows[:, a:b]))
+
+    run_blocks(one, col_blocks(nw, threads, align=1), threads)
+    return out
+
+
 def qsgd_local_mean(x: np.ndarray, s: int, seed: int):
     """Local-norm QSGD ablation. Returns (norms float32 [n], codes int32 [n, d], mean [d])."""
     x = _rows(x)

@@ -9,7 +9,6 @@ seeded generators of workloads.py and only the oracle computes expected
 values.
 """
 import math
-import os
 import sys
 import time
 
@@ -304,75 +303,6 @@ def test_local_qsgd_matches_oracle(n, d, dtype):
         check_norm(gn[i], norms[i])
     assert np.array_equal(host(gcodes), oracle.pack(codes, W))
     assert np.array_equal(host(gmean), mean)
-
-
-# ---------------------------------------------------------------------------
-# Full-size workloads, in the launch configuration the benchmark times:
-# the norm over every input, the code sums and means at sampled coordinates
-# (all tile boundaries near both ends plus random ones), and at every
-# coordinate the properties |sum| <= n M and mean == fp32(sum kappa).
-
-def _sample_cols(d, rng, k=20000):
-    edge = np.concatenate([np.arange(0, min(d, 4100)), np.arange(max(0, d - 4100), d)])
-    return np.unique(np.concatenate([edge, rng.integers(0, d, size=k)]))
-
-
-def _fields(buf: np.ndarray, d: int, W: int) -> np.ndarray:
-    if W in (8, 16, 32):
-        return buf.view({8: np.int8, 16: np.int16, 32: np.int32}[W])[:d].astype(np.int64)
-    return oracle.unpack(buf, 1, d, W)[0].astype(np.int64)
-
-
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("key", [1, 2, 3, 4, 5])
-def test_workload_full_size(key):
-    w = wl.WORKLOADS[key]
-    threads = min(16, os.cpu_count() or 1)
-    log(f"workload {key} {w.name}: generating {w.input_bytes / 1e9:.2f} GB")
-    x = wl.generate(w, threads=threads)
-    log("oracle norm")
-    N, _ = oracle.global_norm_rows(x, w.q, w.p, threads=threads)
-    log("device copy")
-    xd = to_dev(x)
-    W = w.code_bits
-    mean_b, norm_b, _ = gq.gq_compress_mean(xd, w.s, w.q, w.p, w.scheme, w.seed)  # benchmarked call
-    mean, norm, csum = gq.gq_compress_mean(xd, w.s, w.q, w.p, w.scheme, w.seed, code_bits=W,
-                                           want_code_sum=True)
-    check_norm(host(norm)[0], N)
-    gmean = host(mean)
-    assert np.array_equal(gmean, host(mean_b))
-    sums = _fields(host(csum), w.d, W)
-    log("sampled oracle columns")
-    rng = np.random.default_rng(key)
-    cols = _sample_cols(w.d, rng)
-    osums, omean = oracle.compress_mean_cols(x, N, w.s, SCH[w.scheme], w.seed, cols)
-    assert np.array_equal(sums[cols], osums)
-    assert np.array_equal(gmean[cols], omean)
-    # properties at every coordinate
-    M = M_of(w.s, w.scheme)
-    assert np.abs(sums).max() <= w.n * M
-    kappa = float(N) / (w.n * M)
-    assert np.array_equal(gmean, (sums.astype(np.float64) * kappa).astype(np.float32))
-    if key == 2:
-        # the unfused four-call path at full size agrees with the fused one
-        codes = gq.gq_quantize(xd, w.s, w.scheme, norm, w.seed, W)
-        csum2 = gq.gq_reduce_codes(codes, w.n, w.d, W)
-        mean2 = gq.gq_dequantize(csum2, w.n, w.d, w.s, w.scheme, W, norm)
-        assert np.array_equal(host(csum2), host(csum))
-        assert np.array_equal(host(mean2), gmean)
-        del codes
-    if key == 5:
-        # the local-norm ablation at full size: norms of every row, sampled columns
-        log("local-norm ablation")
-        lmean, lnorms, _ = gq.gq_qsgd_local_mean(xd, w.s, w.seed)
-        onorms = oracle.local_norms(x, threads=threads)
-        assert np.array_equal(host(lnorms), onorms)
-        _, exp = oracle.qsgd_local_cols(x, onorms, w.s, w.seed, cols)
-        assert np.array_equal(host(lmean)[cols], exp)
-    del xd, x
-    torch.cuda.empty_cache()
-    log(f"workload {key} ok")
-
 
 
 # ---------------------------------------------------------------------------

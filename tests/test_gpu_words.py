@@ -3,14 +3,11 @@
 floor(32 / W) fields of code + M per 32-bit word, so that a plain uint32
 SUM over the rows adds every code exactly.  Bar: words, summed words and
 code sums bit-exact against the oracle; the mean bit-exact against the
-oracle's dequantization of the same sums (and against the fused path at
-full size).  Inputs come from the seeded generators of workloads.py; only
+oracle's dequantization of the same sums.  Full-size workloads are checked
+at every coordinate in test_gpu_full_size.py.  Inputs come from the seeded generators of workloads.py; only
 the oracle computes expected values.
 """
 import math
-import os
-import sys
-import time
 
 import numpy as np
 import pytest
@@ -25,10 +22,6 @@ pytestmark = pytest.mark.gpu
 INF = math.inf
 SCH = {"L": oracle.SCHEME_L, "E": oracle.SCHEME_E}
 DEV = "cuda:0"
-
-
-def log(msg):
-    print(f"[gpu-words {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -236,45 +229,3 @@ def test_shards_summed_together_reproduce_the_whole():
     mean = gq.gq_dequantize_words(gsum, n, d, s, scheme, W, norm)
     fmean, _, _ = gq.gq_compress_mean(xd, s, 2.0, INF, scheme, 5)
     assert np.array_equal(host(mean), host(fmean))
-
-
-def _sample_cols(d, rng, k=20000):
-    edge = np.concatenate([np.arange(0, min(d, 4100)), np.arange(max(0, d - 4100), d)])
-    return np.unique(np.concatenate([edge, rng.integers(0, d, size=k)]))
-
-
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("key", [2, 3, 4, 5])
-def test_workload_full_size(key):
-    """Full-size workloads at the minimal width (11 and 13 bits, 2 fields per
-    word; 8 bits from bf16 input, 4 per word; 9 bits, 3 per word): the word
-    path's sums and mean equal the fused path's at every coordinate, and
-    sampled columns equal the oracle's at the device's norm."""
-    w = wl.WORKLOADS[key]
-    threads = min(16, os.cpu_count() or 1)
-    log(f"workload {key} {w.name}: generating {w.input_bytes / 1e9:.2f} GB")
-    x = wl.generate(w, threads=threads)
-    xd = to_dev(x)
-    W = gq.gq_min_code_bits(w.n, w.s, w.scheme)
-    M = M_of(w.s, w.scheme)
-    fmean, norm, fsum = gq.gq_compress_mean(xd, w.s, w.q, w.p, w.scheme, w.seed, code_bits=32,
-                                            want_code_sum=True)
-    words = gq.gq_quantize_words(xd, w.s, w.scheme, norm, w.seed, W)
-    wsum = gq.gq_sum_words(words, w.n, w.d, W)
-    mean = gq.gq_dequantize_words(wsum, w.n, w.d, w.s, w.scheme, W, norm)
-    csum = gq.gq_compress_words_from_norm(xd, w.s, w.scheme, norm, w.seed, W)
-    assert torch.equal(csum, wsum)
-    log("unpacking")
-    sums = oracle.unpack_word_sums(words_host(wsum), w.n, w.d, W, M)
-    assert np.array_equal(sums, host(fsum).view(np.int32)[: w.d].astype(np.int64))
-    gmean = host(mean)
-    assert np.array_equal(gmean, host(fmean))
-    log("sampled oracle columns")
-    cols = _sample_cols(w.d, np.random.default_rng(key))
-    N = np.float32(host(norm)[0])
-    osums, omean = oracle.compress_mean_cols(x, N, w.s, SCH[w.scheme], w.seed, cols)
-    assert np.array_equal(sums[cols], osums)
-    assert np.array_equal(gmean[cols], omean)
-    del xd, x, words
-    torch.cuda.empty_cache()
-    log(f"workload {key} ok")
