@@ -34,6 +34,7 @@ SIGNATURES = {
     "gq_min_code_bits": (_i32, [_i64, _i32, _i32]),
     "gq_code_row_bytes": (_i64, [_i64, _i32]),
     "gq_workspace_bytes": (_i64, [_i64, _i64]),
+    "gq_compress_workspace_bytes": (_i64, [_i64, _i64]),
     "gq_global_norm": (_i32, [_vp, _i32, _i64, _i64, _f32, _f32, _vp, _vp, _i64, _vp]),
     "gq_norm_term": (_i32, [_vp, _i32, _i64, _i64, _f32, _f32, _vp, _vp, _i64, _vp]),
     "gq_norm_from_term": (_i32, [_vp, _f32, _f32, _vp, _vp]),
@@ -51,6 +52,8 @@ SIGNATURES = {
                                           _vp, _vp, _vp]),
     "gq_compress_mean": (_i32, [_vp, _i32, _i64, _i64, _i32, _f32, _f32, _i32, _u64, _i32, _vp,
                                 _vp, _vp, _vp, _i64, _vp]),
+    "gq_compress_sums8": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _u64, _vp, _vp, _vp]),
+    "gq_dequantize_sums8": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _u64, _vp, _vp, _vp, _vp]),
     "gq_compress_mean_noalloc": (_i32, [_vp, _i32, _i64, _i64, _i32, _f32, _f32, _i32, _u64,
                                         _i32, _vp, _vp, _vp, _vp]),
     "gq_qsgd_local_mean": (_i32, [_vp, _i32, _i64, _i64, _i32, _u64, _vp, _vp, _vp, _i32, _vp,
@@ -146,6 +149,11 @@ def gq_workspace_bytes(n: int, d: int) -> int:
     return int(lib().gq_workspace_bytes(n, d))
 
 
+def gq_compress_workspace_bytes(n: int, d: int) -> int:
+    """Workspace with which gq_compress_mean runs fastest (>= gq_workspace_bytes)."""
+    return int(lib().gq_compress_workspace_bytes(n, d))
+
+
 def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
@@ -175,10 +183,13 @@ def _norm_in(norm, device):
     return _buf(norm, 4, "norm", device, torch.float32)
 
 
-def _workspace(ws, n, d, device):
+def _workspace(ws, n, d, device, alloc=None):
+    """The caller's workspace (at least gq_workspace_bytes), or a new one of
+    `alloc` bytes (default: gq_workspace_bytes)."""
     need = gq_workspace_bytes(n, d)
     if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(need if alloc is None else alloc, 16), dtype=torch.uint8,
+                         device=device)
     return _buf(ws, need, "workspace", device)
 
 
@@ -361,11 +372,40 @@ def gq_compress_mean(x: torch.Tensor, s: int, q, p, scheme, seed: int, *, code_b
     _buf(mean, 4 * d, "mean", x.device, torch.float32)
     _buf(norm, 4, "norm", x.device, torch.float32)
     _buf(code_sum, max(gq_code_row_bytes(d, code_bits), 0), "code_sum", x.device)
-    ws = _workspace(workspace, n, d, x.device)
+    ws = _workspace(workspace, n, d, x.device, alloc=gq_compress_workspace_bytes(n, d))
     _check(lib().gq_compress_mean(_ptr(x), dt, n, d, s, _order(q), _order(p), _scheme(scheme), seed,
                                   code_bits, _ptr(mean), _ptr(norm), _ptr(code_sum), _ptr(ws),
                                   _nbytes(ws), _stream(stream)))
     return mean, norm, code_sum
+
+
+def gq_compress_sums8(x: torch.Tensor, s: int, scheme, seed: int, norm: torch.Tensor, *,
+                      sums8=None, stream=None):
+    """Exact code sums as bytes (-128: beyond one byte), int8 [d]."""
+    dt = _input(x)
+    n, d = x.shape
+    _norm_in(norm, x.device)
+    if sums8 is None:
+        sums8 = torch.empty(max(d, 1), dtype=torch.int8, device=x.device)
+    _buf(sums8, d, "sums8", x.device)
+    _check(lib().gq_compress_sums8(_ptr(x), dt, n, d, s, _scheme(scheme), seed, _ptr(norm),
+                                   _ptr(sums8), _stream(stream)))
+    return sums8
+
+
+def gq_dequantize_sums8(x: torch.Tensor, s: int, scheme, seed: int, norm: torch.Tensor,
+                        sums8: torch.Tensor, *, mean=None, stream=None):
+    """The mean from gq_compress_sums8's bytes (escaped groups recomputed from x)."""
+    dt = _input(x)
+    n, d = x.shape
+    _norm_in(norm, x.device)
+    _buf(sums8, d, "sums8", x.device)
+    if mean is None:
+        mean = torch.empty(d, dtype=torch.float32, device=x.device)
+    _buf(mean, 4 * d, "mean", x.device, torch.float32)
+    _check(lib().gq_dequantize_sums8(_ptr(x), dt, n, d, s, _scheme(scheme), seed, _ptr(norm),
+                                     _ptr(sums8), _ptr(mean), _stream(stream)))
+    return mean
 
 
 # bytes of the device array behind gq_compress_mean_noalloc (GQ_NOALLOC_SCRATCH_BYTES)

@@ -8,6 +8,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", "gq.hip")]
 LIB_PATH = os.path.join(PKG, "libgq.so")
+# measurement kernels (read and VALU-issue ceilings), a library of their own
+PROBE_SOURCES = [os.path.join(PKG, "csrc", "probe.hip")]
+PROBE_LIB_PATH = os.path.join(PKG, "libgq_probe.so")
 
 # -ffp-contract=off: every float operation rounds once, as the contract states.
 # -fno-gpu-flush-denormals-to-zero: subnormal inputs are quantized, not flushed.
@@ -31,9 +34,10 @@ def hipcc() -> str:
 BUILD_TIMEOUT_S = 900
 
 
-def build_library(verbose: bool = False) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
+def build_library(verbose: bool = False, sources=None, lib_path: str = LIB_PATH) -> str:
+    sources = SOURCES if sources is None else sources
+    tmp = lib_path + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *sources, "-o", tmp]
     try:
         r = subprocess.run(cmd, capture_output=True, text=True, timeout=BUILD_TIMEOUT_S)
     except subprocess.TimeoutExpired as e:
@@ -42,9 +46,14 @@ def build_library(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
     if verbose and r.stderr:
         print(r.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
+
+
+def build_probe(verbose: bool = False) -> str:
+    return build_library(verbose, PROBE_SOURCES, PROBE_LIB_PATH)
 
 
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_probe(verbose=True))

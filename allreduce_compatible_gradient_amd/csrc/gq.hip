@@ -72,6 +72,7 @@ constexpr int kPer = 8;                     // coordinates per thread: one Philo
 constexpr int kTile = kThreads * kPer;      // 2048 coordinates per block
 constexpr int64_t kNormTargetBlocks = 8192; // pass-1 blocks: ~32 per CU on 256 CUs
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+constexpr int64_t kSums8MinN = 32;          // workers from which fp32 compress stages 1-byte sums
 
 thread_local char g_err[512];
 
@@ -188,6 +189,8 @@ OneShotGeom oneshot_geom(int64_t n, int64_t d, int64_t elem_bytes)
 
 struct WsLayout {
     int64_t partials, mid, per_worker, params, total;
+    // gq_compress_mean's optional staging of 1-byte code sums (n >= kSums8MinN)
+    int64_t sums8, total_compress;
 };
 
 // The layout covers the pass-1 geometry of either input type.
@@ -207,6 +210,8 @@ WsLayout ws_layout(int64_t n, int64_t d)
     w.per_worker = w.mid + align256(mid);
     w.params = w.per_worker + align256(8 * n);
     w.total = w.params + align256(16 * n);
+    w.sums8 = w.total;
+    w.total_compress = (n >= kSums8MinN && d > 0) ? w.total + align256(d) : w.total;
     return w;
 }
 
@@ -1235,6 +1240,113 @@ __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restri
     }
     if (code_sum)
         store_tile_packed(lds, acc, W, code_sum, tile, row_bytes(d, W));
+}
+
+// Many workers (n >= kSums8MinN, fp32): the compress step in two kernels.
+// While the pass streams n rows per tile, every byte it writes costs far
+// more than its share of bandwidth: on a 64 x 64M fp32 input the pass takes
+// 2.66 ms without writes, 2.95 ms with the 256 MB mean interleaved, 2.75 ms
+// with 64 MB of 1-byte sums (about 1.2 us per MB written).  So the pass
+// writes each coordinate's exact code sum as one byte when it lies in
+// [-127, 127], else the escape byte -128, and a second streaming kernel
+// turns the bytes into the mean, recomputing an escaped group's sums from x
+// (the same accumulation, so the same integers).  Sums that large need many
+// workers on the top levels and are rare in gradients; an input where every
+// group escapes is still exact, at the cost of a second full pass.
+constexpr int kSums8Escape = -128;
+
+template <int DT, int SCH, int ACC>
+__global__ __launch_bounds__(kThreads) void k_compress_sums8(const void *__restrict__ x, int64_t n,
+                                                             int64_t d, int s, uint64_t seed,
+                                                             const float *__restrict__ norm_dev,
+                                                             int8_t *__restrict__ sums8)
+{
+    // the residency cap of the fused pass (32 KB of LDS: 5 blocks per CU)
+    __shared__ alignas(16) uint32_t lds[8192];
+    if (n < 0)
+        lds[threadIdx.x] = 0;
+    const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;
+    const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
+    if (j0 >= d)
+        return;
+    const QParams q = make_qparams(*norm_dev, n, s, SCH);
+    float accf[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int acc[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (!q.zero) {
+        const bool vec = (d & 7) == 0;
+        const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+        if (q.prescale)
+            accumulate_workers<DT, SCH, true, ACC == kAccF32>(x, n, d, j0, vec, q, k0, k1, accf, acc);
+        else
+            accumulate_workers<DT, SCH, false, ACC == kAccF32>(x, n, d, j0, vec, q, k0, k1, accf, acc);
+        if (ACC == kAccF32) {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+                acc[k] = (int)accf[k];
+        }
+    }
+    uint32_t b[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        b[k] = (uint32_t)((acc[k] >= -127 && acc[k] <= 127) ? acc[k] : kSums8Escape) & 0xFFu;
+    if (j0 + kPer <= d && (d & 7) == 0) {
+        const uint2 o = make_uint2(b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24,
+                                   b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24);
+        nt_store((uint8_t *)sums8 + j0, o);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            if (j0 + k < d)
+                sums8[j0 + k] = (int8_t)b[k];
+    }
+}
+
+template <int DT, int SCH, int ACC>
+__global__ __launch_bounds__(kThreads) void k_dequantize_sums8(const void *__restrict__ x, int64_t n,
+                                                               int64_t d, int s, uint64_t seed,
+                                                               const float *__restrict__ norm_dev,
+                                                               const int8_t *__restrict__ sums8,
+                                                               float *__restrict__ mean)
+{
+    const int64_t j0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
+    if (j0 >= d)
+        return;
+    const QParams q = make_qparams(*norm_dev, n, s, SCH);
+    int acc[kPer];
+    bool esc = false;
+    if (j0 + kPer <= d && (d & 7) == 0) {
+        const uint2 w = *(const uint2 *)(sums8 + j0);
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            acc[k] = (int)(int8_t)(((k < 4 ? w.x : w.y) >> (8 * (k & 3))) & 0xFFu);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            acc[k] = j0 + k < d ? (int)sums8[j0 + k] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        esc |= acc[k] == kSums8Escape;
+    if (esc) {
+        // a sum outside [-127, 127] in this group: recompute the group's
+        // exact sums over the n workers, as the pass formed them
+        float accf[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+        int acci[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+        const bool vec = (d & 7) == 0;
+        const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+        if (q.prescale)
+            accumulate_workers<DT, SCH, true, ACC == kAccF32>(x, n, d, j0, vec, q, k0, k1, accf, acci);
+        else
+            accumulate_workers<DT, SCH, false, ACC == kAccF32>(x, n, d, j0, vec, q, k0, k1, accf, acci);
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            acc[k] = ACC == kAccF32 ? (int)accf[k] : acci[k];
+    }
+    float m[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        m[k] = (float)((double)acc[k] * q.kappa);
+    store_mean8<false>(mean, j0, d, m);
 }
 
 // Codes of one 8-coordinate group of worker wk (v already loaded).
@@ -2363,9 +2475,50 @@ int32_t launch_norm(const void *x, int32_t dtype, int64_t n, int64_t d, float q,
     return check_launch("k_norm_finalize");
 }
 
+// The staged compress step: mean == nullptr launches the pass that writes
+// the 1-byte sums, otherwise the kernel that turns them into the mean.
+int32_t launch_sums8(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                     int32_t scheme, uint64_t seed, const float *norm_dev, int8_t *sums8,
+                     float *mean, hipStream_t st)
+{
+    const int64_t tiles = (d + kTile - 1) / kTile;
+    if (tiles == 0)
+        return ok();
+    const dim3 grid((unsigned)tiles), block(kThreads);
+    const bool facc = n * top_code(s, scheme) <= ((int64_t)1 << 24);
+#define GQ_S8(DT, SCH, ACC)                                                                        \
+    do {                                                                                           \
+        if (!mean)                                                                                 \
+            k_compress_sums8<DT, SCH, ACC><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev,     \
+                                                                   sums8);                         \
+        else                                                                                       \
+            k_dequantize_sums8<DT, SCH, ACC><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev,   \
+                                                                     sums8, mean);                 \
+    } while (0)
+#define GQ_S8_DT(DT)                                     \
+    do {                                                 \
+        if (scheme == GQ_SCHEME_L) {                     \
+            if (facc)                                    \
+                GQ_S8(DT, GQ_SCHEME_L, kAccF32);         \
+            else                                         \
+                GQ_S8(DT, GQ_SCHEME_L, kAccInt);         \
+        } else if (facc)                                 \
+            GQ_S8(DT, GQ_SCHEME_E, kAccF32);             \
+        else                                             \
+            GQ_S8(DT, GQ_SCHEME_E, kAccInt);             \
+    } while (0)
+    if (dtype == GQ_IN_F32)
+        GQ_S8_DT(GQ_IN_F32);
+    else
+        GQ_S8_DT(GQ_IN_BF16);
+#undef GQ_S8_DT
+#undef GQ_S8
+    return check_launch(mean ? "k_dequantize_sums8" : "k_compress_sums8");
+}
+
 int32_t launch_compress(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
                         int32_t scheme, uint64_t seed, const float *norm_dev, int32_t W,
-                        float *mean, void *code_sum, hipStream_t st)
+                        float *mean, void *code_sum, hipStream_t st, int8_t *sums8 = nullptr)
 {
     const int64_t tiles = (d + kTile - 1) / kTile;
     if (tiles == 0)
@@ -2376,6 +2529,11 @@ int32_t launch_compress(const void *x, int32_t dtype, int64_t n, int64_t d, int3
     // packed int16 sums for bf16 standard dithering while n s < 2^15
     const int64_t nm = n * top_code(s, scheme);
     const bool facc = nm <= ((int64_t)1 << 24);
+    if (sums8 && !code_sum && dtype == GQ_IN_F32 && n >= kSums8MinN) {
+        // many workers: 1-byte sums from the pass, the mean from a second kernel
+        GQ_TRY(launch_sums8(x, dtype, n, d, s, scheme, seed, norm_dev, sums8, nullptr, st));
+        return launch_sums8(x, dtype, n, d, s, scheme, seed, norm_dev, sums8, mean, st);
+    }
     const bool pk16 = dtype == GQ_IN_BF16 && scheme == GQ_SCHEME_L && nm < ((int64_t)1 << 15);
 #define GQ_COMPRESS(DT, SCH, ACC) \
     k_compress_mean<DT, SCH, ACC><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, mean, cs, W)
@@ -2455,6 +2613,13 @@ int64_t gq_workspace_bytes(int64_t n, int64_t d)
     if (n < 1 || n > 0x7FFFFFFF || d < 0 || (d > 0 && n > INT64_MAX / 8 / d))
         return -1;
     return ws_layout(n, d).total;
+}
+
+int64_t gq_compress_workspace_bytes(int64_t n, int64_t d)
+{
+    if (n < 1 || n > 0x7FFFFFFF || d < 0 || (d > 0 && n > INT64_MAX / 8 / d))
+        return -1;
+    return ws_layout(n, d).total_compress;
 }
 
 const char *gq_status_str(int32_t status)
@@ -2868,8 +3033,44 @@ int32_t gq_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int
     GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
     hipStream_t st = (hipStream_t)stream;
     GQ_TRY(launch_norm(x, dtype, n, d, q, p, false, norm_dev, workspace, 0, st));
+    const WsLayout L = ws_layout(n, d);
+    int8_t *sums8 = (L.total_compress > L.total && workspace_bytes >= L.total_compress)
+                        ? (int8_t *)((char *)workspace + L.sums8)
+                        : nullptr;
     return launch_compress(x, dtype, n, d, s, scheme, seed, norm_dev, code_bits, mean,
-                           code_sum_or_null, st);
+                           code_sum_or_null, st, sums8);
+}
+
+int32_t gq_compress_sums8(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                          int32_t scheme, uint64_t seed, const float *norm_dev, void *sums8,
+                          void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    GQ_TRY(validate_scheme(s, scheme));
+    if (!norm_dev || (!sums8 && d > 0))
+        return fail(GQ_ERR_NULL, "norm_dev or sums8 is NULL");
+    if (min_bits(n, s, scheme) > 32)
+        return fail(GQ_ERR_CODE_WIDTH, "sums of %lld codes do not fit 32 bits", (long long)n);
+    if (!aligned16(sums8))
+        return fail(GQ_ERR_ALIGN, "sums8 is not 16-byte aligned");
+    return launch_sums8(x, dtype, n, d, s, scheme, seed, norm_dev, (int8_t *)sums8, nullptr,
+                        (hipStream_t)stream);
+}
+
+int32_t gq_dequantize_sums8(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                            int32_t scheme, uint64_t seed, const float *norm_dev,
+                            const void *sums8, float *mean, void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    GQ_TRY(validate_scheme(s, scheme));
+    if (!norm_dev || ((!sums8 || !mean) && d > 0))
+        return fail(GQ_ERR_NULL, "norm_dev, sums8 or mean is NULL");
+    if (min_bits(n, s, scheme) > 32)
+        return fail(GQ_ERR_CODE_WIDTH, "sums of %lld codes do not fit 32 bits", (long long)n);
+    if (!aligned16(sums8) || !aligned16(mean))
+        return fail(GQ_ERR_ALIGN, "sums8 or mean is not 16-byte aligned");
+    return launch_sums8(x, dtype, n, d, s, scheme, seed, norm_dev, (int8_t *)sums8, mean,
+                        (hipStream_t)stream);
 }
 
 int32_t gq_compress_mean_noalloc(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,

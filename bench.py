@@ -3,13 +3,21 @@
 One step = one gq_compress_mean call over one batch of n simulated workers'
 gradient shards already resident in HBM: the global (q,p)-norm pass, then
 the fused quantize / exact integer sum / dequantize pass.  The default
-workload is the ResNet-50-sized bucket: standard dithering, s = 127,
-q = 2, p = inf, n = 8 workers x d = 25,557,032 fp32 coordinates.
+workload is the largest fp32 one that fits one GPU: n = 64 workers x
+d = 64,000,000 fp32 coordinates (16.4 GB), standard dithering, s = 3,
+q = p = 2, with local-norm QSGD timed beside it.  The three other large
+workloads (ResNet-50-, BERT-base- and GPT-2-medium-sized buckets) are timed
+in the same run and reported under "configs".
 
 Prints one JSON line.  `value` is input GB/s (n d bytes-per-element / step
-time); `roofline` describes the dominant kernel (k_compress_mean) timed per
-launch with HIP events on the stream it runs on; `cpu_baseline` is the CPU
-oracle timed on a bounded prefix of the same workload.
+time); `roofline` describes the dominant kernel (k_compress_mean, or for
+many fp32 workers k_compress_sums8, the pass that stages 1-byte sums) timed
+per launch with HIP events on the stream it runs on; `read_ceiling` is the best
+plain stream read of the same input (libgq_probe.so), `valu_ceiling` the
+measured issue rate of the instruction kinds the VALU-heavy kernels use;
+`e8_omega` the byte rate of the pages' 8-bit custom reduction against an
+fp32 sum; `cpu_baseline` is the CPU oracle on every host core (and on one)
+over a bounded prefix of the same workload.
 """
 from __future__ import annotations
 
@@ -33,9 +41,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, help="workload key in workloads.WORKLOADS")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--workload", type=int, default=5, help="workload key in workloads.WORKLOADS")
+    ap.add_argument("--configs", default="2,3,4",
+                    help="other workload keys timed in the same run ('' for none)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the multi-threaded oracle baseline (0 disables it)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the read ceiling, VALU rates, 8-bit omega and DDP hook figures "
+                         "(counter passes of one workload)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
     ap.add_argument("--unfused", action="store_true", help="also time the four-call unfused path")
@@ -80,25 +93,49 @@ def event_pairs(torch, k):
 
 
 def cpu_baseline(w, target_s: float):
-    """The oracle as it is (one thread, scalar C) on the first d' coordinates of every worker."""
+    """The oracle as it is (scalar C, never tuned for this) on the first d'
+    coordinates of every worker: the whole operation (norm, codes, exact
+    sum, dequantization).  On every host core the rows' norms and then
+    blocks of columns run in a pool of threads, each block one oracle call;
+    the one-core figure is one oracle call over a smaller prefix."""
     import oracle
     import workloads as wl
     scheme = oracle.SCHEME_L if w.scheme == "L" else oracle.SCHEME_E
-    d0 = min(w.d, 1 << 16)
+    threads = oracle._threads(None)
+    d0 = min(w.d, 1 << 15)
     x = wl.generate(w, d=d0)
     t0 = time.perf_counter()
     oracle.compress_mean(x, w.s, w.q, w.p, scheme, w.seed)
-    per_elem = (time.perf_counter() - t0) / (w.n * d0)
-    d1 = int(min(w.d, max(d0, target_s / per_elem / w.n)))
-    x = wl.generate(w, d=d1)
+    per_elem = (time.perf_counter() - t0) / (w.n * d0)   # one core, seconds per element
+
+    def whole(xs, nthreads):
+        t0 = time.perf_counter()
+        N, _ = oracle.global_norm_rows(xs, w.q, w.p, threads=nthreads)
+        oracle.compress_mean_all(xs, N, w.s, scheme, w.seed, threads=nthreads)
+        return time.perf_counter() - t0
+
+    # all host threads: about target_s of wall time
+    d1 = int(min(w.d, max(d0, target_s * threads / per_elem / w.n)))
+    x = wl.generate(w, d=d1, threads=threads)
+    dt = whole(x, threads)
+    del x
+    # one thread: a third of that time
+    d2 = int(min(w.d, max(d0, target_s / 3.0 / per_elem / w.n)))
+    x = wl.generate(w, d=d2, threads=threads)
     t0 = time.perf_counter()
     oracle.compress_mean(x, w.s, w.q, w.p, scheme, w.seed)
-    dt = time.perf_counter() - t0
+    dt1 = time.perf_counter() - t0
+    del x
     gbs = w.n * d1 * w.elem_bytes / dt / 1e9
-    return {"value": round(gbs, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    gbs1 = w.n * d2 * w.elem_bytes / dt1 / 1e9
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"first {d1} of {w.d} coordinates of all {w.n} workers "
-                      f"({w.n * d1} elements, {dt:.1f} s)",
-            "cpu_model": _cpu_model()}
+                      f"({w.n * d1} elements, {dt:.1f} s on {threads} threads: row norms, then "
+                      f"column blocks, each block one oracle call)",
+            "cpu_model": _cpu_model(),
+            "one_core": {"value": round(gbs1, 6), "unit": "GB/s", "cores": 1,
+                         "sample": f"first {d2} coordinates of all {w.n} workers "
+                                   f"({w.n * d2} elements, {dt1:.1f} s, one oracle call)"}}
 
 
 def _cpu_model() -> str:
@@ -151,19 +188,21 @@ def _time_us(torch, stream, fn, reps):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
-def e8_report(gq, torch, w, xd, stream, steps, ws):
-    """The 8-bit exponential format: omega of its custom pair reduction, and
-    the fused norm + codes + re-rounding tree + dequantization path."""
+def e8_omega(gq, torch, stream, dev):
+    """omega of the pages' 8-bit custom reduction ("Global-QSGD: Practical
+    Floatless Quantization ...", Sec. 5: the byte rate of the custom pair
+    reduction over that of an fp32 sum), with omega_S of a plain uint8 sum,
+    at the pages' 25 MB bucket and at 1 GB."""
     out = {}
     g = torch.Generator(device="cpu").manual_seed(0)
     for label, nbytes in (("25MB", 25 << 20), ("1GB", 1 << 30)):
         d = nbytes // 4  # elements of an fp32 buffer of that size
-        a = torch.randn(d, generator=g).to(xd.device)
-        b = torch.randn(d, generator=g).to(xd.device)
+        a = torch.randn(d, generator=g).to(dev)
+        b = torch.randn(d, generator=g).to(dev)
         c = torch.empty_like(a)
         t_f32 = _time_us(torch, stream, lambda st: torch.add(a, b, out=c), 50)
-        au = torch.randint(0, 256, (d,), dtype=torch.uint8, generator=g).to(xd.device)
-        bu = torch.randint(0, 256, (d,), dtype=torch.uint8, generator=g).to(xd.device)
+        au = torch.randint(0, 256, (d,), dtype=torch.uint8, generator=g).to(dev)
+        bu = torch.randint(0, 256, (d,), dtype=torch.uint8, generator=g).to(dev)
         cu = torch.empty_like(au)
         t_u8 = _time_us(torch, stream, lambda st: torch.add(au, bu, out=cu), 50)
         t_e8 = _time_us(torch, stream, lambda st: gq.gq_e8_reduce_pair(au, bu, d, 1, 1, 0, out=cu,
@@ -175,6 +214,15 @@ def e8_report(gq, torch, w, xd, stream, steps, ws):
                       "e8_pair_reduce_us": round(t_e8, 3), "omega_E": round(om_e, 4),
                       "omega_S": round(om_s, 4),
                       "eq8_beta_over_gamma_E": eq8_threshold(4.0, om_e)}
+        del au, bu, cu
+    torch.cuda.empty_cache()
+    return out
+
+
+def e8_report(gq, torch, w, xd, stream, steps, ws):
+    """The 8-bit exponential format: omega of its custom pair reduction, and
+    the fused norm + codes + re-rounding tree + dequantization path."""
+    out = e8_omega(gq, torch, stream, xd.device)
     n, d = w.n, w.d
     if n & (n - 1) == 0:
         mean = torch.empty(d, dtype=torch.float32, device=xd.device)
@@ -331,6 +379,193 @@ def ablation(gq, torch, w, xd, stream, steps, global_ms, gmean, gnorm, ws):
     }
 
 
+def load_workload(np, torch, wl, w, dev):
+    """Generate workload w on the host (seeded, threads) and copy it to the device."""
+    t0 = time.perf_counter()
+    x = wl.generate(w, threads=min(16, os.cpu_count() or 1))
+    xd = torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).to(dev)
+    if w.dtype == "bf16":
+        xd = xd.view(torch.bfloat16)
+    del x
+    return xd, time.perf_counter() - t0
+
+
+def workload_config(w, wmin):
+    return {"workload": w.name, "scheme": f"Global-{w.scheme}_s", "s": w.s,
+            "q": w.q if w.q != float("inf") else "inf",
+            "p": w.p if w.p != float("inf") else "inf",
+            "n_workers": w.n, "d": w.d, "input_dtype": w.dtype, "code_bits": w.code_bits,
+            "min_code_bits": wmin, "values": w.values}
+
+
+def time_workload(gq, np, torch, w, xd, stream, steps, warmup, full):
+    """The whole step (norm pass + fused pass) over `steps` back-to-back calls,
+    then each pass alone with one HIP event pair per launch on the stream it
+    runs on.  full: also cold-cache and graph-replayed step times."""
+    n, d = w.n, w.d
+    dev = xd.device
+    mean = torch.empty(d, dtype=torch.float32, device=dev)
+    norm = torch.empty(1, dtype=torch.float32, device=dev)
+    # the workspace with which gq_compress_mean is fastest (for many fp32
+    # workers it stages 1-byte sums between two kernels)
+    ws = torch.empty(gq.gq_compress_workspace_bytes(n, d), dtype=torch.uint8, device=dev)
+    staged = w.dtype == "f32" and gq.gq_compress_workspace_bytes(n, d) > gq.gq_workspace_bytes(n, d)
+
+    def step():
+        gq.gq_compress_mean(xd, w.s, w.q, w.p, w.scheme, w.seed, mean=mean, norm=norm,
+                            workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    in_bytes = n * d * w.elem_bytes
+    out = {}
+    if full:
+        # the same step with the caches cold: reading 1 GiB before each step
+        # evicts L2 and the 256 MB Infinity Cache, so no step re-reads what
+        # the previous one left there.  The flush only reads, so it leaves no
+        # dirty lines to be written back inside the step.
+        flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+        fsum = torch.empty((), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        cpairs = event_pairs(torch, min(steps, 20))
+        for a, b in cpairs:
+            torch.sum(flush, 0, out=fsum)
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        cold_ms = float(np.median([a.elapsed_time(b) for a, b in cpairs]))
+        del flush
+        # graph replays: device time without host launch overhead (what bounds
+        # the small workload is the launches themselves)
+        graph_us = _time_us(torch, stream, lambda st: gq.gq_compress_mean(
+            xd, w.s, w.q, w.p, w.scheme, w.seed, mean=mean, norm=norm, workspace=ws, stream=st),
+            min(steps, 50))
+        out["graph_replay"] = {"ms_per_step": round(graph_us * 1e-3, 6),
+                               "input_GBs": round(in_bytes / (graph_us * 1e-6) / 1e9, 3)}
+        out["cold_cache"] = {"ms_per_step": round(cold_ms, 6),
+                             "input_GBs": round(in_bytes / (cold_ms * 1e-3) / 1e9, 3),
+                             "steps": len(cpairs), "stat": "median"}
+    # each kernel of the step alone, one event pair per launch on the same stream
+    npairs, kpairs, qpairs = (event_pairs(torch, steps) for _ in range(3))
+    sums8 = torch.empty(d, dtype=torch.int8, device=dev) if staged else None
+    for i in range(steps):
+        npairs[i][0].record(stream)
+        gq.gq_global_norm(xd, w.q, w.p, norm=norm, workspace=ws, stream=stream)
+        npairs[i][1].record(stream)
+        kpairs[i][0].record(stream)
+        if staged:
+            gq.gq_compress_sums8(xd, w.s, w.scheme, w.seed, norm, sums8=sums8, stream=stream)
+            kpairs[i][1].record(stream)
+            qpairs[i][0].record(stream)
+            gq.gq_dequantize_sums8(xd, w.s, w.scheme, w.seed, norm, sums8, mean=mean,
+                                   stream=stream)
+            qpairs[i][1].record(stream)
+        else:
+            gq.gq_compress_mean_from_norm(xd, w.s, w.scheme, w.seed, norm, mean=mean,
+                                          stream=stream)
+            kpairs[i][1].record(stream)
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in kpairs]))
+    n_ms = float(np.mean([a.elapsed_time(b) for a, b in npairs]))
+    q_ms = float(np.mean([a.elapsed_time(b) for a, b in qpairs])) if staged else 0.0
+    kernel = "k_compress_sums8" if staged else DOMINANT
+    # algorithmic bytes of the dominant kernel: one read of x, and the 1-byte
+    # sums (staged) or the fp32 mean written
+    k_alg = in_bytes + (d if staged else 4 * d)
+    fused_alg = 2 * in_bytes + 4 * d              # both passes of the whole step
+    achieved = k_alg / (k_ms * 1e-3) / 1e9
+    traffic = traffic_for(w.name)
+    out.update({
+        "ms_per_step": round(ms, 6),
+        "input_GBs": round(in_bytes / (ms * 1e-3) / 1e9, 3),
+        "hbm_frac_fused": round(fused_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernels_ms": ({"norm_pass": round(n_ms, 6), kernel: round(k_ms, 6),
+                        "k_dequantize_sums8": round(q_ms, 6)} if staged else
+                       {"norm_pass": round(n_ms, 6), kernel: round(k_ms, 6)}),
+        # the whole compress step after the norm (both kernels when staged):
+        # one read of x and the fp32 mean written
+        "compress_step": {"ms": round(k_ms + q_ms, 6),
+                          "frac": round((in_bytes + 4 * d) / ((k_ms + q_ms) * 1e-3) / 1e9
+                                        / HBM_PEAK_GBS, 4),
+                          "staged_sums8": staged},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": kernel, "alg_bytes_per_launch": k_alg,
+                     "traffic_over_alg": round(traffic / k_alg, 4) if traffic else None},
+        "_mean": mean, "_norm": norm, "_ws": ws,
+    })
+    return out
+
+
+class _Bucket:
+    """The part of DDP's GradBucket the hook reads: a flat gradient buffer and its index."""
+
+    def __init__(self, buf, index):
+        self._buf, self._index = buf, index
+
+    def buffer(self):
+        return self._buf
+
+    def index(self):
+        return self._index
+
+
+def ddp_hook_report(torch, w, stream, steps):
+    """The DDP communication hook (allreduce_compatible_gradient_amd.ddp) on one
+    rank over RCCL, per gradient bucket of 25 and 100 MB: the norm term, its
+    all-reduce, N, the codes in the word layout, the integer all-reduce and
+    the dequantization, with the workload's scheme and orders.  `us` is the
+    wall time per bucket of back-to-back hook calls (host work included, as
+    DDP would see it), `latency_us` that of one call waited for alone."""
+    import socket
+
+    import torch.distributed as dist
+
+    from allreduce_compatible_gradient_amd.ddp import GlobalQSGDState, global_qsgd_hook
+    with socket.socket() as sk:
+        sk.bind(("127.0.0.1", 0))
+        port = sk.getsockname()[1]
+    dist.init_process_group("nccl", init_method=f"tcp://127.0.0.1:{port}", rank=0, world_size=1)
+    out = {"scheme": f"Global-{w.scheme}_s", "s": w.s, "world": 1}
+    try:
+        state = GlobalQSGDState(scheme=w.scheme, s=w.s, q=w.q, p=w.p, seed=w.seed)
+        g = torch.Generator(device="cuda").manual_seed(0)
+        for label, nbytes in (("25MB", 25 << 20), ("100MB", 100 << 20)):
+            buf = torch.randn(nbytes // 4, device="cuda", generator=g) * 1e-3
+            b = _Bucket(buf, 0)
+            for _ in range(3):
+                global_qsgd_hook(state, b).wait()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                fut = global_qsgd_hook(state, b)
+            fut.wait()
+            torch.cuda.synchronize()
+            us = (time.perf_counter() - t0) / steps * 1e6
+            lat = []
+            for _ in range(min(steps, 20)):
+                t0 = time.perf_counter()
+                global_qsgd_hook(state, b).wait()
+                torch.cuda.synchronize()
+                lat.append(time.perf_counter() - t0)
+            out[label] = {"elements": buf.numel(), "us": round(us, 2),
+                          "bucket_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                          "latency_us": round(1e6 * sorted(lat)[len(lat) // 2], 1)}
+            del buf
+    finally:
+        dist.destroy_process_group()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -361,110 +596,50 @@ def main():
         return
 
     w = wl.WORKLOADS[args.workload]
-    t0 = time.perf_counter()
-    x = wl.generate(w, threads=min(16, os.cpu_count() or 1))
-    xd = torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).to(dev)
-    if w.dtype == "bf16":
-        xd = xd.view(torch.bfloat16)
-    del x
-    gen_s = time.perf_counter() - t0
+    xd, gen_s = load_workload(np, torch, wl, w, dev)
     n, d = w.n, w.d
-    mean = torch.empty(d, dtype=torch.float32, device=dev)
-    norm = torch.empty(1, dtype=torch.float32, device=dev)
-    ws = torch.empty(gq.gq_workspace_bytes(n, d), dtype=torch.uint8, device=dev)
-
-    def step():
-        gq.gq_compress_mean(xd, w.s, w.q, w.p, w.scheme, w.seed, mean=mean, norm=norm,
-                            workspace=ws, stream=stream)
-
-    # ---- the timed steps (value)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-
-    # ---- the same step with the caches cold: reading 1 GiB before each step
-    # evicts L2 and the 256 MB Infinity Cache, so no step re-reads what the
-    # previous one left there.  The flush only reads, so it leaves no dirty
-    # lines to be written back inside the step; only the step itself lies
-    # between its events.
-    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
-    fsum = torch.empty((), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-    cpairs = event_pairs(torch, min(args.steps, 20))
-    for a, b in cpairs:
-        torch.sum(flush, 0, out=fsum)
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    cold_ms = float(np.median([a.elapsed_time(b) for a, b in cpairs]))
-    del flush
-
-    # ---- the same step as graph replays: device time without host launch
-    # overhead (what bounds the small workload is the launches themselves)
-    graph_us = _time_us(torch, stream, lambda st: gq.gq_compress_mean(
-        xd, w.s, w.q, w.p, w.scheme, w.seed, mean=mean, norm=norm, workspace=ws, stream=st),
-        min(args.steps, 50))
-
-    # ---- the dominant kernel alone, one event pair per launch on the same stream
-    kpairs = event_pairs(torch, args.steps)
-    npairs = event_pairs(torch, args.steps)
-    for i in range(args.steps):
-        npairs[i][0].record(stream)
-        gq.gq_global_norm(xd, w.q, w.p, norm=norm, workspace=ws, stream=stream)
-        npairs[i][1].record(stream)
-        kpairs[i][0].record(stream)
-        gq.gq_compress_mean_from_norm(xd, w.s, w.scheme, w.seed, norm, mean=mean, stream=stream)
-        kpairs[i][1].record(stream)
-    torch.cuda.synchronize()
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in kpairs]))
-    n_ms = float(np.mean([a.elapsed_time(b) for a, b in npairs]))
-
+    t = time_workload(gq, np, torch, w, xd, stream, args.steps, args.warmup, full=True)
+    mean, norm, ws, ms = t.pop("_mean"), t.pop("_norm"), t.pop("_ws"), t["ms_per_step"]
     in_bytes = n * d * w.elem_bytes
-    k_alg = in_bytes + 4 * d                      # one read of x, one write of the mean
-    fused_alg = 2 * in_bytes + 4 * d              # both passes
-    value = in_bytes / (ms * 1e-3) / 1e9
-    achieved = k_alg / (k_ms * 1e-3) / 1e9
     W = gq.gq_min_code_bits(n, w.s, w.scheme)
     out = {
         "metric": "fused Global-QSGD compress+int-sum+dequant GB/s (fp32 in) and % HBM peak",
-        "value": round(value, 3),
+        "value": t["input_GBs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 6),
+        "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "scheme": f"Global-{w.scheme}_s", "s": w.s,
-                   "q": w.q if w.q != float("inf") else "inf",
-                   "p": w.p if w.p != float("inf") else "inf",
-                   "n_workers": n, "d": d, "input_dtype": w.dtype, "code_bits": w.code_bits,
-                   "min_code_bits": W, "values": w.values},
-        "hbm_frac_fused": round(fused_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "graph_replay": {"ms_per_step": round(graph_us * 1e-3, 6),
-                         "input_GBs": round(in_bytes / (graph_us * 1e-6) / 1e9, 3)},
-        "cold_cache": {"ms_per_step": round(cold_ms, 6),
-                       "input_GBs": round(in_bytes / (cold_ms * 1e-3) / 1e9, 3),
-                       "steps": len(cpairs), "stat": "median"},
-        "kernels_ms": {"norm_pass": round(n_ms, 6), DOMINANT: round(k_ms, 6)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for(w.name), "kernel": DOMINANT,
-                     "alg_bytes_per_launch": k_alg},
+        "config": workload_config(w, W),
+        "hbm_frac_fused": t["hbm_frac_fused"],
+        "graph_replay": t["graph_replay"],
+        "cold_cache": t["cold_cache"],
+        "kernels_ms": t["kernels_ms"],
+        "compress_step": t["compress_step"],
+        "roofline": t["roofline"],
         "bits_per_element": w.code_bits,
         "input_gen_s": round(gen_s, 2),
     }
+    # ---- the measured read ceiling: the best plain stream read of this input
+    # (probe kernels in several launch shapes, and the library's own norm
+    # pass, which reads the same bytes and nothing else)
+    from allreduce_compatible_gradient_amd import probe
+    if not args.no_extras:
+        rc = probe.read_ceiling(xd, reps=5, stream=stream)
+        norm_gbs = in_bytes / (t["kernels_ms"]["norm_pass"] * 1e-3) / 1e9
+        rc["norm_pass_GBs"] = round(norm_gbs, 1)
+        if norm_gbs > rc["GBs"]:
+            rc["GBs"], rc["shape"] = round(norm_gbs, 1), "the norm pass (read-only)"
+            rc["frac_of_8TBs"] = round(norm_gbs / HBM_PEAK_GBS, 4)
+        out["read_ceiling"] = rc
+        out["roofline"]["frac_of_read_ceiling"] = round(out["roofline"]["achieved"] / rc["GBs"], 4)
+        out["frac_of_read_ceiling_fused"] = round(
+            (2 * in_bytes + 4 * d) / (ms * 1e-3) / 1e9 / rc["GBs"], 4)
     if args.unfused:
         def unfused_at(W, reps):
             codes = torch.empty((n, gq.gq_code_row_bytes(d, W)), dtype=torch.uint8, device=dev)
@@ -478,6 +653,7 @@ def main():
             for _ in range(3):
                 ustep()
             torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(reps):
                 ustep()
@@ -501,6 +677,34 @@ def main():
         out["e8"] = e8_report(gq, torch, w, xd, stream, min(args.steps, 50), ws)
     if args.ablation or w.key == 5:
         out["ablation"] = ablation(gq, torch, w, xd, stream, args.steps, ms, mean, norm, ws)
+    del xd, mean, norm, ws
+    torch.cuda.empty_cache()
+
+    # ---- the other large workloads, each whole step and each pass timed the same way
+    keys = [int(k) for k in args.configs.split(",") if k.strip() and int(k) != w.key]
+    if keys:
+        out["configs"] = {}
+        for key in keys:
+            wk = wl.WORKLOADS[key]
+            xk, _ = load_workload(np, torch, wl, wk, dev)
+            tk = time_workload(gq, np, torch, wk, xk, stream, max(10, min(args.steps, 50)),
+                               min(args.warmup, 5), full=False)
+            for k in ("_mean", "_norm", "_ws"):
+                del tk[k]
+            tk["config"] = workload_config(wk, gq.gq_min_code_bits(wk.n, wk.s, wk.scheme))
+            out["configs"][wk.name] = tk
+            del xk
+            torch.cuda.empty_cache()
+
+    # ---- the pages' 8-bit custom reduction against an fp32 sum (omega), and
+    # the measured issue rates behind the VALU-bound kernels' ALU roofline
+    if not args.no_extras:
+        out["e8_omega"] = e8_omega(gq, torch, stream, dev)
+        out["valu_ceiling"] = probe.valu_rates(stream=stream)
+        try:
+            out["ddp_hook"] = ddp_hook_report(torch, w, stream, min(args.steps, 50))
+        except Exception as e:  # the record keeps the headline even if RCCL cannot start here
+            out["ddp_hook"] = {"error": f"{type(e).__name__}: {e}"}
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -92,6 +92,18 @@ int64_t gq_code_row_bytes(int64_t d, int32_t code_bits);
  * for invalid sizes.                                                       */
 int64_t gq_workspace_bytes(int64_t n, int64_t d);
 
+/* Workspace with which gq_compress_mean runs fastest: gq_workspace_bytes
+ * plus, for n >= 32 workers, d bytes (rounded up to 256) in which an fp32
+ * input's fused pass stages 1-byte code sums (an exact sum in [-127, 127],
+ * else an escape byte whose group the next kernel recomputes from x) for a
+ * separate dequantization kernel.  With n workers streamed per coordinate,
+ * writing the fp32 mean inside the pass costs several times its bytes;
+ * staging a quarter of them and writing the mean afterwards is faster.
+ * The results are the same bits either way; a workspace of only
+ * gq_workspace_bytes(n, d) bytes runs the single fused pass.  Returns -1
+ * for invalid sizes.                                                       */
+int64_t gq_compress_workspace_bytes(int64_t n, int64_t d);
+
 /* Global (q,p)-norm of the concatenation (Sec. 2 notation):
  *   q = 2: S_i = sum_j x_ij^2 in fp64 (each square exact); q = inf:
  *   m_i = max_j |x_ij|; other q: S_i = sum_j |x_ij|^q (fp64 pow).
@@ -220,11 +232,32 @@ int32_t gq_compress_mean_from_norm(const void *x, int32_t dtype, int64_t n, int6
                                    void *stream);
 
 /* The whole path: gq_global_norm, then gq_compress_mean_from_norm.
- * Writes N to norm_dev[0] and the dequantized mean to mean[0..d).          */
+ * Writes N to norm_dev[0] and the dequantized mean to mean[0..d).  With a
+ * workspace of gq_compress_workspace_bytes(n, d), n >= 32, fp32 input and
+ * no code sums requested, the compress step runs as two kernels through
+ * 1-byte sums staged in the workspace (same results, faster).               */
 int32_t gq_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s, float q,
                          float p, int32_t scheme, uint64_t seed, int32_t code_bits, float *mean,
                          float *norm_dev, void *code_sum_or_null, void *workspace,
                          int64_t workspace_bytes, void *stream);
+
+/* The two kernels of gq_compress_mean's staged compress step (many
+ * workers; the fused pass itself, split where its only write would be).
+ * gq_compress_sums8, given N in norm_dev[0]: the exact code sum of every
+ * coordinate over the n workers, as in gq_compress_mean_from_norm, stored
+ * as one signed byte when it lies in [-127, 127] and as the escape byte -128
+ * otherwise; sums8 holds d bytes (16-byte aligned).
+ * gq_dequantize_sums8, with the same x, n, s, scheme, seed and N: the mean,
+ * mean[j] = fp32(sum_j kappa) as in gq_dequantize.  A byte -128 marks a
+ * group of 8 coordinates whose sums it recomputes from x (the same codes,
+ * so the same integers); with no escape it reads only the bytes.  Together
+ * they give gq_compress_mean_from_norm's mean bit for bit.                */
+int32_t gq_compress_sums8(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                          int32_t scheme, uint64_t seed, const float *norm_dev, void *sums8,
+                          void *stream);
+int32_t gq_dequantize_sums8(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                            int32_t scheme, uint64_t seed, const float *norm_dev,
+                            const void *sums8, float *mean, void *stream);
 
 /* gq_compress_mean without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,

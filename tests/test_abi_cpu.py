@@ -142,6 +142,22 @@ def test_other_entry_points_reject():
     assert L.gq_qsgd_local_mean(A, 0, 4, 100, 3, 1, NUL, A, NUL, 0, A, ws, NUL) == 1
 
 
+def test_staged_sums_entry_points_reject():
+    L = gq.lib()
+    assert L.gq_compress_sums8(NUL, 0, 4, 100, 7, 0, 1, A, A, NUL) == 1
+    assert L.gq_compress_sums8(A, 0, 4, 100, 7, 0, 1, NUL, A, NUL) == 1
+    assert L.gq_compress_sums8(A, 0, 4, 100, 7, 0, 1, A, U, NUL) == 6
+    assert L.gq_compress_sums8(A, 0, 4, 100, 0, 0, 1, A, A, NUL) == 2
+    assert L.gq_compress_sums8(A, 2, 4, 100, 7, 0, 1, A, A, NUL) == 2
+    assert L.gq_dequantize_sums8(A, 0, 4, 100, 7, 0, 1, A, NUL, A, NUL) == 1
+    assert L.gq_dequantize_sums8(A, 0, 4, 100, 7, 0, 1, A, A, U, NUL) == 6
+    # the staging workspace: d more bytes (256-aligned) from 32 workers on
+    for n, d in ((31, 1000), (32, 1000), (64, 64_000_000)):
+        extra = gq.gq_compress_workspace_bytes(n, d) - gq.gq_workspace_bytes(n, d)
+        assert extra == (0 if n < 32 else -(-d // 256) * 256)
+    assert gq.gq_compress_workspace_bytes(0, 5) == -1
+
+
 def test_noalloc_entry_point_rejects():
     """The no-allocation entry point checks every argument, and the scratch
     it would need, before any HIP call (so these run without a GPU)."""

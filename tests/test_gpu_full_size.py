@@ -5,7 +5,9 @@ compared with the CPU oracle at every coordinate, bit-exact. The results
 come from the launch configuration the benchmark times.
 
 - **Fused path.** The norm, the code sums at the container width and the
-  dequantized mean (`gq_compress_mean`, with and without code sums).
+  dequantized mean (`gq_compress_mean`, with and without code sums), and
+  the staged step's 1-byte sums and mean (`gq_compress_sums8`,
+  `gq_dequantize_sums8`).
 - **Unfused path.** Every worker's packed codes (`gq_quantize`) at the
   minimal and at the container width, their integer sum
   (`gq_reduce_codes`), and the mean from it (`gq_dequantize`).
@@ -111,6 +113,13 @@ def test_every_coordinate(key):
     exp_c = oracle.pack_row(osums, Wc, threads=THREADS)
     assert same_bytes(host(csum), exp_c), "fused code sums differ"
     del mean_c, csum
+    # the staged compress step's two kernels: 1-byte sums (escape -128) and the mean
+    b8 = gq.gq_compress_sums8(xd, s, w.scheme, seed, norm)
+    want8 = np.where(np.abs(osums) <= 127, osums, -128).astype(np.int8)
+    assert np.array_equal(host(b8)[:d], want8), "staged 1-byte sums differ"
+    assert same_bytes(host(gq.gq_dequantize_sums8(xd, s, w.scheme, seed, norm, b8)), omean)
+    compared += 2 * d
+    del b8, want8
 
     # ---- unfused path and word layout: every worker's row
     widths = sorted({Wmin, Wc})

@@ -199,6 +199,55 @@ def test_int32_accumulator_above_2_24(scheme, s, n, dtype):
         assert np.array_equal(host(wmean), mean), W
 
 
+@pytest.mark.parametrize("n,d,scheme,s,q,p,escapes", [(32, 10_007, "L", 3, 2.0, 2.0, False),
+                                                       (40, 4104, "E", 8, 2.0, INF, True),
+                                                       (64, 2049, "L", 127, INF, 2.0, True),
+                                                       (33, 16_384, "E", 5, INF, INF, True),
+                                                       (48, 5000, "L", 1 << 20, 2.0, 2.0, True),
+                                                       (32, 7, "L", 7, 2.0, 2.0, False)])
+def test_staged_sums_for_many_workers(n, d, scheme, s, q, p, escapes):
+    """n >= 32 fp32 workers with the larger workspace: the pass stages
+    1-byte sums and a second kernel writes the mean.  Sums outside
+    [-127, 127] (the first 300 coordinates sit at the top level in every
+    row, so they sum to +-n M; the E rows flip signs) take the escape and
+    are recomputed from x.  Against the oracle and the single fused pass."""
+    x = wl.random_rows(n, d, seed=n * 7 + d, scale=0.2)
+    x[:, : min(d, 300)] = 2.0
+    if scheme == "E":
+        x[::3, : min(d, 100)] = -2.0
+    N, sums, mean = oracle.compress_mean(x, s, q, p, SCH[scheme], 17)
+    # escaped sums (beyond one byte) beside plain ones where the case asks for them
+    assert ((np.abs(sums) > 127).any() and (np.abs(sums) <= 127).any()) == escapes
+    xd = to_dev(x)
+    big = torch.empty(gq.gq_compress_workspace_bytes(n, d), dtype=torch.uint8, device=DEV)
+    small = torch.empty(gq.gq_workspace_bytes(n, d), dtype=torch.uint8, device=DEV)
+    assert big.numel() >= small.numel() + d
+    gmean, gnorm, _ = gq.gq_compress_mean(xd, s, q, p, scheme, 17, workspace=big)
+    check_norm(host(gnorm)[0], N)
+    assert np.array_equal(host(gmean), mean)
+    one, _, _ = gq.gq_compress_mean(xd, s, q, p, scheme, 17, workspace=small)
+    assert np.array_equal(host(one), mean)
+    # the two staged kernels through their own entry points, fp32 and bf16
+    want = np.where(np.abs(sums) <= 127, sums, -128).astype(np.int8)
+    b8 = gq.gq_compress_sums8(xd, s, scheme, 17, gnorm)
+    assert np.array_equal(host(b8)[:d], want)
+    assert np.array_equal(host(gq.gq_dequantize_sums8(xd, s, scheme, 17, gnorm, b8)), mean)
+    xb = wl.f32_to_bf16_bits(x)
+    Nb, sb, meanb = oracle.compress_mean(xb, s, q, p, SCH[scheme], 19)
+    xbd = to_dev(xb)
+    nb = gq.gq_global_norm(xbd, q, p)
+    check_norm(host(nb)[0], Nb)
+    b8 = gq.gq_compress_sums8(xbd, s, scheme, 19, nb)
+    assert np.array_equal(host(b8)[:d], np.where(np.abs(sb) <= 127, sb, -128).astype(np.int8))
+    assert np.array_equal(host(gq.gq_dequantize_sums8(xbd, s, scheme, 19, nb, b8)), meanb)
+    # subnormal inputs (the exact pre-scale) on the same path
+    y = (x * np.float32(1e-40)).astype(np.float32)
+    N2, _, mean2 = oracle.compress_mean(y, s, q, p, SCH[scheme], 18)
+    g2, n2, _ = gq.gq_compress_mean(to_dev(y), s, q, p, scheme, 18, workspace=big)
+    check_norm(host(n2)[0], N2)
+    assert np.array_equal(host(g2), mean2)
+
+
 def test_worker_base_shards_reproduce_the_whole():
     n, d, s = 6, 3000, 9
     x = wl.random_rows(n, d, seed=5)

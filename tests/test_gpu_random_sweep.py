@@ -149,6 +149,30 @@ def test_random_case(k):
     assert np.array_equal(host(wmean), mean)
 
 
+@pytest.mark.parametrize("k", range(0, N_CASES, 4))
+def test_random_case_many_workers(k):
+    """32 to 79 fp32 workers: the path that stages 1-byte sums (with escapes
+    for sums beyond [-127, 127]) between the pass and the mean."""
+    rng = np.random.default_rng([0x5EED, 7, k])
+    n = int(rng.integers(32, 80))
+    d = int(math.exp(rng.uniform(0.0, math.log(20000.0))))
+    scheme = "E" if rng.random() < 0.4 else "L"
+    s = int(rng.integers(1, 13)) if scheme == "E" else max(1, int(math.exp(rng.uniform(0, 7))))
+    q, p = float(rng.choice(ORDERS)), float(rng.choice(ORDERS))
+    seed = int(rng.integers(0, 2**63, dtype=np.int64))
+    x = wl.random_rows(n, d, seed=5000 + k, dtype="f32", scale=10.0 ** rng.uniform(-3, 1))
+    x[rng.random((n, d)) < 0.2] = 0.0
+    if rng.random() < 0.5 and d > 8:  # some columns at one value: large sums, escapes
+        x[:, rng.integers(0, d, size=max(1, d // 10))] = np.abs(x).max()
+    log(f"many-workers case {k}: n={n} d={d} {scheme} s={s} q={q} p={p}")
+    N, _ = oracle.global_norm(x, q, p)
+    gmean, gnorm, _ = gq.gq_compress_mean(to_dev(x), s, q, p, scheme, seed)
+    gN = np.float32(host(gnorm)[0])
+    assert abs(float(gN) - float(N)) <= 1e-6 * abs(float(N)) or gN == N
+    _, _, mean = oracle_at(x, N if gN == N else gN, dict(s=s, scheme=scheme, seed=seed, n=n))
+    assert np.array_equal(host(gmean), mean)
+
+
 @pytest.mark.parametrize("k", range(0, N_CASES, 3))
 def test_random_case_local_and_e8(k):
     c = draw_case(k)
