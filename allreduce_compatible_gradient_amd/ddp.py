@@ -42,7 +42,7 @@ import torch
 import torch.distributed as dist
 
 from . import (gq_dequantize_words, gq_min_code_bits, gq_norm_from_term, gq_norm_term,
-               gq_quantize_words)
+               gq_quantize_words, gq_word_row_bytes, gq_workspace_bytes)
 
 _MASK64 = (1 << 64) - 1
 
@@ -78,10 +78,33 @@ class GlobalQSGDState:
     process_group: object = None
     ops: object = None
     calls: dict = field(default_factory=dict)
+    buffers: dict = field(default_factory=dict)
 
     def __post_init__(self):
         if self.ops is None:
             self.ops = library_ops()
+
+    def bucket_buffers(self, bucket_index: int, buf: torch.Tensor, W: int):
+        """Device buffers of one bucket's reduction, kept between calls: the
+        norm term, N, the norm pass's workspace and the word row.  Reuse is
+        ordered by the stream: a bucket's next codes are written after its
+        previous dequantization, which waits for the all-reduce that read
+        the words."""
+        d = buf.numel()
+        key = (bucket_index, d, buf.dtype, buf.device, W)
+        b = self.buffers.get(key)
+        if b is None:
+            dev = buf.device
+            b = SimpleNamespace(
+                term=torch.empty(1, dtype=torch.float64, device=dev),
+                norm=torch.empty(1, dtype=torch.float32, device=dev),
+                ws=torch.empty(max(gq_workspace_bytes(1, d), 16), dtype=torch.uint8, device=dev)
+                if dev.type == "cuda" else None,
+                words=torch.empty((1, max(gq_word_row_bytes(d, W), 16) // 4), dtype=torch.int32,
+                                  device=dev) if dev.type == "cuda" else None)
+            self.buffers = {k: v for k, v in self.buffers.items() if k[0] != bucket_index}
+            self.buffers[key] = b
+        return b
 
     def next_seed(self, bucket_index: int) -> int:
         """Philox key of this reduction of the bucket: distinct for every
@@ -105,14 +128,15 @@ def global_qsgd_hook(state: GlobalQSGDState, bucket) -> torch.futures.Future:
     W = gq_min_code_bits(world, state.s, state.scheme)
     if W < 0 or W > 32:
         raise ValueError(f"sums of {world} codes with s = {state.s} do not fit 32 bits")
+    bb = state.bucket_buffers(bucket.index(), buf, W)
     # 1. global norm: each rank's term, one all-reduce of a double
-    term = ops.norm_term(x, state.q, state.p)
+    term = ops.norm_term(x, state.q, state.p, term=bb.term, workspace=bb.ws)
     dist.all_reduce(term, op=dist.ReduceOp.MAX if math.isinf(state.p) else dist.ReduceOp.SUM,
                     group=group)
-    norm = ops.norm_from_term(term, state.q, state.p)
+    norm = ops.norm_from_term(term, state.q, state.p, norm=bb.norm)
     # 2. this rank's codes in the word layout, at its worker index
     words = ops.quantize_words(x, state.s, state.scheme, norm, state.next_seed(bucket.index()),
-                               W, worker_base=rank)[0]
+                               W, worker_base=rank, words=bb.words)[0]
     # 3. the integer all-reduce of the codes
     fut = dist.all_reduce(words, op=dist.ReduceOp.SUM, group=group, async_op=True).get_future()
 

@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the read ceiling, VALU rates, 8-bit omega and DDP hook figures "
                          "(counter passes of one workload)")
+    ap.add_argument("--valu-probe", action="store_true",
+                    help="with --no-extras: still run the VALU issue-rate probe kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
     ap.add_argument("--unfused", action="store_true", help="also time the four-call unfused path")
@@ -698,6 +700,8 @@ def main():
 
     # ---- the pages' 8-bit custom reduction against an fp32 sum (omega), and
     # the measured issue rates behind the VALU-bound kernels' ALU roofline
+    if args.valu_probe and args.no_extras:
+        out["valu_ceiling"] = probe.valu_rates(stream=stream)
     if not args.no_extras:
         out["e8_omega"] = e8_omega(gq, torch, stream, dev)
         out["valu_ceiling"] = probe.valu_rates(stream=stream)

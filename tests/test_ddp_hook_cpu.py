@@ -36,20 +36,20 @@ CASES = [("L", 7, 2.0, 2.0), ("E", 6, math.inf, 2.0), ("L", 127, 2.0, math.inf),
 
 def oracle_ops():
     """The hook's four device calls, computed by the oracle on CPU tensors."""
-    def norm_term(x, q, p):
+    def norm_term(x, q, p, term=None, workspace=None):
         _, pw = oracle.global_norm(x.detach().numpy(), q, p)
         t = float(pw[0])  # sum of squares (q = 2) or max |x| (q = inf)
         if math.isinf(q) and not math.isinf(p):
             t = t * t      # the term of (inf, 2) is the square of the max (exact in fp64)
         return torch.tensor([t], dtype=torch.float64)
 
-    def norm_from_term(term, q, p):
+    def norm_from_term(term, q, p, norm=None):
         T = np.array([float(term[0])], dtype=np.float64)
         qq = math.inf if (math.isinf(q) and math.isinf(p)) else 2.0
         N = oracle.lib().oracle_norm_from_partials(T.ctypes.data_as(ctypes.c_void_p), 1, qq, qq)
         return torch.tensor([N], dtype=torch.float32)
 
-    def quantize_words(x, s, scheme, norm, seed, W, worker_base=0):
+    def quantize_words(x, s, scheme, norm, seed, W, worker_base=0, words=None):
         codes = oracle.quantize(x.detach().numpy(), float(norm[0]), s, SCH[scheme], seed,
                                 worker_base=worker_base)
         rows = oracle.pack_words(codes, W, oracle.top_code(s, SCH[scheme]))
