@@ -49,7 +49,9 @@ __global__ __launch_bounds__(THREADS) void k_read(const uint4 *__restrict__ buf,
 
 // ---------------------------------------------------------------------------
 // VALU issue: `iters` iterations of 8 independent instructions of one kind
-// per lane; the eight chains are combined and written once per lane.
+// per lane; the eight chains are combined and written once per lane.  The
+// loop is unrolled 4 times (32 VALU instructions per taken branch), so that
+// its scalar counter and branch take a negligible share of the issue slots.
 enum { kFmaF32 = 0, kAddU32 = 1, kBitop3 = 2, kMadU64 = 3, kAddF64 = 4, kFmaF64 = 5 };
 
 template <int OP>
@@ -62,6 +64,7 @@ __global__ __launch_bounds__(256) void k_valu(int iters, uint32_t seed, uint32_t
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             a[k] = (float)(t + k);
+#pragma unroll 4
         for (int i = 0; i < iters; ++i) {
 #pragma unroll
             for (int k = 0; k < 8; ++k)
@@ -70,15 +73,39 @@ __global__ __launch_bounds__(256) void k_valu(int iters, uint32_t seed, uint32_t
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             r ^= __float_as_uint(a[k]);
-    } else if constexpr (OP == kAddU32 || OP == kBitop3) {
+    } else if constexpr (OP == kAddU32) {
+        // one v_add_u32 per chain and step, written out (plain C adds of a
+        // loop-invariant value would be folded into fewer instructions)
+        uint32_t a[8], b = seed | 1u;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            a[k] = t + (uint32_t)k;
+        int i = 0;
+        for (; i + 4 <= iters; i += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    asm("v_add_u32 %0, %1, %2" : "=v"(a[k]) : "v"(a[k]), "v"(b));
+        }
+        for (; i < iters; ++i) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                asm("v_add_u32 %0, %1, %2" : "=v"(a[k]) : "v"(a[k]), "v"(b));
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            r ^= a[k];
+    } else if constexpr (OP == kBitop3) {
         uint32_t a[8], b = seed | 1u, c = t * 0x9E3779B9u;
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             a[k] = t + (uint32_t)k;
+#pragma unroll 4
         for (int i = 0; i < iters; ++i) {
 #pragma unroll
             for (int k = 0; k < 8; ++k)
-                a[k] = OP == kAddU32 ? a[k] + b : __builtin_amdgcn_bitop3_b32(a[k], b, c, 0x96);
+                a[k] = __builtin_amdgcn_bitop3_b32(a[k], b, c, 0x96);
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k)
@@ -90,6 +117,7 @@ __global__ __launch_bounds__(256) void k_valu(int iters, uint32_t seed, uint32_t
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             a[k] = (uint64_t)(t + (uint32_t)k) << 7;
+#pragma unroll 4
         for (int i = 0; i < iters; ++i) {
 #pragma unroll
             for (int k = 0; k < 8; ++k)
@@ -103,6 +131,7 @@ __global__ __launch_bounds__(256) void k_valu(int iters, uint32_t seed, uint32_t
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             a[k] = (double)(t + (uint32_t)k);
+#pragma unroll 4
         for (int i = 0; i < iters; ++i) {
 #pragma unroll
             for (int k = 0; k < 8; ++k)

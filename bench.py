@@ -521,13 +521,36 @@ class _Bucket:
         return self._index
 
 
+def _hook_device_us(torch, stream, state, buf, steps):
+    """Device time of the hook's four library launches for one bucket (norm
+    term, N from the term, codes in the word layout, dequantization), with
+    the two collectives left out: graph replays, so host time is excluded."""
+    import allreduce_compatible_gradient_amd as gq
+    d = buf.numel()
+    W = gq.gq_min_code_bits(1, state.s, state.scheme)
+    x = buf.view(1, -1)
+    term = torch.empty(1, dtype=torch.float64, device=buf.device)
+    norm = torch.empty(1, dtype=torch.float32, device=buf.device)
+    ws = torch.empty(max(gq.gq_workspace_bytes(1, d), 16), dtype=torch.uint8, device=buf.device)
+    words = torch.empty((1, gq.gq_word_row_bytes(d, W) // 4), dtype=torch.int32, device=buf.device)
+    mean = torch.empty(d, dtype=torch.float32, device=buf.device)
+
+    def launches(st):
+        gq.gq_norm_term(x, state.q, state.p, term=term, workspace=ws, stream=st)
+        gq.gq_norm_from_term(term, state.q, state.p, norm=norm, stream=st)
+        gq.gq_quantize_words(x, state.s, state.scheme, norm, state.seed, W, words=words, stream=st)
+        gq.gq_dequantize_words(words[0], 1, d, state.s, state.scheme, W, norm, mean=mean, stream=st)
+    return _time_us(torch, stream, launches, steps)
+
+
 def ddp_hook_report(torch, w, stream, steps):
     """The DDP communication hook (allreduce_compatible_gradient_amd.ddp) on one
     rank over RCCL, per gradient bucket of 25 and 100 MB: the norm term, its
     all-reduce, N, the codes in the word layout, the integer all-reduce and
     the dequantization, with the workload's scheme and orders.  `us` is the
     wall time per bucket of back-to-back hook calls (host work included, as
-    DDP would see it), `latency_us` that of one call waited for alone."""
+    DDP would see it), `latency_us` that of one call waited for alone, and
+    `device_us` the GPU time of the hook's four library launches."""
     import socket
 
     import torch.distributed as dist
@@ -544,9 +567,11 @@ def ddp_hook_report(torch, w, stream, steps):
         for label, nbytes in (("25MB", 25 << 20), ("100MB", 100 << 20)):
             buf = torch.randn(nbytes // 4, device="cuda", generator=g) * 1e-3
             b = _Bucket(buf, 0)
-            for _ in range(3):
+            for _ in range(10):
                 global_qsgd_hook(state, b).wait()
             torch.cuda.synchronize()
+            # the four library launches of one bucket alone, as graph replays
+            dev_us = _hook_device_us(torch, stream, state, buf, steps)
             t0 = time.perf_counter()
             for _ in range(steps):
                 fut = global_qsgd_hook(state, b)
@@ -561,7 +586,8 @@ def ddp_hook_report(torch, w, stream, steps):
                 lat.append(time.perf_counter() - t0)
             out[label] = {"elements": buf.numel(), "us": round(us, 2),
                           "bucket_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
-                          "latency_us": round(1e6 * sorted(lat)[len(lat) // 2], 1)}
+                          "latency_us": round(1e6 * sorted(lat)[len(lat) // 2], 1),
+                          "device_us": round(dev_us, 2)}
             del buf
     finally:
         dist.destroy_process_group()
