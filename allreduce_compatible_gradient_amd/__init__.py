@@ -52,6 +52,7 @@ SIGNATURES = {
                                           _vp, _vp, _vp]),
     "gq_compress_mean": (_i32, [_vp, _i32, _i64, _i64, _i32, _f32, _f32, _i32, _u64, _i32, _vp,
                                 _vp, _vp, _vp, _i64, _vp]),
+    "gq_sums8_bytes": (_i64, [_i64]),
     "gq_compress_sums8": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _u64, _vp, _vp, _vp]),
     "gq_dequantize_sums8": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _u64, _vp, _vp, _vp, _vp]),
     "gq_compress_mean_noalloc": (_i32, [_vp, _i32, _i64, _i64, _i32, _f32, _f32, _i32, _u64,
@@ -379,15 +380,29 @@ def gq_compress_mean(x: torch.Tensor, s: int, q, p, scheme, seed: int, *, code_b
     return mean, norm, code_sum
 
 
+def gq_sums8_bytes(d: int) -> int:
+    """Bytes of the staging buffer of gq_compress_sums8 / gq_dequantize_sums8."""
+    return int(lib().gq_sums8_bytes(d))
+
+
+def sums8_parts(staged: torch.Tensor, d: int):
+    """Views of a staging buffer: (the group mask as int64 words, the d sum bytes as int8)."""
+    mb = (((d + 511) // 512) * 8 + 15) // 16 * 16
+    u8 = staged.view(torch.uint8)
+    return u8[:mb].view(torch.int64)[: (d + 511) // 512], u8[mb:mb + d].view(torch.int8)
+
+
 def gq_compress_sums8(x: torch.Tensor, s: int, scheme, seed: int, norm: torch.Tensor, *,
                       sums8=None, stream=None):
-    """Exact code sums as bytes (-128: beyond one byte), int8 [d]."""
+    """Staged exact code sums: a bit per 8-coordinate group (1: not all zero),
+    then a byte per coordinate of the marked groups (-128: beyond one byte);
+    uint8 [gq_sums8_bytes(d)] (see sums8_parts)."""
     dt = _input(x)
     n, d = x.shape
     _norm_in(norm, x.device)
     if sums8 is None:
-        sums8 = torch.empty(max(d, 1), dtype=torch.int8, device=x.device)
-    _buf(sums8, d, "sums8", x.device)
+        sums8 = torch.empty(max(gq_sums8_bytes(d), 16), dtype=torch.uint8, device=x.device)
+    _buf(sums8, gq_sums8_bytes(d), "sums8", x.device)
     _check(lib().gq_compress_sums8(_ptr(x), dt, n, d, s, _scheme(scheme), seed, _ptr(norm),
                                    _ptr(sums8), _stream(stream)))
     return sums8
@@ -399,7 +414,7 @@ def gq_dequantize_sums8(x: torch.Tensor, s: int, scheme, seed: int, norm: torch.
     dt = _input(x)
     n, d = x.shape
     _norm_in(norm, x.device)
-    _buf(sums8, d, "sums8", x.device)
+    _buf(sums8, gq_sums8_bytes(d), "sums8", x.device)
     if mean is None:
         mean = torch.empty(d, dtype=torch.float32, device=x.device)
     _buf(mean, 4 * d, "mean", x.device, torch.float32)

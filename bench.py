@@ -458,7 +458,8 @@ def time_workload(gq, np, torch, w, xd, stream, steps, warmup, full):
                              "steps": len(cpairs), "stat": "median"}
     # each kernel of the step alone, one event pair per launch on the same stream
     npairs, kpairs, qpairs = (event_pairs(torch, steps) for _ in range(3))
-    sums8 = torch.empty(d, dtype=torch.int8, device=dev) if staged else None
+    sums8 = (torch.empty(gq.gq_sums8_bytes(d), dtype=torch.uint8, device=dev) if staged
+             else None)
     for i in range(steps):
         npairs[i][0].record(stream)
         gq.gq_global_norm(xd, w.q, w.p, norm=norm, workspace=ws, stream=stream)
@@ -480,9 +481,18 @@ def time_workload(gq, np, torch, w, xd, stream, steps, warmup, full):
     n_ms = float(np.mean([a.elapsed_time(b) for a, b in npairs]))
     q_ms = float(np.mean([a.elapsed_time(b) for a, b in qpairs])) if staged else 0.0
     kernel = "k_compress_sums8" if staged else DOMINANT
-    # algorithmic bytes of the dominant kernel: one read of x, and the 1-byte
-    # sums (staged) or the fp32 mean written
-    k_alg = in_bytes + (d if staged else 4 * d)
+    # algorithmic bytes of the dominant kernel: one read of x, and what it
+    # writes: the fp32 mean, or (staged) the group mask and the 8 bytes of
+    # each marked group (the groups holding a non-zero sum, counted here)
+    if staged:
+        mask, _ = gq.sums8_parts(sums8, d)
+        bits = torch.tensor([bin(v).count("1") for v in range(256)], dtype=torch.int64,
+                            device=dev)
+        marked = int(bits[mask.view(torch.uint8).long()].sum())
+        k_alg = in_bytes + 8 * (-(-d // 512)) + 8 * marked
+    else:
+        marked = None
+        k_alg = in_bytes + 4 * d
     fused_alg = 2 * in_bytes + 4 * d              # both passes of the whole step
     achieved = k_alg / (k_ms * 1e-3) / 1e9
     traffic = traffic_for(w.name)
@@ -498,7 +508,9 @@ def time_workload(gq, np, torch, w, xd, stream, steps, warmup, full):
         "compress_step": {"ms": round(k_ms + q_ms, 6),
                           "frac": round((in_bytes + 4 * d) / ((k_ms + q_ms) * 1e-3) / 1e9
                                         / HBM_PEAK_GBS, 4),
-                          "staged_sums8": staged},
+                          "staged_sums8": staged,
+                          "nonzero_group_share": (round(marked / -(-d // 8), 5) if staged
+                                                  else None)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": kernel, "alg_bytes_per_launch": k_alg,

@@ -93,13 +93,14 @@ int64_t gq_code_row_bytes(int64_t d, int32_t code_bits);
 int64_t gq_workspace_bytes(int64_t n, int64_t d);
 
 /* Workspace with which gq_compress_mean runs fastest: gq_workspace_bytes
- * plus, for n >= 32 workers, d bytes (rounded up to 256) in which an fp32
- * input's fused pass stages 1-byte code sums (an exact sum in [-127, 127],
- * else an escape byte whose group the next kernel recomputes from x) for a
- * separate dequantization kernel.  With n workers streamed per coordinate,
- * writing the fp32 mean inside the pass costs several times its bytes;
- * staging a quarter of them and writing the mean afterwards is faster.
- * The results are the same bits either way; a workspace of only
+ * plus, for n >= 32 workers, gq_sums8_bytes(d) (rounded up to 256), where
+ * an fp32 input's fused pass stages its sums for a separate dequantization
+ * kernel: a bit per group of 8 coordinates, and 1-byte sums of the groups
+ * that are not all zero (an exact sum in [-127, 127], else an escape byte
+ * whose group the next kernel recomputes from x).  With n workers streamed
+ * per coordinate, writing inside the pass costs several times its bytes;
+ * writing almost nothing there and the mean afterwards is faster.  The
+ * results are the same bits either way; a workspace of only
  * gq_workspace_bytes(n, d) bytes runs the single fused pass.  Returns -1
  * for invalid sizes.                                                       */
 int64_t gq_compress_workspace_bytes(int64_t n, int64_t d);
@@ -235,7 +236,7 @@ int32_t gq_compress_mean_from_norm(const void *x, int32_t dtype, int64_t n, int6
  * Writes N to norm_dev[0] and the dequantized mean to mean[0..d).  With a
  * workspace of gq_compress_workspace_bytes(n, d), n >= 32, fp32 input and
  * no code sums requested, the compress step runs as two kernels through
- * 1-byte sums staged in the workspace (same results, faster).               */
+ * sums staged in the workspace (gq_compress_sums8; same results, faster).  */
 int32_t gq_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s, float q,
                          float p, int32_t scheme, uint64_t seed, int32_t code_bits, float *mean,
                          float *norm_dev, void *code_sum_or_null, void *workspace,
@@ -243,15 +244,24 @@ int32_t gq_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int
 
 /* The two kernels of gq_compress_mean's staged compress step (many
  * workers; the fused pass itself, split where its only write would be).
+ * Staging buffer `sums8`, gq_sums8_bytes(d) bytes, 16-byte aligned: first a
+ * mask of one bit per group of 8 coordinates (group g is bit g % 64 of the
+ * 64-bit word g / 64; the part is 8 ceil(d / 512) bytes rounded up to 16,
+ * and that padding is never written), then d bytes (rounded up to 16) of
+ * sums.
  * gq_compress_sums8, given N in norm_dev[0]: the exact code sum of every
- * coordinate over the n workers, as in gq_compress_mean_from_norm, stored
- * as one signed byte when it lies in [-127, 127] and as the escape byte -128
- * otherwise; sums8 holds d bytes (16-byte aligned).
+ * coordinate over the n workers, as in gq_compress_mean_from_norm.  Every
+ * mask word is written; bit g is 1 iff group g holds a non-zero sum (bits
+ * past the last group are 0).  Only such a
+ * group's 8 bytes are written, each sum as one signed byte when it lies in
+ * [-127, 127] and as the escape byte -128 otherwise; the bytes of groups
+ * whose sums are all zero are left as they were.
  * gq_dequantize_sums8, with the same x, n, s, scheme, seed and N: the mean,
- * mean[j] = fp32(sum_j kappa) as in gq_dequantize.  A byte -128 marks a
- * group of 8 coordinates whose sums it recomputes from x (the same codes,
- * so the same integers); with no escape it reads only the bytes.  Together
- * they give gq_compress_mean_from_norm's mean bit for bit.                */
+ * mean[j] = fp32(sum_j kappa) as in gq_dequantize, reading the bytes of the
+ * marked groups only.  A byte -128 makes it recompute that group's sums
+ * from x (the same codes, so the same integers).  Together they give
+ * gq_compress_mean_from_norm's mean bit for bit.                          */
+int64_t gq_sums8_bytes(int64_t d);
 int32_t gq_compress_sums8(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
                           int32_t scheme, uint64_t seed, const float *norm_dev, void *sums8,
                           void *stream);

@@ -151,10 +151,16 @@ def test_staged_sums_entry_points_reject():
     assert L.gq_compress_sums8(A, 2, 4, 100, 7, 0, 1, A, A, NUL) == 2
     assert L.gq_dequantize_sums8(A, 0, 4, 100, 7, 0, 1, A, NUL, A, NUL) == 1
     assert L.gq_dequantize_sums8(A, 0, 4, 100, 7, 0, 1, A, A, U, NUL) == 6
-    # the staging workspace: d more bytes (256-aligned) from 32 workers on
+    # the staging buffer: a bit per 8-coordinate group in 64-bit words, then a
+    # byte per coordinate, each part 16-byte aligned; in the workspace from 32
+    # workers on, 256-byte aligned
+    for d in (0, 1, 8, 511, 512, 513, 64_000_000):
+        mask = (-(-d // 512) * 8 + 15) // 16 * 16
+        assert gq.gq_sums8_bytes(d) == mask + -(-d // 16) * 16
+    assert gq.gq_sums8_bytes(-1) == -1
     for n, d in ((31, 1000), (32, 1000), (64, 64_000_000)):
         extra = gq.gq_compress_workspace_bytes(n, d) - gq.gq_workspace_bytes(n, d)
-        assert extra == (0 if n < 32 else -(-d // 256) * 256)
+        assert extra == (0 if n < 32 else -(-gq.gq_sums8_bytes(d) // 256) * 256)
     assert gq.gq_compress_workspace_bytes(0, 5) == -1
 
 

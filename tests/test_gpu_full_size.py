@@ -113,13 +113,26 @@ def test_every_coordinate(key):
     exp_c = oracle.pack_row(osums, Wc, threads=THREADS)
     assert same_bytes(host(csum), exp_c), "fused code sums differ"
     del mean_c, csum
-    # the staged compress step's two kernels: 1-byte sums (escape -128) and the mean
+    # the staged compress step's two kernels: the group mask and the 1-byte
+    # sums of the marked groups (escape -128), then the mean
     b8 = gq.gq_compress_sums8(xd, s, w.scheme, seed, norm)
-    want8 = np.where(np.abs(osums) <= 127, osums, -128).astype(np.int8)
-    assert np.array_equal(host(b8)[:d], want8), "staged 1-byte sums differ"
+    groups = -(-d // 8)
+    words = -(-d // 512)
+    mb = (words * 8 + 15) // 16 * 16
+    hb8 = host(b8)
+    bits = np.unpackbits(hb8[:words * 8], bitorder="little")
+    padded = np.zeros(groups * 8, np.int64)
+    padded[:d] = osums
+    nzg = (padded.reshape(groups, 8) != 0).any(axis=1)
+    del padded
+    assert np.array_equal(bits[:groups].astype(bool), nzg) and not bits[groups:].any()
+    cols = np.flatnonzero(np.repeat(nzg, 8)[:d])
+    want8 = np.where(np.abs(osums[cols]) <= 127, osums[cols], -128).astype(np.int8)
+    assert np.array_equal(hb8[mb:mb + d].view(np.int8)[cols], want8), "staged 1-byte sums differ"
+    log(f"staged sums: {nzg.mean():.4f} of the 8-coordinate groups are non-zero")
     assert same_bytes(host(gq.gq_dequantize_sums8(xd, s, w.scheme, seed, norm, b8)), omean)
     compared += 2 * d
-    del b8, want8
+    del b8, hb8, want8, cols, bits, nzg
 
     # ---- unfused path and word layout: every worker's row
     widths = sorted({Wmin, Wc})

@@ -199,18 +199,40 @@ def test_int32_accumulator_above_2_24(scheme, s, n, dtype):
         assert np.array_equal(host(wmean), mean), W
 
 
-@pytest.mark.parametrize("n,d,scheme,s,q,p,escapes", [(32, 10_007, "L", 3, 2.0, 2.0, False),
+def staged_matches(staged: np.ndarray, sums: np.ndarray) -> bool:
+    """gq_compress_sums8's buffer against the oracle's exact sums: the group
+    mask (bit g = group g holds a non-zero sum; the bits past the last group
+    in its word zero) and the bytes of the marked groups (the sum, or -128
+    beyond [-127, 127])."""
+    d = sums.size
+    groups = -(-d // 8)
+    words = -(-d // 512)  # the mask's 64-bit words (its 16-byte padding is not written)
+    mb = (words * 8 + 15) // 16 * 16
+    bits = np.unpackbits(staged[:words * 8].view(np.uint8), bitorder="little")
+    padded = np.zeros(groups * 8, np.int64)
+    padded[:d] = sums
+    nzg = (padded.reshape(groups, 8) != 0).any(axis=1)
+    if not (np.array_equal(bits[:groups].astype(bool), nzg) and not bits[groups:].any()):
+        return False
+    cols = np.flatnonzero(np.repeat(nzg, 8)[:d])
+    want = np.where(np.abs(sums) <= 127, sums, -128).astype(np.int8)
+    return np.array_equal(staged[mb:mb + d].view(np.int8)[cols], want[cols])
+
+
+@pytest.mark.parametrize("n,d,scheme,s,q,p,escapes", [(16, 7001, "E", 8, INF, INF, True),
+                                                       (32, 10_007, "L", 3, 2.0, 2.0, False),
                                                        (40, 4104, "E", 8, 2.0, INF, True),
                                                        (64, 2049, "L", 127, INF, 2.0, True),
                                                        (33, 16_384, "E", 5, INF, INF, True),
                                                        (48, 5000, "L", 1 << 20, 2.0, 2.0, True),
                                                        (32, 7, "L", 7, 2.0, 2.0, False)])
 def test_staged_sums_for_many_workers(n, d, scheme, s, q, p, escapes):
-    """n >= 32 fp32 workers with the larger workspace: the pass stages
-    1-byte sums and a second kernel writes the mean.  Sums outside
-    [-127, 127] (the first 300 coordinates sit at the top level in every
-    row, so they sum to +-n M; the E rows flip signs) take the escape and
-    are recomputed from x.  Against the oracle and the single fused pass."""
+    """n >= 32 fp32 workers with the larger workspace: the pass stages a
+    bit per 8-coordinate group and 1-byte sums of the non-zero groups, and
+    a second kernel writes the mean.  Sums outside [-127, 127] (the first
+    300 coordinates sit at the top level in every row, so they sum to
+    +-n M; the E rows flip signs) take the escape and are recomputed from
+    x.  Against the oracle and the single fused pass."""
     x = wl.random_rows(n, d, seed=n * 7 + d, scale=0.2)
     x[:, : min(d, 300)] = 2.0
     if scheme == "E":
@@ -221,16 +243,17 @@ def test_staged_sums_for_many_workers(n, d, scheme, s, q, p, escapes):
     xd = to_dev(x)
     big = torch.empty(gq.gq_compress_workspace_bytes(n, d), dtype=torch.uint8, device=DEV)
     small = torch.empty(gq.gq_workspace_bytes(n, d), dtype=torch.uint8, device=DEV)
-    assert big.numel() >= small.numel() + d
+    assert (big.numel() >= small.numel() + d) == (n >= 32)  # the staging from 32 workers
     gmean, gnorm, _ = gq.gq_compress_mean(xd, s, q, p, scheme, 17, workspace=big)
     check_norm(host(gnorm)[0], N)
     assert np.array_equal(host(gmean), mean)
     one, _, _ = gq.gq_compress_mean(xd, s, q, p, scheme, 17, workspace=small)
     assert np.array_equal(host(one), mean)
-    # the two staged kernels through their own entry points, fp32 and bf16
-    want = np.where(np.abs(sums) <= 127, sums, -128).astype(np.int8)
-    b8 = gq.gq_compress_sums8(xd, s, scheme, 17, gnorm)
-    assert np.array_equal(host(b8)[:d], want)
+    # the two staged kernels through their own entry points, fp32 and bf16;
+    # the staging buffer starts full of garbage (unmarked groups stay unread)
+    b8 = torch.full((gq.gq_sums8_bytes(d),), 0x7F, dtype=torch.uint8, device=DEV)
+    gq.gq_compress_sums8(xd, s, scheme, 17, gnorm, sums8=b8)
+    assert staged_matches(host(b8), sums)
     assert np.array_equal(host(gq.gq_dequantize_sums8(xd, s, scheme, 17, gnorm, b8)), mean)
     xb = wl.f32_to_bf16_bits(x)
     Nb, sb, meanb = oracle.compress_mean(xb, s, q, p, SCH[scheme], 19)
@@ -238,8 +261,14 @@ def test_staged_sums_for_many_workers(n, d, scheme, s, q, p, escapes):
     nb = gq.gq_global_norm(xbd, q, p)
     check_norm(host(nb)[0], Nb)
     b8 = gq.gq_compress_sums8(xbd, s, scheme, 19, nb)
-    assert np.array_equal(host(b8)[:d], np.where(np.abs(sb) <= 127, sb, -128).astype(np.int8))
+    assert staged_matches(host(b8), sb)
     assert np.array_equal(host(gq.gq_dequantize_sums8(xbd, s, scheme, 19, nb, b8)), meanb)
+    # all-zero input: every bit clear, nothing else written, mean zero
+    z = torch.zeros((n, d), dtype=torch.float32, device=DEV)
+    zn = gq.gq_global_norm(z, q, p)
+    gq.gq_compress_sums8(z, s, scheme, 3, zn, sums8=b8)
+    assert staged_matches(host(b8), np.zeros(d, np.int64))
+    assert not host(gq.gq_dequantize_sums8(z, s, scheme, 3, zn, b8)).any()
     # subnormal inputs (the exact pre-scale) on the same path
     y = (x * np.float32(1e-40)).astype(np.float32)
     N2, _, mean2 = oracle.compress_mean(y, s, q, p, SCH[scheme], 18)
