@@ -94,3 +94,51 @@ def test_graph_replays_match_eager(n, d, s, q, p, scheme, W):
         fused(cur)  # eager call between replays
         torch.cuda.synchronize()
     del graph
+
+
+def test_staged_many_worker_pass_replays():
+    """The many-worker path (staged group mask and 1-byte sums, then the
+    mean) and the no-allocation entry point, captured together and replayed.
+    A staging buffer that starts stale (left from another input) must not
+    leak into a replay."""
+    n, d, s = 40, 30_011, 5
+    x = wl.random_rows(n, d, seed=77, scale=0.3)
+    x[:, :64] = 3.0  # sums beyond one byte: escapes recomputed from x
+    xd = torch.from_numpy(x).to(DEV)
+    ws = torch.empty(gq.gq_compress_workspace_bytes(n, d), dtype=torch.uint8, device=DEV)
+    assert ws.numel() > gq.gq_workspace_bytes(n, d)  # the staged path
+    mean = torch.empty(d, dtype=torch.float32, device=DEV)
+    norm = torch.empty(1, dtype=torch.float32, device=DEV)
+    mean2 = torch.empty_like(mean)
+    norm2 = torch.empty_like(norm)
+
+    def step(st):
+        gq.gq_compress_mean(xd, s, INF, INF, "L", 9, mean=mean, norm=norm, workspace=ws, stream=st)
+        gq.gq_compress_mean_noalloc(xd, s, INF, INF, "L", 9, mean=mean2, norm=norm2, stream=st)
+
+    N, sums, omean = oracle.compress_mean(x, s, INF, INF, oracle.SCHEME_L, 9)
+    assert np.abs(sums).max() > 127  # escapes beside plain bytes
+    cur = torch.cuda.current_stream()
+    step(cur)
+    assert np.float32(host(norm)[0]) == N
+    assert np.array_equal(host(mean), omean) and np.array_equal(host(mean2), omean)
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        step(side)
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step(side)
+    other = torch.from_numpy(wl.random_rows(n, d, seed=78, scale=0.3)).to(DEV)
+    for rep in range(3):
+        # eager work between replays, leaving the staging area stale
+        gq.gq_compress_mean(other, s, INF, INF, "L", 10, workspace=ws)
+        mean.zero_()
+        mean2.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        assert np.array_equal(host(mean), omean), rep
+        assert np.array_equal(host(mean2), omean), rep
+    del graph
