@@ -22,6 +22,10 @@ one worker, its bucket one row of the operator's input. Per bucket:
 4. Dequantization. `gq_dequantize_words` with n = world gives the mean
    gradient, which DDP writes into the parameters' gradients.
 
+Every step is enqueued in stream order: each collective makes the current
+stream wait for it, and the host never blocks. The returned future is
+already complete, and on a GPU it carries the current stream's events.
+
 The arithmetic of every step runs in libgq.so's kernels. This module only
 orders the calls and the two collectives, and derives each call's Philox
 seed. The seed comes from (base seed, bucket index, how many times that
@@ -137,16 +141,17 @@ def global_qsgd_hook(state: GlobalQSGDState, bucket) -> torch.futures.Future:
     # 2. this rank's codes in the word layout, at its worker index
     words = ops.quantize_words(x, state.s, state.scheme, norm, state.next_seed(bucket.index()),
                                W, worker_base=rank, words=bb.words)[0]
-    # 3. the integer all-reduce of the codes
-    fut = dist.all_reduce(words, op=dist.ReduceOp.SUM, group=group, async_op=True).get_future()
-
-    # 4. one dequantization to the mean, written into the bucket
-    def finish(f):
-        wsum = f.value()[0]
-        if buf.dtype == torch.float32:
-            ops.dequantize_words(wsum, world, d, state.s, state.scheme, W, norm, mean=buf)
-        else:
-            buf.copy_(ops.dequantize_words(wsum, world, d, state.s, state.scheme, W, norm))
-        return buf
-
-    return fut.then(finish)
+    # 3. the integer all-reduce of the codes, ordered on the current stream
+    #    like the norm term's (the host does not wait for it)
+    dist.all_reduce(words, op=dist.ReduceOp.SUM, group=group)
+    # 4. one dequantization to the mean, written into the bucket after it
+    if buf.dtype == torch.float32:
+        ops.dequantize_words(words, world, d, state.s, state.scheme, W, norm, mean=buf)
+    else:
+        buf.copy_(ops.dequantize_words(words, world, d, state.s, state.scheme, W, norm))
+    # a future already holding the bucket; on a GPU it records the current
+    # stream, so whoever waits on it waits for the work above (a continuation
+    # on the all-reduce's own future measured 57 against 9 us of host time)
+    fut = torch.futures.Future(devices=[buf.device]) if buf.is_cuda else torch.futures.Future()
+    fut.set_result(buf)
+    return fut
