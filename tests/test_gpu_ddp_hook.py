@@ -98,3 +98,46 @@ def test_hook_buckets_match_the_oracle(one_rank_group, scheme, s, q, p):
                                   for prm in model.parameters()]))
     want = np.sort(np.concatenate([o.cpu().numpy() for o in last.values()]))
     assert np.array_equal(got, want)
+
+
+class _Bucket:
+    """The part of DDP's GradBucket the hook reads."""
+
+    def __init__(self, buf, index):
+        self._buf, self._index = buf, index
+
+    def buffer(self):
+        return self._buf
+
+    def index(self):
+        return self._index
+
+
+@pytest.mark.parametrize("scheme,s,q,p", [("L", 15, 2.0, 2.0), ("E", 8, math.inf, 2.0)])
+def test_hook_on_a_bf16_bucket(one_rank_group, scheme, s, q, p):
+    """A bf16 gradient bucket (a bf16 model's): the codes come from the
+    bf16 values widened exactly, the mean is formed in fp32 and written back
+    rounded to bf16 (to nearest, ties to even) -- the oracle's mean rounded
+    the same way, bit for bit.  Two calls on one bucket use two seeds."""
+    import workloads as wl
+
+    from allreduce_compatible_gradient_amd.ddp import GlobalQSGDState, global_qsgd_hook
+    d = 3_000_017
+    x = wl.random_rows(1, d, seed=21, dtype="bf16", scale=0.02)
+    state = GlobalQSGDState(scheme=scheme, s=s, q=q, p=p, seed=3)
+    seeds = []
+    plain_next = state.next_seed
+
+    def next_seed(i):
+        seeds.append(plain_next(i))
+        return seeds[-1]
+    state.next_seed = next_seed
+    for call in range(2):
+        buf = torch.from_numpy(x.view(np.int16).copy()).to("cuda").view(torch.bfloat16)[0]
+        out = global_qsgd_hook(state, _Bucket(buf, 4)).wait()
+        torch.cuda.synchronize()
+        _, _, mean = oracle.compress_mean(x, s, q, p, SCH[scheme], seeds[-1])
+        want = wl.f32_to_bf16_bits(mean)
+        assert out.dtype == torch.bfloat16
+        assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), want), call
+    assert seeds[0] != seeds[1]
