@@ -52,6 +52,11 @@ SIGNATURES = {
                                           _vp, _vp, _vp]),
     "gq_compress_mean": (_i32, [_vp, _i32, _i64, _i64, _i32, _f32, _f32, _i32, _u64, _i32, _vp,
                                 _vp, _vp, _vp, _i64, _vp]),
+    "gq_span_bounds_bytes": (_i64, [_i64, _i64]),
+    "gq_global_norm_bounds": (_i32, [_vp, _i32, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _i64,
+                                     _vp]),
+    "gq_compress_mean_skip": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _u64, _vp, _vp, _i32,
+                                     _vp, _vp, _vp]),
     "gq_sums8_bytes": (_i64, [_i64]),
     "gq_compress_sums8": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _u64, _vp, _vp, _vp]),
     "gq_dequantize_sums8": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _u64, _vp, _vp, _vp, _vp]),
@@ -354,6 +359,54 @@ def gq_compress_mean_from_norm(x: torch.Tensor, s: int, scheme, seed: int, norm:
     _check(lib().gq_compress_mean_from_norm(_ptr(x), dt, n, d, s, _scheme(scheme), seed,
                                             _ptr(norm), code_bits, _ptr(mean), _ptr(code_sum),
                                             _stream(stream)))
+    return mean, code_sum
+
+
+def gq_span_bounds_bytes(n: int, d: int) -> int:
+    """Bytes of the span bounds of the zero-code skip: 2 n stride, with
+    stride = 16 ceil(d / 8192) entries per row (one per 512 coordinates,
+    padded)."""
+    return int(lib().gq_span_bounds_bytes(n, d))
+
+
+def gq_global_norm_bounds(x: torch.Tensor, q=2.0, p=2.0, *, norm=None, bounds=None,
+                          workspace=None, stream=None):
+    """The global norm and, in the same pass, the span bounds of the
+    zero-code skip: (norm, bounds), bounds a uint8 device tensor of
+    gq_span_bounds_bytes(n, d) bytes holding the 16-bit bounds."""
+    dt = _input(x)
+    n, d = x.shape
+    norm = (torch.empty(1, dtype=torch.float32, device=x.device) if norm is None
+            else _buf(norm, 4, "norm", x.device, torch.float32))
+    nb = max(gq_span_bounds_bytes(n, d), 0)
+    if bounds is None:
+        bounds = torch.empty(max(nb, 2), dtype=torch.uint8, device=x.device)
+    _buf(bounds, nb, "bounds", x.device)
+    ws = _workspace(workspace, n, d, x.device)
+    _check(lib().gq_global_norm_bounds(_ptr(x), dt, n, d, _order(q), _order(p), _ptr(norm),
+                                       _ptr(bounds), _ptr(ws), _nbytes(ws), _stream(stream)))
+    return norm, bounds
+
+
+def gq_compress_mean_skip(x: torch.Tensor, s: int, scheme, seed: int, norm: torch.Tensor,
+                          bounds: torch.Tensor, *, code_bits: int = 0,
+                          want_code_sum: bool = False, mean=None, code_sum=None, stream=None):
+    """gq_compress_mean_from_norm with the zero-code skip, given the bounds
+    gq_global_norm_bounds wrote for this x: (mean, code_sum or None)."""
+    dt = _input(x)
+    n, d = x.shape
+    _norm_in(norm, x.device)
+    _buf(bounds, max(gq_span_bounds_bytes(n, d), 0), "bounds", x.device)
+    if mean is None:
+        mean = torch.empty(d, dtype=torch.float32, device=x.device)
+    _buf(mean, 4 * d, "mean", x.device, torch.float32)
+    if want_code_sum and code_sum is None:
+        code_sum = torch.empty(max(gq_code_row_bytes(d, code_bits), 0), dtype=torch.uint8,
+                               device=x.device)
+    _buf(code_sum, max(gq_code_row_bytes(d, code_bits), 0), "code_sum", x.device)
+    _check(lib().gq_compress_mean_skip(_ptr(x), dt, n, d, s, _scheme(scheme), seed, _ptr(norm),
+                                       _ptr(bounds), code_bits, _ptr(mean), _ptr(code_sum),
+                                       _stream(stream)))
     return mean, code_sum
 
 

@@ -134,6 +134,15 @@ __host__ __device__ inline int64_t row_bytes(int64_t d, int32_t W) { return ((d 
 __host__ __device__ inline int64_t sums8_mask_bytes(int64_t d) { return ((d + 511) / 512 * 8 + 15) / 16 * 16; }
 __host__ __device__ inline int64_t sums8_bytes(int64_t d) { return sums8_mask_bytes(d) + (d + 15) / 16 * 16; }
 
+// Bounds of |x| that let the fused pass skip coordinates whose code is
+// provably 0: one 16-bit bound per (row, 512-coordinate span), the span one
+// wave of the fused pass covers; written by pass 1, row-major.
+constexpr int kSpan = 512;
+__host__ __device__ inline int64_t bound_spans(int64_t d) { return (d + kSpan - 1) / kSpan; }
+// Entries per row: the spans rounded up to 16, so that a one-shot pass-1
+// block's 8 (fp32) or 16 (bf16) bounds are one aligned 16- or 32-byte store.
+__host__ __device__ inline int64_t bound_stride(int64_t d) { return (bound_spans(d) + 15) / 16 * 16; }
+
 inline int64_t align256(int64_t b) { return (b + 255) & ~(int64_t)255; }
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -195,8 +204,8 @@ OneShotGeom oneshot_geom(int64_t n, int64_t d, int64_t elem_bytes)
 
 struct WsLayout {
     int64_t partials, mid, per_worker, params, total;
-    // gq_compress_mean's optional staging of 1-byte code sums (n >= kSums8MinN)
-    int64_t sums8, total_compress;
+    // gq_compress_mean's optional span bounds (u16 [n][bound_stride(d)])
+    int64_t bounds, total_compress;
 };
 
 // The layout covers the pass-1 geometry of either input type.
@@ -216,8 +225,8 @@ WsLayout ws_layout(int64_t n, int64_t d)
     w.per_worker = w.mid + align256(mid);
     w.params = w.per_worker + align256(8 * n);
     w.total = w.params + align256(16 * n);
-    w.sums8 = w.total;
-    w.total_compress = (n >= kSums8MinN && d > 0) ? w.total + align256(sums8_bytes(d)) : w.total;
+    w.bounds = w.total;
+    w.total_compress = d > 0 ? w.total + align256(2 * n * bound_stride(d)) : w.total;
     return w;
 }
 
@@ -724,6 +733,49 @@ __device__ __forceinline__ float wave_max(float v)
     return v;
 }
 
+// Span bounds.  The largest |x| of 8 widened inputs as an ordered integer:
+// max of (bits & 0x7FFFFFFF), so an inf or a NaN exceeds every finite value.
+__device__ __forceinline__ uint32_t abs_bits_max(const float (&v)[kPer])
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        m = max(m, __float_as_uint(v[k]) & 0x7FFFFFFFu);
+    return m;
+}
+
+// Every lane of the wave must be active.  Within each row of 16 lanes the
+// partners are lane ^ 1 and lane ^ 2 (quad permutations), then the mirror
+// of each 8-lane half and of the row (DPP moves, no LDS round trip); the
+// four rows' maxima are then read from lanes 0, 16, 32 and 48.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false)); // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false)); // row_mirror
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+// The stored bound: the high half of the largest pattern, rounded up, i.e.
+// the smallest bf16 pattern whose value is >= every |x| of the span.  Values
+// 0x7F80 and above stand for inf or NaN (or a finite value that rounds up
+// to inf) and make the span dense.
+__device__ __forceinline__ uint16_t bound16(uint32_t m) { return (uint16_t)((m + 0xFFFFu) >> 16); }
+
+// One wave's bound for the span starting at coordinate jw of row i (all
+// lanes active; lane 0 stores it when the span starts inside the row).
+// stride: entries per row (bound_stride).
+__device__ __forceinline__ void store_bound(uint16_t *__restrict__ bounds, int64_t stride,
+                                            int64_t i, int64_t jw, int64_t d, uint32_t lane_max)
+{
+    const uint32_t m = wave_max_u32(lane_max);
+    if ((threadIdx.x & 63) == 0 && jw < d)
+        bounds[i * stride + jw / kSpan] = bound16(m);
+}
+
 // Block reduction with a fixed tree: butterflies inside each wave, then the
 // WAVES wave results in order.  Result valid in thread 0.
 template <bool MAX, int WAVES = kThreads / 64>
@@ -750,14 +802,18 @@ __device__ __forceinline__ double block_reduce(double v, double *lds)
 
 // ---------------------------------------------------------------------------
 // Pass 1: per-(chunk, worker) partial norms.  Block b reads chunk b / n of
-// row b % n, so the last blocks to run read the ends of all rows.
+// row b % n, so the last blocks to run read the ends of all rows.  With
+// `bounds`, each wave also stores the bound of every 512-coordinate span it
+// reads (see bound16).
 
 // QM: 0 = q 2 (exact squares), 1 = q inf (max |x|), 2 = other q (fp64 pow)
 template <int DT, int QM>
 __global__ __launch_bounds__(kThreads) void k_norm_partial(const void *__restrict__ x, int64_t n,
                                                            int64_t d, int64_t chunks,
                                                            int64_t chunk_len, double qd,
-                                                           double *__restrict__ partials)
+                                                           double *__restrict__ partials,
+                                                           uint16_t *__restrict__ bounds,
+                                                           int64_t bstride)
 {
     constexpr bool QINF = QM == 1;
     __shared__ double red[4];
@@ -767,6 +823,12 @@ __global__ __launch_bounds__(kThreads) void k_norm_partial(const void *__restric
     const int64_t je = (jb + chunk_len < d) ? jb + chunk_len : d;
     const bool vec_row = (d & 7) == 0;
     const int64_t row_off = i * d;
+    // lanes run the loops below in lockstep until the last lane's group
+    // leaves the chunk: a wave's bounds are formed in the steps where its
+    // last lane is still inside (so is every other), and the steps where it
+    // is not -- only at a row end that is not a whole tile, within the last
+    // four tiles -- are redone after the loops
+    const int64_t to_last = 8 * (63 - (int64_t)(threadIdx.x & 63));
     double s0 = 0.0, s1 = 0.0;
     float mx = 0.0f;
     int64_t j = jb + (int64_t)threadIdx.x * kPer;
@@ -778,6 +840,13 @@ __global__ __launch_bounds__(kThreads) void k_norm_partial(const void *__restric
             load_group<DT>(x, row_off, j + kTile, d, true, v1);
             load_group<DT>(x, row_off, j + 2 * kTile, d, true, v2);
             load_group<DT>(x, row_off, j + 3 * kTile, d, true, v3);
+            if (bounds && j + to_last + 3 * kTile < je) {
+                const int64_t jw = j - 8 * (int64_t)(threadIdx.x & 63);
+                store_bound(bounds, bstride, i, jw, d, abs_bits_max(v0));
+                store_bound(bounds, bstride, i, jw + kTile, d, abs_bits_max(v1));
+                store_bound(bounds, bstride, i, jw + 2 * kTile, d, abs_bits_max(v2));
+                store_bound(bounds, bstride, i, jw + 3 * kTile, d, abs_bits_max(v3));
+            }
 #pragma unroll
             for (int k = 0; k < kPer; ++k) {
                 if (QINF) {
@@ -800,6 +869,9 @@ __global__ __launch_bounds__(kThreads) void k_norm_partial(const void *__restric
     for (; j < je; j += kTile) {
         float v[kPer];
         load_group<DT>(x, row_off, j, je, vec_row, v);
+        if (bounds && j + to_last < je)
+            store_bound(bounds, bstride, i, j - 8 * (int64_t)(threadIdx.x & 63), d,
+                        abs_bits_max(v));
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             if (QINF)
@@ -810,6 +882,19 @@ __global__ __launch_bounds__(kThreads) void k_norm_partial(const void *__restric
                 s0 += pow(fabs((double)v[k]), qd);
         }
     }
+    if (bounds && (je - jb) % kTile != 0) {
+        // the last four tiles of a chunk ending inside a tile, with every
+        // lane of the block active (loads past the end give 0)
+        const int64_t last = jb + (je - jb - 1) / kTile * kTile;
+        for (int64_t jt = (last - 3 * kTile > jb) ? last - 3 * kTile : jb; jt < je; jt += kTile) {
+            const int64_t jj = jt + (int64_t)threadIdx.x * kPer;
+            float v[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (jj < je)
+                load_group<DT>(x, row_off, jj, je, vec_row, v);
+            store_bound(bounds, bstride, i, jt + (int64_t)(threadIdx.x >> 6) * kSpan, d,
+                        abs_bits_max(v));
+        }
+    }
     const double r = QINF ? block_reduce<true>((double)mx, red) : block_reduce<false>(s0 + s1, red);
     if (threadIdx.x == 0)
         partials[i * chunks + c] = r;
@@ -818,14 +903,19 @@ __global__ __launch_bounds__(kThreads) void k_norm_partial(const void *__restric
 // Pass 1, one-shot: block b reads elements [g span, (g + 1) span) of row
 // i = b / bpr, g = b % bpr: groups of 8 at (u * 512 + thread) * 8 for
 // u < 16 KB / (8 * 512 * element bytes), all loads issued before the sums.
+// With `bounds`, each wave stores the bound of each 512-coordinate span it
+// reads (see bound16).
 template <int DT, int QM>
 __global__ __launch_bounds__(kOsThreads) void k_norm_oneshot(const void *__restrict__ x, int64_t d,
                                                              int64_t bpr, int64_t span, double qd,
-                                                             double *__restrict__ partials)
+                                                             double *__restrict__ partials,
+                                                             uint16_t *__restrict__ bounds,
+                                                             int64_t bstride)
 {
     constexpr bool QINF = QM == 1;
     constexpr int G = DT == GQ_IN_F32 ? 1 : 2; // 8-element groups per thread
     __shared__ double red[kOsThreads / 64];
+    __shared__ alignas(16) uint16_t blk_bounds[G * (kOsThreads / 64)];
     const int64_t i = blockIdx.x / bpr, g = blockIdx.x % bpr;
     float v[G][kPer];
     if ((d & 7) == 0) {
@@ -866,6 +956,18 @@ __global__ __launch_bounds__(kOsThreads) void k_norm_oneshot(const void *__restr
             }
         }
     }
+    if (bounds) {
+        // group u of lane l of wave w starts at g span + (u 512 + 64 w + l) 8,
+        // so wave w's bound for group u is the block's entry u 8 + w; the
+        // block's 8 G entries go out together below (one aligned store:
+        // the row stride is a multiple of 16 entries)
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            const uint32_t m = wave_max_u32(abs_bits_max(v[u]));
+            if ((threadIdx.x & 63) == 0)
+                blk_bounds[u * (kOsThreads / 64) + (threadIdx.x >> 6)] = bound16(m);
+        }
+    }
     double s0 = 0.0, s1 = 0.0;
     float mx = 0.0f;
 #pragma unroll
@@ -887,6 +989,10 @@ __global__ __launch_bounds__(kOsThreads) void k_norm_oneshot(const void *__restr
                           : block_reduce<false, kOsThreads / 64>(s0 + s1, red);
     if (threadIdx.x == 0)
         partials[blockIdx.x] = r;
+    // entries past the row's last span land in the row's padding
+    if (bounds && threadIdx.x < G)
+        *(uint4 *)(bounds + i * bstride + g * (span / kSpan) + 8 * threadIdx.x) =
+            *(const uint4 *)(blk_bounds + 8 * threadIdx.x);
 }
 
 // Middle reduction of the one-shot partials: block b sums (or maxes) the
@@ -1112,12 +1218,208 @@ typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ i16x2 as_i16x2(uint32_t w) { return __builtin_bit_cast(i16x2, w); }
 
+// ---------------------------------------------------------------------------
+// Zero-code skip of the fused pass.  With one global norm over a long
+// concatenation |x| / N is small, and most coordinates round to code 0.  Let
+// K = 16 (L) or s + 15 (E) and sigK = sigma 2^K (exact, a power-of-two
+// scaling), so that t 2^K = |x| pre sigK.  Where t is below the first
+// non-zero level -- t < 1 (L) or t < 2^(1-s) (E), i.e. t 2^K < 2^16 -- the
+// lower level is 0 and F >> 16 = floor(t 2^K) = (uint)(|x| pre sigK): the
+// code is non-zero only if the 16-bit uniform h is below it, or equal to it
+// and the second draw decides.  Pass 1 stores, per (row, 512-coordinate
+// span), a bf16 pattern B >= every |x| of the span (bound16).  The
+// threshold H = (uint)(B pre sigK) is then >= F >> 16 of every coordinate of
+// the span, fp32 multiplication and truncation being monotone, so a group
+// whose eight h all exceed H has eight zero codes and is never loaded.  A
+// span whose H would reach 2^16 (some t may reach the first level), whose B
+// is inf or NaN, or a sigK that overflows, is dense: every group is loaded
+// and quantized as without the skip.
+
+// Lane l: the threshold of row c + l for this wave's span (0x10000: dense).
+template <bool PRE>
+__device__ __forceinline__ uint32_t span_threshold(const uint16_t *__restrict__ bounds,
+                                                   int64_t bstride, int64_t span, int64_t c,
+                                                   int64_t n, const QParams &q, float sigK,
+                                                   bool sparse_ok)
+{
+    const int64_t r = c + (int64_t)(threadIdx.x & 63);
+    uint32_t H = 0x10000u;
+    if (sparse_ok && r < n) {
+        const uint32_t b = bounds[r * bstride + span];
+        if (b < 0x7F80u) {
+            float a = __uint_as_float(b << 16);
+            if (PRE)
+                a = a * q.pre;
+            const float th = a * sigK;
+            if (th < 65536.0f)
+                H = (uint32_t)th;
+        }
+    }
+    return H;
+}
+
+// The smallest of the eight 16-bit uniform halves of one Philox block.
+__device__ __forceinline__ uint32_t min_half16(const uint4 &A)
+{
+    const u16x2 m = __builtin_elementwise_min(
+        __builtin_elementwise_min(__builtin_bit_cast(u16x2, A.x), __builtin_bit_cast(u16x2, A.y)),
+        __builtin_elementwise_min(__builtin_bit_cast(u16x2, A.z), __builtin_bit_cast(u16x2, A.w)));
+    return min((uint32_t)m.x, (uint32_t)m.y);
+}
+
+// Magnitudes (0 or 1) of a group in a sparse span, from draw 0: T = F >> 16
+// as above, and S = T + (0xFFFF - h) carries into bit 16 iff h < T; its low
+// half is all ones iff h == T, a tie for the second draw.
+template <bool PRE>
+__device__ __forceinline__ void quant_group_sparse(const float (&v)[kPer], const uint4 &A,
+                                                   const QParams &q, float sigK,
+                                                   float (&m)[kPer], bool &tie)
+{
+    const uint32_t hx[kPer / 2] = {~A.x, ~A.y, ~A.z, ~A.w}; // 0xFFFF - h, two per word
+    uint32_t S[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        float a = fabsf(v[k]);
+        if (PRE)
+            a = a * q.pre;
+        const uint32_t T = cvt_u32_sat(a * sigK);
+        S[k] = (k & 1) ? add_half16<1>(T, hx[k >> 1]) : add_half16<0>(T, hx[k >> 1]);
+        m[k] = (float)((S[k] >> 16) & 0xFFu);
+    }
+    const uint32_t mx = max3_lo16(S[6], S[7], max3_lo16(S[0], S[1], S[2]));
+    tie |= ((uint16_t)mx == 0xFFFFu) | ((uint16_t)max3_lo16(S[3], S[4], S[5]) == 0xFFFFu);
+}
+
+// accumulate_workers with the zero-code skip: every lane of the wave must be
+// here (the thresholds are shared through lane reads); `live` marks lanes
+// whose group is inside the row.  Rows of a dense span take quant_group.
+template <int DT, int SCH, bool PRE, bool FACC>
+__device__ __forceinline__ void accumulate_workers_skip(const void *__restrict__ x, int64_t n,
+                                                        int64_t d, int64_t j0, bool vec,
+                                                        bool live, const QParams &q,
+                                                        uint32_t k0, uint32_t k1,
+                                                        const uint16_t *__restrict__ bounds,
+                                                        int64_t bstride, int64_t span, float sigK,
+                                                        bool sparse_ok, float (&accf)[kPer],
+                                                        int (&acci)[kPer])
+{
+    const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
+    for (int64_t c = 0; c < n; c += 64) {
+        const uint32_t Hl = span_threshold<PRE>(bounds, bstride, span, c, n, q, sigK, sparse_ok);
+        const int cnt = (int)(n - c < 64 ? n - c : 64);
+        for (int r = 0; r < cnt; ++r) {
+            const int64_t i = c + r;
+            const uint32_t H = __builtin_amdgcn_readlane(Hl, r);
+            const bool dense = H > 0xFFFFu;
+            const uint4 A = philox10(make_uint4(blo, bhi, (uint32_t)i, 0u), k0, k1);
+            if (live && (dense || min_half16(A) <= H)) {
+                float v[kPer], m[kPer];
+                bool tie = false;
+                load_group<DT>(x, i * d, j0, d, vec, v);
+                if (dense)
+                    quant_group<SCH, PRE, false>(v, A, q, m, tie);
+                else
+                    quant_group_sparse<PRE>(v, A, q, sigK, m, tie);
+                if (tie) {
+                    const uint4 B = philox10(make_uint4(blo, bhi, (uint32_t)i, 1u), k0, k1);
+                    settle_ties<SCH, PRE>(v, A, B, q, m);
+                }
+#pragma unroll
+                for (int k = 0; k < kPer; ++k) {
+                    if (FACC)
+                        accf[k] = fmaf(copysignf(1.0f, v[k]), m[k], accf[k]);
+                    else
+                        acci[k] += (int)copysignf(m[k], v[k]);
+                }
+            }
+        }
+    }
+}
+
 template <int DT, bool PRE>
+__device__ __forceinline__ void pk16_row(const void *__restrict__ x, int64_t d, int64_t j0,
+                                         bool vec, int64_t i, const uint4 &A, const QParams &q,
+                                         float sigma16, float top16, uint32_t blo, uint32_t bhi,
+                                         uint32_t wi, uint32_t k0, uint32_t k1,
+                                         i16x2 (&acc2)[kPer / 2])
+{
+    static_assert(DT == GQ_IN_BF16, "packed 16-bit sums take bf16 input");
+    // raw bf16 pairs (0 past the end of the row): the sign bits of both
+    // coordinates sit at bits 15 and 31 of each word
+    uint32_t rw[kPer / 2];
+    const uint16_t *row = (const uint16_t *)x + i * d + j0;
+    if (vec) {
+        const uint4 r = *(const uint4 *)row;
+        rw[0] = r.x; rw[1] = r.y; rw[2] = r.z; rw[3] = r.w;
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPer / 2; ++k)
+            rw[k] = ((j0 + 2 * k < d) ? (uint32_t)row[2 * k] : 0u) |
+                    ((j0 + 2 * k + 1 < d) ? (uint32_t)row[2 * k + 1] << 16 : 0u);
+    }
+    float v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer / 2; ++k) {
+        v[2 * k] = __uint_as_float(rw[k] << 16);
+        v[2 * k + 1] = __uint_as_float(rw[k] & 0xFFFF0000u);
+    }
+    const uint32_t Aw[kPer / 2] = {A.x, A.y, A.z, A.w};
+    uint32_t T[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        float a = fabsf(v[k]);
+        if (PRE)
+            a = a * q.pre;
+        T[k] = (uint32_t)fminf(a * sigma16, top16);
+    }
+    // S = T + (0xFFFF - h): its low half is 0xFFFF exactly when h equals
+    // the low half of T (a tie), so the max of the 8 low halves finds any
+    // tie in the group.  As SDWA adds and 16-bit max3 these steps take 8
+    // fewer VALU instructions per worker than the compiler's own lowering
+    // (measured -2.8% on this pass).
+    uint32_t m2[kPer / 2], S[kPer];
+#pragma unroll
+    for (int p = 0; p < kPer / 2; ++p) {
+        const uint32_t hx = ~Aw[p]; // 0xFFFF - h of both coordinates
+        S[2 * p] = add_half16<0>(T[2 * p], hx);
+        S[2 * p + 1] = add_half16<1>(T[2 * p + 1], hx);
+        m2[p] = __builtin_amdgcn_perm(S[2 * p + 1], S[2 * p], 0x07060302u); // high halves
+    }
+    const uint32_t mx = max3_lo16(S[6], S[7], max3_lo16(S[0], S[1], S[2]));
+    const bool tie = ((uint16_t)mx == 0xFFFFu) | ((uint16_t)max3_lo16(S[3], S[4], S[5]) == 0xFFFFu);
+    if (tie) {
+        const uint4 B = philox10(make_uint4(blo, bhi, wi, 1u), k0, k1);
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            if ((S[k] & 0xFFFFu) == 0xFFFFu) { // tie: h == F >> 16
+                float lo, step;
+                uint32_t Fh, F;
+                bracket<GQ_SCHEME_L, PRE>(v[k], q, lo, step, Fh, &F);
+                if (half16(B, k) < (F & 0xFFFFu))
+                    m2[k >> 1] += (k & 1) ? 0x00010000u : 0x00000001u;
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < kPer / 2; ++p) {
+        // +1 / -1 per lane from the sign bits of the two inputs
+        const i16x2 sgn = (as_i16x2(rw[p]) >> (i16x2)15) | (i16x2)1;
+        acc2[p] += as_i16x2(m2[p]) * sgn;
+    }
+}
+
+// SKIP: the zero-code skip of the fused pass (see span_thresholds); then
+// every lane of the wave must be here, `live` marking those with
+// coordinates in the row.
+template <int DT, bool PRE, bool SKIP>
 __device__ __forceinline__ void accumulate_workers_pk16(const void *__restrict__ x, int64_t n,
                                                         int64_t d, int64_t j0, bool vec,
                                                         const QParams &q, uint32_t k0,
                                                         uint32_t k1, int (&acc)[kPer],
-                                                        uint32_t wb = 0)
+                                                        uint32_t wb = 0, bool live = true,
+                                                        const uint16_t *__restrict__ bounds = nullptr,
+                                                        int64_t bstride = 0, int64_t span = 0,
+                                                        bool sparse_ok = false)
 {
     const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
     const float sigma16 = q.sigma * 0x1p16f, top16 = q.top * 0x1p16f;
@@ -1125,70 +1427,24 @@ __device__ __forceinline__ void accumulate_workers_pk16(const void *__restrict__
 #pragma unroll
     for (int p = 0; p < kPer / 2; ++p)
         acc2[p] = as_i16x2(0u);
-    static_assert(DT == GQ_IN_BF16, "packed 16-bit sums take bf16 input");
-    for (int64_t i = 0; i < n; ++i) {
-        // raw bf16 pairs (0 past the end of the row): the sign bits of both
-        // coordinates sit at bits 15 and 31 of each word
-        uint32_t rw[kPer / 2];
-        const uint16_t *row = (const uint16_t *)x + i * d + j0;
-        if (vec) {
-            const uint4 r = *(const uint4 *)row;
-            rw[0] = r.x; rw[1] = r.y; rw[2] = r.z; rw[3] = r.w;
-        } else {
-#pragma unroll
-            for (int k = 0; k < kPer / 2; ++k)
-                rw[k] = ((j0 + 2 * k < d) ? (uint32_t)row[2 * k] : 0u) |
-                        ((j0 + 2 * k + 1 < d) ? (uint32_t)row[2 * k + 1] << 16 : 0u);
-        }
-        float v[kPer];
-#pragma unroll
-        for (int k = 0; k < kPer / 2; ++k) {
-            v[2 * k] = __uint_as_float(rw[k] << 16);
-            v[2 * k + 1] = __uint_as_float(rw[k] & 0xFFFF0000u);
-        }
-        const uint4 A = philox10(make_uint4(blo, bhi, wb + (uint32_t)i, 0u), k0, k1);
-        const uint32_t Aw[kPer / 2] = {A.x, A.y, A.z, A.w};
-        uint32_t T[kPer];
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            float a = fabsf(v[k]);
-            if (PRE)
-                a = a * q.pre;
-            T[k] = (uint32_t)fminf(a * sigma16, top16);
-        }
-        // S = T + (0xFFFF - h): its low half is 0xFFFF exactly when h equals
-        // the low half of T (a tie), so the max of the 8 low halves finds any
-        // tie in the group.  As SDWA adds and 16-bit max3 these steps take 8
-        // fewer VALU instructions per worker than the compiler's own lowering
-        // (measured -2.8% on this pass).
-        uint32_t m2[kPer / 2], S[kPer];
-#pragma unroll
-        for (int p = 0; p < kPer / 2; ++p) {
-            const uint32_t hx = ~Aw[p]; // 0xFFFF - h of both coordinates
-            S[2 * p] = add_half16<0>(T[2 * p], hx);
-            S[2 * p + 1] = add_half16<1>(T[2 * p + 1], hx);
-            m2[p] = __builtin_amdgcn_perm(S[2 * p + 1], S[2 * p], 0x07060302u); // high halves
-        }
-        const uint32_t mx = max3_lo16(S[6], S[7], max3_lo16(S[0], S[1], S[2]));
-        const bool tie = ((uint16_t)mx == 0xFFFFu) | ((uint16_t)max3_lo16(S[3], S[4], S[5]) == 0xFFFFu);
-        if (tie) {
-            const uint4 B = philox10(make_uint4(blo, bhi, wb + (uint32_t)i, 1u), k0, k1);
-#pragma unroll
-            for (int k = 0; k < kPer; ++k) {
-                if ((S[k] & 0xFFFFu) == 0xFFFFu) { // tie: h == F >> 16
-                    float lo, step;
-                    uint32_t Fh, F;
-                    bracket<GQ_SCHEME_L, PRE>(v[k], q, lo, step, Fh, &F);
-                    if (half16(B, k) < (F & 0xFFFFu))
-                        m2[k >> 1] += (k & 1) ? 0x00010000u : 0x00000001u;
-                }
+    if constexpr (SKIP) {
+        for (int64_t c = 0; c < n; c += 64) {
+            const uint32_t Hl = span_threshold<PRE>(bounds, bstride, span, c, n, q, sigma16, sparse_ok);
+            const int cnt = (int)(n - c < 64 ? n - c : 64);
+            for (int r = 0; r < cnt; ++r) {
+                const int64_t i = c + r;
+                const uint32_t H = __builtin_amdgcn_readlane(Hl, r);
+                const uint4 A = philox10(make_uint4(blo, bhi, wb + (uint32_t)i, 0u), k0, k1);
+                if (live && (H > 0xFFFFu || min_half16(A) <= H))
+                    pk16_row<DT, PRE>(x, d, j0, vec, i, A, q, sigma16, top16, blo, bhi,
+                                      wb + (uint32_t)i, k0, k1, acc2);
             }
         }
-#pragma unroll
-        for (int p = 0; p < kPer / 2; ++p) {
-            // +1 / -1 per lane from the sign bits of the two inputs
-            const i16x2 sgn = (as_i16x2(rw[p]) >> (i16x2)15) | (i16x2)1;
-            acc2[p] += as_i16x2(m2[p]) * sgn;
+    } else {
+        for (int64_t i = 0; i < n; ++i) {
+            const uint4 A = philox10(make_uint4(blo, bhi, wb + (uint32_t)i, 0u), k0, k1);
+            pk16_row<DT, PRE>(x, d, j0, vec, i, A, q, sigma16, top16, blo, bhi, wb + (uint32_t)i,
+                              k0, k1, acc2);
         }
     }
 #pragma unroll
@@ -1197,20 +1453,23 @@ __device__ __forceinline__ void accumulate_workers_pk16(const void *__restrict__
         acc[2 * p + 1] = acc2[p].y;
     }
 }
-
-template <int DT, int SCH, int ACC>
+// SKIP: with pass 1's span bounds (u16 [n][bstride]), groups whose codes are
+// provably all 0 are neither loaded nor quantized (the zero-code skip).
+template <int DT, int SCH, int ACC, bool SKIP>
 __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restrict__ x, int64_t n,
                                                             int64_t d, int s, uint64_t seed,
                                                             const float *__restrict__ norm_dev,
                                                             float *__restrict__ mean,
-                                                            uint8_t *__restrict__ code_sum, int W)
+                                                            uint8_t *__restrict__ code_sum, int W,
+                                                            const uint16_t *__restrict__ bounds,
+                                                            int64_t bstride)
 {
     // fp32: 32 KB of LDS caps residency at 5 blocks (20 waves) per CU.
     // Fewer concurrent waves interleave fewer HBM read and write streams:
     // measured -6% on this pass for fp32 at 0.8-16 GB (4 and 5 blocks alike,
     // 6 no gain); bf16, bound by vector ALU work, needs the full residency
     // (5 blocks: +15%).  Only the code-sum packing uses the first 8 KB.
-    __shared__ alignas(16) uint32_t lds[DT == GQ_IN_F32 ? 8192 : kTile];
+    __shared__ alignas(16) uint32_t lds[DT == GQ_IN_F32 && !SKIP ? 8192 : kTile];
     // Reverse of pass 1's order: pass 1's blocks finish on the last chunks of
     // every row, so starting pass 2 there re-reads data the memory-side cache
     // still holds (measured: -7% time on an 0.8 GB input, neutral on 7-16 GB).
@@ -1219,14 +1478,42 @@ __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restri
     const QParams q = make_qparams(*norm_dev, n, s, SCH);
     float accf[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
     int acc[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (!q.zero && j0 < d) {
+    if constexpr (SKIP) {
+        // one span per wave; the whole wave enters when its span starts
+        // inside the row
+        const int64_t span = tile * (kTile / kSpan) + (int64_t)(threadIdx.x >> 6);
+        if (!q.zero && span * kSpan < d) {
+            const bool vec = (d & 7) == 0, live = j0 < d;
+            const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+            const float sigK = q.sigma * (SCH == GQ_SCHEME_L ? 0x1p16f : q.p2E16);
+            const bool sparse_ok = sigK < INFINITY; // false for NaN too
+            if constexpr (ACC == kAccPk16) {
+                if (q.prescale)
+                    accumulate_workers_pk16<DT, true, true>(x, n, d, j0, vec, q, k0, k1, acc, 0u,
+                                                            live, bounds, bstride, span, sparse_ok);
+                else
+                    accumulate_workers_pk16<DT, false, true>(x, n, d, j0, vec, q, k0, k1, acc, 0u,
+                                                             live, bounds, bstride, span, sparse_ok);
+            } else if (q.prescale)
+                accumulate_workers_skip<DT, SCH, true, ACC == kAccF32>(
+                    x, n, d, j0, vec, live, q, k0, k1, bounds, bstride, span, sigK, sparse_ok, accf, acc);
+            else
+                accumulate_workers_skip<DT, SCH, false, ACC == kAccF32>(
+                    x, n, d, j0, vec, live, q, k0, k1, bounds, bstride, span, sigK, sparse_ok, accf, acc);
+            if (ACC == kAccF32) {
+#pragma unroll
+                for (int k = 0; k < kPer; ++k)
+                    acc[k] = (int)accf[k];
+            }
+        }
+    } else if (!q.zero && j0 < d) {
         const bool vec = (d & 7) == 0;
         const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
         if constexpr (ACC == kAccPk16) {
             if (q.prescale)
-                accumulate_workers_pk16<DT, true>(x, n, d, j0, vec, q, k0, k1, acc);
+                accumulate_workers_pk16<DT, true, false>(x, n, d, j0, vec, q, k0, k1, acc);
             else
-                accumulate_workers_pk16<DT, false>(x, n, d, j0, vec, q, k0, k1, acc);
+                accumulate_workers_pk16<DT, false, false>(x, n, d, j0, vec, q, k0, k1, acc);
         } else if (q.prescale)
             accumulate_workers<DT, SCH, true, ACC == kAccF32>(x, n, d, j0, vec, q, k0, k1, accf, acc);
         else
@@ -1618,10 +1905,10 @@ __global__ __launch_bounds__(kThreads) void k_quantize_words(const void *__restr
                     const void *xrow = (const uint16_t *)x + i * d;
                     const uint32_t wk = (uint32_t)(worker_base + i);
                     if (q.prescale)
-                        accumulate_workers_pk16<DT, true>(xrow, 1, d, j0, vec, q, (uint32_t)seed,
+                        accumulate_workers_pk16<DT, true, false>(xrow, 1, d, j0, vec, q, (uint32_t)seed,
                                                           (uint32_t)(seed >> 32), code, wk);
                     else
-                        accumulate_workers_pk16<DT, false>(xrow, 1, d, j0, vec, q, (uint32_t)seed,
+                        accumulate_workers_pk16<DT, false, false>(xrow, 1, d, j0, vec, q, (uint32_t)seed,
                                                            (uint32_t)(seed >> 32), code, wk);
                 } else {
                     float v[kPer];
@@ -1739,9 +2026,9 @@ __global__ __launch_bounds__(kThreads) void k_compress_words(const void *__restr
         if (!q.zero && j0 < d) {
             if constexpr (ACC == kAccPk16) {
                 if (q.prescale)
-                    accumulate_workers_pk16<DT, true>(x, n, d, j0, vec, q, k0, k1, acc, wb);
+                    accumulate_workers_pk16<DT, true, false>(x, n, d, j0, vec, q, k0, k1, acc, wb);
                 else
-                    accumulate_workers_pk16<DT, false>(x, n, d, j0, vec, q, k0, k1, acc, wb);
+                    accumulate_workers_pk16<DT, false, false>(x, n, d, j0, vec, q, k0, k1, acc, wb);
             } else {
                 float accf[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
                 if (q.prescale)
@@ -2436,10 +2723,13 @@ int32_t validate_ws(const void *ws, int64_t ws_bytes, int64_t n, int64_t d)
     } while (0)
 
 // Enqueue pass 1 (partials + finalize).  Arguments already validated.
+// bounds: if not NULL, pass 1 also stores the span bounds there (u16
+// [n][bound_stride(d)]) for the zero-code skip of the fused pass.
 int32_t launch_norm(const void *x, int32_t dtype, int64_t n, int64_t d, float q, float p,
                     bool local, float *norm_out, void *ws, int s, hipStream_t st,
-                    double *term_out = nullptr)
+                    double *term_out = nullptr, uint16_t *bounds = nullptr)
 {
+    const int64_t bstride = bound_stride(d);
     const NormGeom g = norm_geom(n, d);
     const OneShotGeom o = oneshot_geom(n, d, dtype == GQ_IN_F32 ? 4 : 2);
     const WsLayout L = ws_layout(n, d);
@@ -2458,7 +2748,7 @@ int32_t launch_norm(const void *x, int32_t dtype, int64_t n, int64_t d, float q,
             return fail(GQ_ERR_UNSUPPORTED, "norm grid too large");
         const dim3 grid((unsigned)(n * o.bpr)), block(kOsThreads);
 #define GQ_ONESHOT(DT, QM) \
-    k_norm_oneshot<DT, QM><<<grid, block, 0, st>>>(x, d, o.bpr, o.span, qd, partials)
+    k_norm_oneshot<DT, QM><<<grid, block, 0, st>>>(x, d, o.bpr, o.span, qd, partials, bounds, bstride)
         if (dtype == GQ_IN_F32) {
             if (qm == 0) GQ_ONESHOT(GQ_IN_F32, 0); else if (qm == 1) GQ_ONESHOT(GQ_IN_F32, 1); else GQ_ONESHOT(GQ_IN_F32, 2);
         } else {
@@ -2479,7 +2769,8 @@ int32_t launch_norm(const void *x, int32_t dtype, int64_t n, int64_t d, float q,
             return fail(GQ_ERR_UNSUPPORTED, "norm grid too large");
         const dim3 grid((unsigned)g.blocks), block(kThreads);
 #define GQ_PARTIAL(DT, QM) \
-    k_norm_partial<DT, QM><<<grid, block, 0, st>>>(x, n, d, g.chunks, g.chunk_len, qd, partials)
+    k_norm_partial<DT, QM><<<grid, block, 0, st>>>(x, n, d, g.chunks, g.chunk_len, qd, partials, \
+                                                   bounds, bstride)
         if (dtype == GQ_IN_F32) {
             if (qm == 0) GQ_PARTIAL(GQ_IN_F32, 0); else if (qm == 1) GQ_PARTIAL(GQ_IN_F32, 1); else GQ_PARTIAL(GQ_IN_F32, 2);
         } else {
@@ -2551,10 +2842,13 @@ int32_t launch_sums8(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t
     return check_launch(mean ? "k_dequantize_sums8" : "k_compress_sums8");
 }
 
+// bounds: pass 1's span bounds for the zero-code skip, or NULL.
 int32_t launch_compress(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
                         int32_t scheme, uint64_t seed, const float *norm_dev, int32_t W,
-                        float *mean, void *code_sum, hipStream_t st, uint8_t *sums8 = nullptr)
+                        float *mean, void *code_sum, hipStream_t st,
+                        const uint16_t *bounds = nullptr)
 {
+    const int64_t bstride = bound_stride(d);
     const int64_t tiles = (d + kTile - 1) / kTile;
     if (tiles == 0)
         return ok();
@@ -2564,20 +2858,28 @@ int32_t launch_compress(const void *x, int32_t dtype, int64_t n, int64_t d, int3
     // packed int16 sums for bf16 standard dithering while n s < 2^15
     const int64_t nm = n * top_code(s, scheme);
     const bool facc = nm <= ((int64_t)1 << 24);
-    if (sums8 && !code_sum && dtype == GQ_IN_F32 && n >= kSums8MinN) {
-        // many workers: 1-byte sums from the pass, the mean from a second kernel
-        GQ_TRY(launch_sums8(x, dtype, n, d, s, scheme, seed, norm_dev, sums8, nullptr, st));
-        return launch_sums8(x, dtype, n, d, s, scheme, seed, norm_dev, sums8, mean, st);
-    }
     const bool pk16 = dtype == GQ_IN_BF16 && scheme == GQ_SCHEME_L && nm < ((int64_t)1 << 15);
-#define GQ_COMPRESS(DT, SCH, ACC) \
-    k_compress_mean<DT, SCH, ACC><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, mean, cs, W)
-#define GQ_COMPRESS_DT(DT)                                                                      \
-    do {                                                                                        \
-        if (scheme == GQ_SCHEME_L)                                                              \
-            facc ? GQ_COMPRESS(DT, GQ_SCHEME_L, kAccF32) : GQ_COMPRESS(DT, GQ_SCHEME_L, kAccInt); \
-        else                                                                                    \
-            facc ? GQ_COMPRESS(DT, GQ_SCHEME_E, kAccF32) : GQ_COMPRESS(DT, GQ_SCHEME_E, kAccInt); \
+#define GQ_COMPRESS(DT, SCH, ACC)                                                                 \
+    do {                                                                                          \
+        if (bounds)                                                                               \
+            k_compress_mean<DT, SCH, ACC, true><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, \
+                                                                        mean, cs, W, bounds, bstride); \
+        else                                                                                      \
+            k_compress_mean<DT, SCH, ACC, false><<<grid, block, 0, st>>>(x, n, d, s, seed,         \
+                                                                         norm_dev, mean, cs, W,   \
+                                                                         nullptr, 0);             \
+    } while (0)
+#define GQ_COMPRESS_DT(DT)                          \
+    do {                                            \
+        if (scheme == GQ_SCHEME_L) {                \
+            if (facc)                               \
+                GQ_COMPRESS(DT, GQ_SCHEME_L, kAccF32); \
+            else                                    \
+                GQ_COMPRESS(DT, GQ_SCHEME_L, kAccInt); \
+        } else if (facc)                            \
+            GQ_COMPRESS(DT, GQ_SCHEME_E, kAccF32);  \
+        else                                        \
+            GQ_COMPRESS(DT, GQ_SCHEME_E, kAccInt);  \
     } while (0)
     if (dtype == GQ_IN_F32)
         GQ_COMPRESS_DT(GQ_IN_F32);
@@ -3052,6 +3354,53 @@ int32_t gq_compress_mean_from_norm(const void *x, int32_t dtype, int64_t n, int6
                            code_sum_or_null, (hipStream_t)stream);
 }
 
+int64_t gq_span_bounds_bytes(int64_t n, int64_t d)
+{
+    if (n < 1 || d < 0 || d > INT64_MAX / 4 / n)
+        return -1;
+    return 2 * n * bound_stride(d);
+}
+
+int32_t gq_global_norm_bounds(const void *x, int32_t dtype, int64_t n, int64_t d, float q,
+                              float p, float *norm_dev, uint16_t *bounds, void *workspace,
+                              int64_t workspace_bytes, void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    if (!norm_dev || (!bounds && d > 0))
+        return fail(GQ_ERR_NULL, "norm_dev or bounds is NULL");
+    if (!order_ok(q) || !order_ok(p))
+        return fail(GQ_ERR_UNSUPPORTED, "q and p must be reals >= 1 or +inf");
+    if (!aligned16(bounds))
+        return fail(GQ_ERR_ALIGN, "bounds is not 16-byte aligned");
+    GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
+    return launch_norm(x, dtype, n, d, q, p, false, norm_dev, workspace, 0, (hipStream_t)stream,
+                       nullptr, d > 0 ? bounds : nullptr);
+}
+
+int32_t gq_compress_mean_skip(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                              int32_t scheme, uint64_t seed, const float *norm_dev,
+                              const uint16_t *bounds, int32_t code_bits, float *mean,
+                              void *code_sum_or_null, void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    GQ_TRY(validate_scheme(s, scheme));
+    if (!norm_dev || ((!mean || !bounds) && d > 0))
+        return fail(GQ_ERR_NULL, "norm_dev, bounds or mean is NULL");
+    if (!aligned16(bounds))
+        return fail(GQ_ERR_ALIGN, "bounds is not 16-byte aligned");
+    if (min_bits(n, s, scheme) > 32)
+        return fail(GQ_ERR_CODE_WIDTH, "sums of %lld codes do not fit 32 bits", (long long)n);
+    if (code_sum_or_null) {
+        GQ_TRY(validate_width(n, s, scheme, code_bits));
+        if (!aligned16(code_sum_or_null))
+            return fail(GQ_ERR_ALIGN, "code_sum is not 16-byte aligned");
+    }
+    if (!aligned16(mean))
+        return fail(GQ_ERR_ALIGN, "mean is not 16-byte aligned");
+    return launch_compress(x, dtype, n, d, s, scheme, seed, norm_dev, code_bits, mean,
+                           code_sum_or_null, (hipStream_t)stream, d > 0 ? bounds : nullptr);
+}
+
 int32_t gq_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s, float q,
                          float p, int32_t scheme, uint64_t seed, int32_t code_bits, float *mean,
                          float *norm_dev, void *code_sum_or_null, void *workspace,
@@ -3074,13 +3423,14 @@ int32_t gq_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int
         return fail(GQ_ERR_ALIGN, "mean is not 16-byte aligned");
     GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
     hipStream_t st = (hipStream_t)stream;
-    GQ_TRY(launch_norm(x, dtype, n, d, q, p, false, norm_dev, workspace, 0, st));
     const WsLayout L = ws_layout(n, d);
-    uint8_t *sums8 = (L.total_compress > L.total && workspace_bytes >= L.total_compress)
-                         ? (uint8_t *)((char *)workspace + L.sums8)
-                         : nullptr;
+    // with room for the span bounds, the fused pass skips provably zero codes
+    uint16_t *bounds = (L.total_compress > L.total && workspace_bytes >= L.total_compress)
+                           ? (uint16_t *)((char *)workspace + L.bounds)
+                           : nullptr;
+    GQ_TRY(launch_norm(x, dtype, n, d, q, p, false, norm_dev, workspace, 0, st, nullptr, bounds));
     return launch_compress(x, dtype, n, d, s, scheme, seed, norm_dev, code_bits, mean,
-                           code_sum_or_null, st, sums8);
+                           code_sum_or_null, st, bounds);
 }
 
 int32_t gq_compress_sums8(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
@@ -3135,7 +3485,8 @@ int32_t gq_compress_mean_noalloc(const void *x, int32_t dtype, int64_t n, int64_
     }
     if (!aligned16(mean))
         return fail(GQ_ERR_ALIGN, "mean is not 16-byte aligned");
-    const int64_t need = ws_layout(n, d).total;
+    const WsLayout L = ws_layout(n, d);
+    const int64_t need = L.total;
     if (need > GQ_NOALLOC_SCRATCH_BYTES)
         return fail(GQ_ERR_WORKSPACE,
                     "n = %lld, d = %lld needs %lld bytes of scratch, beyond the %lld the "
@@ -3145,9 +3496,13 @@ int32_t gq_compress_mean_noalloc(const void *x, int32_t dtype, int64_t n, int64_
     hipStream_t st = (hipStream_t)stream;
     void *ws = nullptr;
     GQ_TRY(noalloc_scratch(st, &ws));
-    GQ_TRY(launch_norm(x, dtype, n, d, q, p, false, norm_dev, ws, 0, st));
+    // the span bounds when they fit as well (the zero-code skip), else none
+    uint16_t *bounds = (L.total_compress > L.total && L.total_compress <= GQ_NOALLOC_SCRATCH_BYTES)
+                           ? (uint16_t *)((char *)ws + L.bounds)
+                           : nullptr;
+    GQ_TRY(launch_norm(x, dtype, n, d, q, p, false, norm_dev, ws, 0, st, nullptr, bounds));
     return launch_compress(x, dtype, n, d, s, scheme, seed, norm_dev, code_bits, mean,
-                           code_sum_or_null, st);
+                           code_sum_or_null, st, bounds);
 }
 
 int32_t gq_qsgd_local_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,

@@ -10,9 +10,11 @@ workloads (ResNet-50-, BERT-base- and GPT-2-medium-sized buckets) are timed
 in the same run and reported under "configs".
 
 Prints one JSON line.  `value` is input GB/s (n d bytes-per-element / step
-time); `roofline` describes the dominant kernel (k_compress_mean, or for
-many fp32 workers k_compress_sums8, the pass that stages 1-byte sums) timed
-per launch with HIP events on the stream it runs on; `read_ceiling` is the best
+time); `roofline` describes the dominant kernel (pass 1, which reads x
+whole: k_norm_oneshot or k_norm_partial) timed per launch with HIP events on
+the stream it runs on, and `compress_step` the fused pass with the zero-code
+skip (bound by the vector ALU: Philox for every worker and group) beside the
+same pass reading every coordinate; `read_ceiling` is the best
 plain stream read of the same input (libgq_probe.so), `valu_ceiling` the
 measured issue rate of the instruction kinds the VALU-heavy kernels use;
 `e8_omega` the byte rate of the pages' 8-bit custom reduction against an
@@ -33,7 +35,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
-DOMINANT = "k_compress_mean"
 
 
 def parse():
@@ -400,6 +401,31 @@ def workload_config(w, wmin):
             "min_code_bits": wmin, "values": w.values}
 
 
+def norm_pass_kernel(w):
+    """The kernel that reads x in pass 1: one-shot 16 KB blocks for fp32 inputs
+    above 1 GiB, chunk-major blocks otherwise."""
+    big = w.dtype == "f32" and w.n * w.d * 4 > (1 << 30)
+    return "k_norm_oneshot" if big else "k_norm_partial"
+
+
+# Vector ALU issue ceiling (wave64 VOP3 instructions per CU per clock, probe
+# kernels in libgq_probe.so) times 256 CUs x 64 lanes x 2.4 GHz
+VALU_LANE_OPS = 0.969 * 256 * 64 * 2.4e9
+
+
+def skip_alu_roofline(w, k_ms):
+    """The fused pass with the zero-code skip is bound by the vector ALU: every
+    (worker, 8-coordinate group) needs its Philox4x32-10 block whether or not
+    its codes are 0.  Algorithmic work: 40 lane-instructions per block (10
+    rounds of two 32x32->64 products and two three-input xors) against the
+    measured issue ceiling."""
+    blocks = w.n * -(-w.d // 8)
+    achieved = 40 * blocks / (k_ms * 1e-3)
+    return {"bound": "alu", "achieved": round(achieved / 1e12, 3), "peak": round(VALU_LANE_OPS / 1e12, 3),
+            "unit": "T lane-instr/s (Philox only)", "frac": round(achieved / VALU_LANE_OPS, 4),
+            "kernel": "k_compress_mean (zero-code skip)"}
+
+
 def time_workload(gq, np, torch, w, xd, stream, steps, warmup, full):
     """The whole step (norm pass + fused pass) over `steps` back-to-back calls,
     then each pass alone with one HIP event pair per launch on the stream it
@@ -408,10 +434,9 @@ def time_workload(gq, np, torch, w, xd, stream, steps, warmup, full):
     dev = xd.device
     mean = torch.empty(d, dtype=torch.float32, device=dev)
     norm = torch.empty(1, dtype=torch.float32, device=dev)
-    # the workspace with which gq_compress_mean is fastest (for many fp32
-    # workers it stages 1-byte sums between two kernels)
+    # the workspace with which gq_compress_mean is fastest (room for the span
+    # bounds of the zero-code skip)
     ws = torch.empty(gq.gq_compress_workspace_bytes(n, d), dtype=torch.uint8, device=dev)
-    staged = w.dtype == "f32" and gq.gq_compress_workspace_bytes(n, d) > gq.gq_workspace_bytes(n, d)
 
     def step():
         gq.gq_compress_mean(xd, w.s, w.q, w.p, w.scheme, w.seed, mean=mean, norm=norm,
@@ -456,65 +481,64 @@ def time_workload(gq, np, torch, w, xd, stream, steps, warmup, full):
         out["cold_cache"] = {"ms_per_step": round(cold_ms, 6),
                              "input_GBs": round(in_bytes / (cold_ms * 1e-3) / 1e9, 3),
                              "steps": len(cpairs), "stat": "median"}
-    # each kernel of the step alone, one event pair per launch on the same stream
-    npairs, kpairs, qpairs = (event_pairs(torch, steps) for _ in range(3))
-    sums8 = (torch.empty(gq.gq_sums8_bytes(d), dtype=torch.uint8, device=dev) if staged
-             else None)
+    # each pass of the step alone, one event pair per launch on the stream it
+    # runs on: pass 1 (the norm, and the span bounds in the same read) and the
+    # fused pass with the zero-code skip -- the two halves gq_compress_mean
+    # runs with this workspace -- and, for comparison, the fused pass reading
+    # every coordinate (gq_compress_mean_from_norm)
+    bounds = torch.empty(gq.gq_span_bounds_bytes(n, d), dtype=torch.uint8, device=dev)
+    npairs, kpairs = event_pairs(torch, steps), event_pairs(torch, steps)
     for i in range(steps):
         npairs[i][0].record(stream)
-        gq.gq_global_norm(xd, w.q, w.p, norm=norm, workspace=ws, stream=stream)
+        gq.gq_global_norm_bounds(xd, w.q, w.p, norm=norm, bounds=bounds, workspace=ws,
+                                 stream=stream)
         npairs[i][1].record(stream)
         kpairs[i][0].record(stream)
-        if staged:
-            gq.gq_compress_sums8(xd, w.s, w.scheme, w.seed, norm, sums8=sums8, stream=stream)
-            kpairs[i][1].record(stream)
-            qpairs[i][0].record(stream)
-            gq.gq_dequantize_sums8(xd, w.s, w.scheme, w.seed, norm, sums8, mean=mean,
-                                   stream=stream)
-            qpairs[i][1].record(stream)
-        else:
-            gq.gq_compress_mean_from_norm(xd, w.s, w.scheme, w.seed, norm, mean=mean,
-                                          stream=stream)
-            kpairs[i][1].record(stream)
+        gq.gq_compress_mean_skip(xd, w.s, w.scheme, w.seed, norm, bounds, mean=mean,
+                                 stream=stream)
+        kpairs[i][1].record(stream)
+    dpairs = event_pairs(torch, min(steps, 10))
+    dense_mean = torch.empty_like(mean)
+    for a, b in dpairs:
+        a.record(stream)
+        gq.gq_compress_mean_from_norm(xd, w.s, w.scheme, w.seed, norm, mean=dense_mean,
+                                      stream=stream)
+        b.record(stream)
     torch.cuda.synchronize()
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in kpairs]))
+    if not torch.equal(dense_mean.view(torch.int32), mean.view(torch.int32)):
+        raise RuntimeError("the fused pass with and without the zero-code skip disagree")
+    del dense_mean
     n_ms = float(np.mean([a.elapsed_time(b) for a, b in npairs]))
-    q_ms = float(np.mean([a.elapsed_time(b) for a, b in qpairs])) if staged else 0.0
-    kernel = "k_compress_sums8" if staged else DOMINANT
-    # algorithmic bytes of the dominant kernel: one read of x, and what it
-    # writes: the fp32 mean, or (staged) the group mask and the 8 bytes of
-    # each marked group (the groups holding a non-zero sum, counted here)
-    if staged:
-        mask, _ = gq.sums8_parts(sums8, d)
-        bits = torch.tensor([bin(v).count("1") for v in range(256)], dtype=torch.int64,
-                            device=dev)
-        marked = int(bits[mask.view(torch.uint8).long()].sum())
-        k_alg = in_bytes + 8 * (-(-d // 512)) + 8 * marked
-    else:
-        marked = None
-        k_alg = in_bytes + 4 * d
-    fused_alg = 2 * in_bytes + 4 * d              # both passes of the whole step
-    achieved = k_alg / (k_ms * 1e-3) / 1e9
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in kpairs]))
+    dense_ms = float(np.mean([a.elapsed_time(b) for a, b in dpairs]))
+    norm_kernel = norm_pass_kernel(w)
+    # pass 1 is the dominant kernel: algorithmic bytes = one read of x and the
+    # span bounds it writes
+    b_bytes = gq.gq_span_bounds_bytes(n, d)
+    n_alg = in_bytes + b_bytes
+    fused_alg = 2 * in_bytes + 4 * d              # both passes of the whole step (8d)
     traffic = traffic_for(w.name)
+    if n_ms >= k_ms:
+        achieved = n_alg / (n_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic, "kernel": norm_kernel, "alg_bytes_per_launch": n_alg,
+                    "traffic_over_alg": round(traffic / n_alg, 4) if traffic else None}
+    else:
+        roofline = skip_alu_roofline(w, k_ms)
     out.update({
         "ms_per_step": round(ms, 6),
         "input_GBs": round(in_bytes / (ms * 1e-3) / 1e9, 3),
+        # the 8d roofline fraction: two reads of x and the fp32 mean over the
+        # step time; the skip re-reads only the groups that may hold a
+        # non-zero code, so this counts bytes the step no longer moves
         "hbm_frac_fused": round(fused_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "kernels_ms": ({"norm_pass": round(n_ms, 6), kernel: round(k_ms, 6),
-                        "k_dequantize_sums8": round(q_ms, 6)} if staged else
-                       {"norm_pass": round(n_ms, 6), kernel: round(k_ms, 6)}),
-        # the whole compress step after the norm (both kernels when staged):
-        # one read of x and the fp32 mean written
-        "compress_step": {"ms": round(k_ms + q_ms, 6),
-                          "frac": round((in_bytes + 4 * d) / ((k_ms + q_ms) * 1e-3) / 1e9
-                                        / HBM_PEAK_GBS, 4),
-                          "staged_sums8": staged,
-                          "nonzero_group_share": (round(marked / -(-d // 8), 5) if staged
-                                                  else None)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": kernel, "alg_bytes_per_launch": k_alg,
-                     "traffic_over_alg": round(traffic / k_alg, 4) if traffic else None},
+        "kernels_ms": {"norm_pass": round(n_ms, 6), "k_compress_mean (zero-code skip)":
+                       round(k_ms, 6)},
+        "compress_step": {"ms": round(k_ms, 6), "ms_reading_every_coordinate": round(dense_ms, 6),
+                          "speedup_of_skip": round(dense_ms / k_ms, 3),
+                          "alu": skip_alu_roofline(w, k_ms)},
+        "roofline": roofline,
         "_mean": mean, "_norm": norm, "_ws": ws,
     })
     return out
@@ -677,7 +701,8 @@ def main():
             rc["GBs"], rc["shape"] = round(norm_gbs, 1), "the norm pass (read-only)"
             rc["frac_of_8TBs"] = round(norm_gbs / HBM_PEAK_GBS, 4)
         out["read_ceiling"] = rc
-        out["roofline"]["frac_of_read_ceiling"] = round(out["roofline"]["achieved"] / rc["GBs"], 4)
+        if out["roofline"]["bound"] == "hbm":
+            out["roofline"]["frac_of_read_ceiling"] = round(out["roofline"]["achieved"] / rc["GBs"], 4)
         out["frac_of_read_ceiling_fused"] = round(
             (2 * in_bytes + 4 * d) / (ms * 1e-3) / 1e9 / rc["GBs"], 4)
     if args.unfused:

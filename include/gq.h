@@ -93,16 +93,11 @@ int64_t gq_code_row_bytes(int64_t d, int32_t code_bits);
 int64_t gq_workspace_bytes(int64_t n, int64_t d);
 
 /* Workspace with which gq_compress_mean runs fastest: gq_workspace_bytes
- * plus, for n >= 32 workers, gq_sums8_bytes(d) (rounded up to 256), where
- * an fp32 input's fused pass stages its sums for a separate dequantization
- * kernel: a bit per group of 8 coordinates, and 1-byte sums of the groups
- * that are not all zero (an exact sum in [-127, 127], else an escape byte
- * whose group the next kernel recomputes from x).  With n workers streamed
- * per coordinate, writing inside the pass costs several times its bytes;
- * writing almost nothing there and the mean afterwards is faster.  The
- * results are the same bits either way; a workspace of only
- * gq_workspace_bytes(n, d) bytes runs the single fused pass.  Returns -1
- * for invalid sizes.                                                       */
+ * plus gq_span_bounds_bytes(n, d) rounded up to 256, where the norm pass
+ * leaves the span bounds of the zero-code skip (see gq_global_norm_bounds).
+ * The results are the same bits either way; with only
+ * gq_workspace_bytes(n, d) bytes the fused pass reads every coordinate.
+ * Returns -1 for invalid sizes.                                            */
 int64_t gq_compress_workspace_bytes(int64_t n, int64_t d);
 
 /* Global (q,p)-norm of the concatenation (Sec. 2 notation):
@@ -232,17 +227,56 @@ int32_t gq_compress_mean_from_norm(const void *x, int32_t dtype, int64_t n, int6
                                    int32_t code_bits, float *mean, void *code_sum_or_null,
                                    void *stream);
 
+/* The zero-code skip: the same results as gq_global_norm followed by
+ * gq_compress_mean_from_norm, bit for bit, without reading most of x a
+ * second time.  The fused pass stochastically rounds t = |x| / N (times s
+ * for L) onto the levels of Sec. 3 ("Global-QSGD: Practical Floatless
+ * Quantization ...", Global-L_s and Global-E_s); where t is below the first
+ * non-zero level the code is 1 with probability F / 2^32 and 0 otherwise,
+ * decided by the 16-bit uniform h (and the second draw on a tie).  With one
+ * norm over a long concatenation most t are tiny, so most codes are 0, and
+ * h alone proves it: a coordinate whose h exceeds a bound on its F >> 16
+ * rounds to 0 whatever its exact value.
+ *   gq_span_bounds_bytes(n, d) = 2 n stride, stride = 16 ceil(d / 8192):
+ *     one 16-bit bound per (row, span of 512 coordinates), row-major with
+ *     rows stride entries apart (-1 for invalid sizes).
+ *   gq_global_norm_bounds: gq_global_norm (same N, same workspace rule),
+ *     and in the same pass over x, bounds[i * stride + k] = the smallest
+ *     bf16 bit pattern whose value is >= |x_ij| for every j of span k of row
+ *     i (patterns 0x7F80 and above: an inf or NaN there), for every
+ *     k < ceil(d / 512); the entries past them may be written too.
+ *     bounds: device, 16-byte aligned, caller-owned.
+ *   gq_compress_mean_skip: gq_compress_mean_from_norm (same arguments and
+ *     results) given N in norm_dev[0] and those bounds for this x.  Per
+ *     span and worker it derives a threshold H from the bound and N; a
+ *     group of 8 coordinates whose eight 16-bit uniforms all exceed H adds
+ *     nothing to the sums and is not loaded.  A span whose bound allows a
+ *     non-zero lower level (t >= 1 for L, t >= 2^(1-s) for E), an inf or
+ *     NaN, is read whole.  Bounds that do not belong to this x make the
+ *     results wrong; they are not checked.
+ * Errors as gq_global_norm and gq_compress_mean_from_norm, plus
+ * GQ_ERR_NULL for a NULL bounds and GQ_ERR_ALIGN for one not 16-byte
+ * aligned.                                                                 */
+int64_t gq_span_bounds_bytes(int64_t n, int64_t d);
+int32_t gq_global_norm_bounds(const void *x, int32_t dtype, int64_t n, int64_t d, float q,
+                              float p, float *norm_dev, uint16_t *bounds, void *workspace,
+                              int64_t workspace_bytes, void *stream);
+int32_t gq_compress_mean_skip(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                              int32_t scheme, uint64_t seed, const float *norm_dev,
+                              const uint16_t *bounds, int32_t code_bits, float *mean,
+                              void *code_sum_or_null, void *stream);
+
 /* The whole path: gq_global_norm, then gq_compress_mean_from_norm.
  * Writes N to norm_dev[0] and the dequantized mean to mean[0..d).  With a
- * workspace of gq_compress_workspace_bytes(n, d), n >= 32, fp32 input and
- * no code sums requested, the compress step runs as two kernels through
- * sums staged in the workspace (gq_compress_sums8; same results, faster).  */
+ * workspace of gq_compress_workspace_bytes(n, d) it runs as
+ * gq_global_norm_bounds then gq_compress_mean_skip, the bounds in the
+ * workspace (same results, faster: provably zero codes are skipped).      */
 int32_t gq_compress_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s, float q,
                          float p, int32_t scheme, uint64_t seed, int32_t code_bits, float *mean,
                          float *norm_dev, void *code_sum_or_null, void *workspace,
                          int64_t workspace_bytes, void *stream);
 
-/* The two kernels of gq_compress_mean's staged compress step (many
+/* The compress step as two kernels with the sums staged in between (many
  * workers; the fused pass itself, split where its only write would be).
  * Staging buffer `sums8`, gq_sums8_bytes(d) bytes, 16-byte aligned: first a
  * mask of one bit per group of 8 coordinates (group g is bit g % 64 of the
@@ -273,10 +307,11 @@ int32_t gq_dequantize_sums8(const void *x, int32_t dtype, int64_t n, int64_t d, 
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, results and errors as
  * gq_compress_mean, bit for bit, except that the norm pass keeps its
- * partial sums in a library-owned device array of GQ_NOALLOC_SCRATCH_BYTES
- * (16 MiB) instead of a workspace; every GPU the library runs on holds its
- * own copy of that array until the process ends.  The call allocates
- * nothing (no hipMalloc, no allocating library routine).
+ * partial sums (and, when gq_compress_workspace_bytes(n, d) fits too, the
+ * span bounds of the zero-code skip) in a library-owned device array of
+ * GQ_NOALLOC_SCRATCH_BYTES (16 MiB) instead of a workspace; every GPU the
+ * library runs on holds its own copy of that array until the process ends.
+ * The call allocates nothing (no hipMalloc, no allocating library routine).
  *   - Size limit: inputs with gq_workspace_bytes(n, d) >
  *     GQ_NOALLOC_SCRATCH_BYTES are rejected with GQ_ERR_WORKSPACE before
  *     any HIP call (fp32 inputs up to about 32 GiB fit; the per-worker

@@ -152,16 +152,41 @@ def test_staged_sums_entry_points_reject():
     assert L.gq_dequantize_sums8(A, 0, 4, 100, 7, 0, 1, A, NUL, A, NUL) == 1
     assert L.gq_dequantize_sums8(A, 0, 4, 100, 7, 0, 1, A, A, U, NUL) == 6
     # the staging buffer: a bit per 8-coordinate group in 64-bit words, then a
-    # byte per coordinate, each part 16-byte aligned; in the workspace from 32
-    # workers on, 256-byte aligned
+    # byte per coordinate, each part 16-byte aligned
     for d in (0, 1, 8, 511, 512, 513, 64_000_000):
         mask = (-(-d // 512) * 8 + 15) // 16 * 16
         assert gq.gq_sums8_bytes(d) == mask + -(-d // 16) * 16
     assert gq.gq_sums8_bytes(-1) == -1
-    for n, d in ((31, 1000), (32, 1000), (64, 64_000_000)):
+
+
+def test_zero_code_skip_sizes_and_rejects():
+    """The span bounds: one 16-bit entry per (row, 512 coordinates), rows
+    padded to a multiple of 16 entries; the compress workspace is the
+    norm's plus the bounds rounded up to 256."""
+    L = gq.lib()
+    for n, d in ((1, 0), (1, 1), (3, 511), (3, 512), (3, 513), (64, 64_000_000),
+                 (8, 355_000_000)):
+        assert gq.gq_span_bounds_bytes(n, d) == 2 * n * -(-d // 8192) * 16
         extra = gq.gq_compress_workspace_bytes(n, d) - gq.gq_workspace_bytes(n, d)
-        assert extra == (0 if n < 32 else -(-gq.gq_sums8_bytes(d) // 256) * 256)
+        assert extra == -(-gq.gq_span_bounds_bytes(n, d) // 256) * 256
+    assert gq.gq_span_bounds_bytes(0, 5) == -1 and gq.gq_span_bounds_bytes(2, -1) == -1
     assert gq.gq_compress_workspace_bytes(0, 5) == -1
+    ws = gq.gq_workspace_bytes(4, 100)
+    B = ctypes.c_void_p(1 << 20)  # an aligned address (never dereferenced: rejected first)
+    # gq_global_norm_bounds(x, dtype, n, d, q, p, norm, bounds, ws, ws_bytes, stream)
+    assert L.gq_global_norm_bounds(NUL, 0, 4, 100, 2.0, 2.0, A, B, A, ws, NUL) == 1
+    assert L.gq_global_norm_bounds(A, 0, 4, 100, 2.0, 2.0, A, NUL, A, ws, NUL) == 1
+    assert L.gq_global_norm_bounds(A, 0, 4, 100, 2.0, 2.0, A, ctypes.c_void_p((1 << 20) + 2), A, ws,
+                                   NUL) == 6
+    assert L.gq_global_norm_bounds(A, 0, 4, 100, 2.0, 0.5, A, B, A, ws, NUL) == 3
+    assert L.gq_global_norm_bounds(A, 0, 4, 100, 2.0, 2.0, A, B, A, ws - 1, NUL) == 5
+    # gq_compress_mean_skip(x, dtype, n, d, s, scheme, seed, norm, bounds, W, mean, code_sum, stream)
+    assert L.gq_compress_mean_skip(A, 0, 4, 100, 7, 0, 1, A, NUL, 0, A, NUL, NUL) == 1
+    assert L.gq_compress_mean_skip(A, 0, 4, 100, 7, 0, 1, A, ctypes.c_void_p((1 << 20) + 8), 0, A,
+                                   NUL, NUL) == 6
+    assert L.gq_compress_mean_skip(A, 0, 4, 100, 7, 0, 1, A, B, 0, U, NUL, NUL) == 6
+    assert L.gq_compress_mean_skip(A, 0, 4, 100, 7, 0, 1, A, B, 5, A, A, NUL) == 4
+    assert L.gq_compress_mean_skip(A, 0, 4, 100, 0, 0, 1, A, B, 0, A, NUL, NUL) == 2
 
 
 def test_noalloc_entry_point_rejects():

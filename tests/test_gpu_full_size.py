@@ -5,9 +5,11 @@ compared with the CPU oracle at every coordinate, bit-exact. The results
 come from the launch configuration the benchmark times.
 
 - **Fused path.** The norm, the code sums at the container width and the
-  dequantized mean (`gq_compress_mean`, with and without code sums), and
-  the staged step's 1-byte sums and mean (`gq_compress_sums8`,
-  `gq_dequantize_sums8`).
+  dequantized mean (`gq_compress_mean`, with and without code sums, which
+  skips provably zero codes), the same pass reading every coordinate
+  (`gq_compress_mean_from_norm`), the span bounds behind the skip
+  (`gq_global_norm_bounds`), and the staged step's 1-byte sums and mean
+  (`gq_compress_sums8`, `gq_dequantize_sums8`).
 - **Unfused path.** Every worker's packed codes (`gq_quantize`) at the
   minimal and at the container width, their integer sum
   (`gq_reduce_codes`), and the mean from it (`gq_dequantize`).
@@ -107,6 +109,37 @@ def test_every_coordinate(key):
     gmean = host(mean_b)
     assert same_bytes(gmean, omean), first_diff(gmean.view(np.uint32), omean.view(np.uint32))
     compared += d
+    # the same pass reading every coordinate (the benchmarked call above
+    # skips the groups whose codes are provably zero)
+    dmean, _ = gq.gq_compress_mean_from_norm(xd, s, w.scheme, seed, norm)
+    assert same_bytes(host(dmean), omean), "the pass without the zero-code skip differs"
+    del dmean
+    compared += d
+    # the span bounds pass 1 wrote with the norm: the bf16 rounding-up of each
+    # 512-coordinate span's largest |x|, every entry
+    nb, bounds = gq.gq_global_norm_bounds(xd, w.q, w.p)
+    assert np.float32(host(nb)[0]) == N
+    spans, stride = -(-d // 512), -(-d // 8192) * 16
+    gb = host(bounds)[: 2 * n * stride].view(np.uint16).reshape(n, stride)[:, :spans]
+    bad_b = []
+
+    def bound_rows(i0, i1):
+        step = 1 << 24  # coordinates per slice (a multiple of 512)
+        for i in range(i0, i1):
+            for j in range(0, d, step):
+                je = min(d, j + step)
+                seg = x[i, j:je]
+                bits = (seg.astype(np.uint32) << np.uint32(16)) if x.dtype == np.uint16 else seg.view(np.uint32)
+                k = -(-(je - j) // 512)
+                row = np.zeros(k * 512, dtype=np.uint32)
+                row[:je - j] = bits & np.uint32(0x7FFFFFFF)
+                m = row.reshape(k, 512).max(axis=1).astype(np.uint64)
+                if not np.array_equal(gb[i, j // 512:j // 512 + k], ((m + 0xFFFF) >> 16).astype(np.uint16)):
+                    bad_b.append((i, j))
+
+    oracle.run_blocks(bound_rows, [(i, i + 1) for i in range(n)], THREADS)
+    assert not bad_b, f"span bounds differ in rows {bad_b[:8]}"
+    del bounds, gb
     mean_c, _, csum = gq.gq_compress_mean(xd, s, w.q, w.p, w.scheme, seed, code_bits=Wc,
                                           want_code_sum=True)
     assert same_bytes(host(mean_c), omean)

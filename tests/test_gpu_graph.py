@@ -96,17 +96,18 @@ def test_graph_replays_match_eager(n, d, s, q, p, scheme, W):
     del graph
 
 
-def test_staged_many_worker_pass_replays():
-    """The many-worker path (staged group mask and 1-byte sums, then the
-    mean) and the no-allocation entry point, captured together and replayed.
-    A staging buffer that starts stale (left from another input) must not
-    leak into a replay."""
+def test_skip_pass_and_noalloc_replay():
+    """gq_compress_mean with the zero-code skip (span bounds written by
+    pass 1 into the workspace) and the no-allocation entry point (bounds in
+    its own scratch), captured together and replayed.  Bounds left in the
+    workspace by another input must not leak into a replay; the first 64
+    coordinates sit at the top level, so their spans are dense."""
     n, d, s = 40, 30_011, 5
     x = wl.random_rows(n, d, seed=77, scale=0.3)
     x[:, :64] = 3.0  # sums beyond one byte: escapes recomputed from x
     xd = torch.from_numpy(x).to(DEV)
     ws = torch.empty(gq.gq_compress_workspace_bytes(n, d), dtype=torch.uint8, device=DEV)
-    assert ws.numel() > gq.gq_workspace_bytes(n, d)  # the staged path
+    assert ws.numel() > gq.gq_workspace_bytes(n, d)  # room for the span bounds
     mean = torch.empty(d, dtype=torch.float32, device=DEV)
     norm = torch.empty(1, dtype=torch.float32, device=DEV)
     mean2 = torch.empty_like(mean)
@@ -133,7 +134,7 @@ def test_staged_many_worker_pass_replays():
         step(side)
     other = torch.from_numpy(wl.random_rows(n, d, seed=78, scale=0.3)).to(DEV)
     for rep in range(3):
-        # eager work between replays, leaving the staging area stale
+        # eager work between replays, leaving another input's bounds behind
         gq.gq_compress_mean(other, s, INF, INF, "L", 10, workspace=ws)
         mean.zero_()
         mean2.zero_()

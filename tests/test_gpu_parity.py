@@ -227,12 +227,14 @@ def staged_matches(staged: np.ndarray, sums: np.ndarray) -> bool:
                                                        (48, 5000, "L", 1 << 20, 2.0, 2.0, True),
                                                        (32, 7, "L", 7, 2.0, 2.0, False)])
 def test_staged_sums_for_many_workers(n, d, scheme, s, q, p, escapes):
-    """n >= 32 fp32 workers with the larger workspace: the pass stages a
-    bit per 8-coordinate group and 1-byte sums of the non-zero groups, and
-    a second kernel writes the mean.  Sums outside [-127, 127] (the first
-    300 coordinates sit at the top level in every row, so they sum to
-    +-n M; the E rows flip signs) take the escape and are recomputed from
-    x.  Against the oracle and the single fused pass."""
+    """The staged compress step (gq_compress_sums8, gq_dequantize_sums8): the
+    pass stages a bit per 8-coordinate group and 1-byte sums of the non-zero
+    groups, and a second kernel writes the mean.  Sums outside [-127, 127]
+    (the first 300 coordinates sit at the top level in every row, so they
+    sum to +-n M; the E rows flip signs) take the escape and are recomputed
+    from x.  Against the oracle, and gq_compress_mean with the larger
+    workspace (the zero-code skip; those first spans are dense) and with the
+    smallest one (every coordinate read)."""
     x = wl.random_rows(n, d, seed=n * 7 + d, scale=0.2)
     x[:, : min(d, 300)] = 2.0
     if scheme == "E":
@@ -243,7 +245,8 @@ def test_staged_sums_for_many_workers(n, d, scheme, s, q, p, escapes):
     xd = to_dev(x)
     big = torch.empty(gq.gq_compress_workspace_bytes(n, d), dtype=torch.uint8, device=DEV)
     small = torch.empty(gq.gq_workspace_bytes(n, d), dtype=torch.uint8, device=DEV)
-    assert (big.numel() >= small.numel() + d) == (n >= 32)  # the staging from 32 workers
+    # room for the span bounds of the zero-code skip
+    assert big.numel() == small.numel() + -(-gq.gq_span_bounds_bytes(n, d) // 256) * 256
     gmean, gnorm, _ = gq.gq_compress_mean(xd, s, q, p, scheme, 17, workspace=big)
     check_norm(host(gnorm)[0], N)
     assert np.array_equal(host(gmean), mean)
