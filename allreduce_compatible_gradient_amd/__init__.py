@@ -477,7 +477,7 @@ def gq_dequantize_sums8(x: torch.Tensor, s: int, scheme, seed: int, norm: torch.
 
 
 # bytes of the device array behind gq_compress_mean_noalloc (GQ_NOALLOC_SCRATCH_BYTES)
-NOALLOC_SCRATCH_BYTES = 16 << 20
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def gq_compress_mean_noalloc(x: torch.Tensor, s: int, q, p, scheme, seed: int, *, mean,

@@ -309,13 +309,14 @@ int32_t gq_dequantize_sums8(const void *x, int32_t dtype, int64_t n, int64_t d, 
  * gq_compress_mean, bit for bit, except that the norm pass keeps its
  * partial sums (and, when gq_compress_workspace_bytes(n, d) fits too, the
  * span bounds of the zero-code skip) in a library-owned device array of
- * GQ_NOALLOC_SCRATCH_BYTES (16 MiB) instead of a workspace; every GPU the
+ * GQ_NOALLOC_SCRATCH_BYTES (64 MiB) instead of a workspace; every GPU the
  * library runs on holds its own copy of that array until the process ends.
  * The call allocates nothing (no hipMalloc, no allocating library routine).
  *   - Size limit: inputs with gq_workspace_bytes(n, d) >
  *     GQ_NOALLOC_SCRATCH_BYTES are rejected with GQ_ERR_WORKSPACE before
- *     any HIP call (fp32 inputs up to about 32 GiB fit; the per-worker
- *     values cap n at about 500k).
+ *     any HIP call (fp32 inputs up to about 128 GiB fit, and up to about
+ *     44 GiB with the span bounds; the per-worker values cap n at about
+ *     2 million).
  *   - Device: the array used is the current device's; a non-NULL stream
  *     must belong to the current device (GQ_ERR_ARG otherwise).  The first
  *     call on a device looks up its copy's address (hipGetSymbolAddress);
@@ -326,7 +327,7 @@ int32_t gq_dequantize_sums8(const void *x, int32_t dtype, int64_t n, int64_t d, 
  *     them, or use gq_compress_mean with separate workspaces.  No value
  *     carries between calls: each call writes every scratch word it reads
  *     before reading it, so nothing needs clearing.                       */
-#define GQ_NOALLOC_SCRATCH_BYTES (16LL << 20)
+#define GQ_NOALLOC_SCRATCH_BYTES (64LL << 20)
 int32_t gq_compress_mean_noalloc(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
                                  float q, float p, int32_t scheme, uint64_t seed,
                                  int32_t code_bits, float *mean, float *norm_dev,

@@ -200,12 +200,13 @@ def test_noalloc_entry_point_rejects():
     assert L.gq_compress_mean_noalloc(A, 0, 4, 100, 7, 2.0, 2.0, 0, 1, 8, U, A, NUL, NUL) == 6
     assert L.gq_compress_mean_noalloc(A, 0, 4, 100, 7, 2.0, 2.0, 0, 1, 8, A, NUL, NUL, NUL) == 1
     # sizes whose norm-pass scratch exceeds the array: rejected, with the size named
-    for n, d in ((1 << 20, 1), (600_000, 4096), (4, 9_000_000_000)):
+    for n, d in ((1 << 22, 1), (2_500_000, 4096), (4, 40_000_000_000)):
         assert gq.gq_workspace_bytes(n, d) > cap
         assert L.gq_compress_mean_noalloc(A, 0, n, d, 7, 2.0, 2.0, 0, 1, 0, A, A, NUL, NUL) == 5
         assert str(cap) in L.gq_last_error().decode()
-    # the largest workload's scratch fits (16 GB of fp32 input)
-    assert gq.gq_workspace_bytes(64, 64_000_000) <= cap
+    # the largest workload's scratch fits (16 GB of fp32 input), with the
+    # span bounds of the zero-code skip too
+    assert gq.gq_compress_workspace_bytes(64, 64_000_000) <= cap
 
 
 def test_binding_fails_loudly_without_a_gpu():

@@ -1,7 +1,8 @@
 """The no-allocation entry point against the entry point it mirrors.
 
-gq_compress_mean_noalloc keeps the norm pass's partial sums in the
-library's own device array instead of a caller workspace.  Called through
+gq_compress_mean_noalloc keeps the norm pass's partial sums, and the span
+bounds of the zero-code skip, in the library's own device array instead of
+a caller workspace.  Called through
 the C ABI with preallocated outputs, it must give gq_compress_mean's norm,
 mean and code sums bit for bit, on consecutive calls that reuse the array
 with a smaller input each time: first above 1 GiB of fp32 (the one-shot
@@ -82,8 +83,8 @@ def test_noalloc_matches_compress_mean_on_consecutive_calls():
 def test_noalloc_rejects_what_the_array_cannot_hold():
     """A size beyond the array is refused with GQ_ERR_WORKSPACE and nothing
     is launched (the check precedes every HIP call)."""
-    x = torch.zeros((600_000, 8), dtype=torch.float32, device=DEV)
-    assert gq.gq_workspace_bytes(600_000, 8) > gq.NOALLOC_SCRATCH_BYTES
+    x = torch.zeros((3_000_000, 8), dtype=torch.float32, device=DEV)
+    assert gq.gq_workspace_bytes(3_000_000, 8) > gq.NOALLOC_SCRATCH_BYTES
     mean = torch.empty(8, dtype=torch.float32, device=DEV)
     norm = torch.empty(1, dtype=torch.float32, device=DEV)
     with pytest.raises(gq.GQError) as e:
