@@ -837,6 +837,61 @@ __global__ __launch_bounds__(kThreads) void k_norm_partial(const void *__restric
     double s0 = 0.0, s1 = 0.0;
     float mx = 0.0f;
     int64_t j = jb + (int64_t)threadIdx.x * kPer;
+    // the sums of four groups (tiles j .. j + 3 kTile) and, where the wave's
+    // last lane is inside, their span bounds
+    auto four = [&](const float (&v0)[kPer], const float (&v1)[kPer], const float (&v2)[kPer],
+                    const float (&v3)[kPer]) {
+        if (bounds && j + to_last + 3 * kTile < je) {
+            const int64_t jw = j - 8 * (int64_t)(threadIdx.x & 63);
+            store_bound(bounds, bstride, i, jw, d, abs_bits_max(v0));
+            store_bound(bounds, bstride, i, jw + kTile, d, abs_bits_max(v1));
+            store_bound(bounds, bstride, i, jw + 2 * kTile, d, abs_bits_max(v2));
+            store_bound(bounds, bstride, i, jw + 3 * kTile, d, abs_bits_max(v3));
+        }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            if (QINF) {
+                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v0[k]), fabsf(v1[k])),
+                                     fmaxf(fabsf(v2[k]), fabsf(v3[k]))));
+            } else if (QM == 0) {
+                s0 += (double)v0[k] * (double)v0[k];
+                s1 += (double)v1[k] * (double)v1[k];
+                s0 += (double)v2[k] * (double)v2[k];
+                s1 += (double)v3[k] * (double)v3[k];
+            } else {
+                s0 += pow(fabs((double)v0[k]), qd);
+                s1 += pow(fabs((double)v1[k]), qd);
+                s0 += pow(fabs((double)v2[k]), qd);
+                s1 += pow(fabs((double)v3[k]), qd);
+            }
+        }
+    };
+    if (DT == GQ_IN_BF16 && vec_row) {
+        // bf16: eight groups' 16-byte words requested together, then summed
+        // as two steps of four in the same order as below (the span bounds
+        // lengthen the work between loads; more bytes in flight cover it)
+        const uint16_t *rowp = (const uint16_t *)x + row_off;
+        auto widen = [](const uint4 &w, float (&v)[kPer]) {
+            const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[2 * k] = __uint_as_float(a[k] << 16);
+                v[2 * k + 1] = __uint_as_float(a[k] & 0xFFFF0000u);
+            }
+        };
+        for (; j + 7 * kTile < je; j += 4 * kTile) {
+            uint4 w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                w[u] = *(const uint4 *)(rowp + j + u * kTile);
+            float v0[kPer], v1[kPer], v2[kPer], v3[kPer];
+            widen(w[0], v0); widen(w[1], v1); widen(w[2], v2); widen(w[3], v3);
+            four(v0, v1, v2, v3);
+            j += 4 * kTile;
+            widen(w[4], v0); widen(w[5], v1); widen(w[6], v2); widen(w[7], v3);
+            four(v0, v1, v2, v3);
+        }
+    }
     if (vec_row) {
         // four groups in flight per thread
         for (; j + 3 * kTile < je; j += 4 * kTile) {
@@ -845,30 +900,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_partial(const void *__restric
             load_group<DT>(x, row_off, j + kTile, d, true, v1);
             load_group<DT>(x, row_off, j + 2 * kTile, d, true, v2);
             load_group<DT>(x, row_off, j + 3 * kTile, d, true, v3);
-            if (bounds && j + to_last + 3 * kTile < je) {
-                const int64_t jw = j - 8 * (int64_t)(threadIdx.x & 63);
-                store_bound(bounds, bstride, i, jw, d, abs_bits_max(v0));
-                store_bound(bounds, bstride, i, jw + kTile, d, abs_bits_max(v1));
-                store_bound(bounds, bstride, i, jw + 2 * kTile, d, abs_bits_max(v2));
-                store_bound(bounds, bstride, i, jw + 3 * kTile, d, abs_bits_max(v3));
-            }
-#pragma unroll
-            for (int k = 0; k < kPer; ++k) {
-                if (QINF) {
-                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v0[k]), fabsf(v1[k])),
-                                         fmaxf(fabsf(v2[k]), fabsf(v3[k]))));
-                } else if (QM == 0) {
-                    s0 += (double)v0[k] * (double)v0[k];
-                    s1 += (double)v1[k] * (double)v1[k];
-                    s0 += (double)v2[k] * (double)v2[k];
-                    s1 += (double)v3[k] * (double)v3[k];
-                } else {
-                    s0 += pow(fabs((double)v0[k]), qd);
-                    s1 += pow(fabs((double)v1[k]), qd);
-                    s0 += pow(fabs((double)v2[k]), qd);
-                    s1 += pow(fabs((double)v3[k]), qd);
-                }
-            }
+            four(v0, v1, v2, v3);
         }
     }
     for (; j < je; j += kTile) {
