@@ -512,7 +512,7 @@ def gq_qsgd_local_mean(x: torch.Tensor, s: int, seed: int, *, code_bits: int = 0
     _buf(mean, 4 * d, "mean", x.device, torch.float32)
     _buf(norms, 4 * n, "norms", x.device, torch.float32)
     _buf(codes, n * max(gq_code_row_bytes(d, code_bits), 0), "codes", x.device)
-    ws = _workspace(workspace, n, d, x.device)
+    ws = _workspace(workspace, n, d, x.device, alloc=gq_compress_workspace_bytes(n, d))
     _check(lib().gq_qsgd_local_mean(_ptr(x), dt, n, d, s, seed, _ptr(mean), _ptr(norms),
                                     _ptr(codes), code_bits, _ptr(ws), _nbytes(ws),
                                     _stream(stream)))

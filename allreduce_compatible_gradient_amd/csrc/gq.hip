@@ -2239,14 +2239,21 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_words(const uint32_t *_
 
 // Ablation: local-norm QSGD.  Worker i uses its own scalars; the mean is an
 // fp64 sum in worker order.  Optional per-worker packed codes.
-template <int DT>
+// SKIP: with pass 1's span bounds, a worker's group whose codes are
+// provably 0 is not loaded (as in the fused pass, with each worker's own
+// sigma); skipping it drops a term fp64(0 kappa_i) = +0 from a sum that is
+// never -0, so the mean keeps its bits.  A worker whose kappa_i or
+// sigma_i 2^16 is not finite is read whole (0 times inf is NaN).
+template <int DT, bool SKIP>
 __global__ __launch_bounds__(kThreads) void k_local_mean(const void *__restrict__ x, int64_t n,
                                                          int64_t d, int s, uint64_t seed,
                                                          const float *__restrict__ norms,
                                                          const WorkerParams *__restrict__ params,
                                                          float *__restrict__ mean,
                                                          uint8_t *__restrict__ codes, int W,
-                                                         int64_t rbytes)
+                                                         int64_t rbytes,
+                                                         const uint16_t *__restrict__ bounds,
+                                                         int64_t bstride)
 {
     __shared__ alignas(16) uint32_t lds[kTile];
     // reverse of pass 1's order, as in the fused pass
@@ -2255,37 +2262,65 @@ __global__ __launch_bounds__(kThreads) void k_local_mean(const void *__restrict_
     const bool vec = (d & 7) == 0;
     const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    // one span per wave; its thresholds exist when the span starts in the row
+    const int64_t span = tile * (kTile / kSpan) + (int64_t)(threadIdx.x >> 6);
+    const bool wave_in = span * kSpan < d;
     double acc[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint32_t Hl = 0x10000u;
     for (int64_t i = 0; i < n; ++i) {
+        if (SKIP && (i & 63) == 0 && wave_in) {
+            // lane l: worker i + l's threshold for this span (0x10000: dense)
+            const int64_t r = i + (int64_t)(threadIdx.x & 63);
+            Hl = 0x10000u;
+            if (r < n) {
+                const WorkerParams pr = params[r];
+                const float sig16 = pr.sigma * 0x1p16f;
+                const uint32_t b = bounds[r * bstride + span];
+                if (sig16 < INFINITY && isfinite(pr.kappa) && b < 0x7F80u) {
+                    const float th = (__uint_as_float(b << 16) * pr.pre) * sig16;
+                    if (th < 65536.0f)
+                        Hl = (uint32_t)th;
+                }
+            }
+        }
+        const uint32_t H = (SKIP && wave_in) ? __builtin_amdgcn_readlane(Hl, (int)(i & 63)) : 0x10000u;
         int code[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
         const WorkerParams wp = params[i];
         if (j0 < d && norms[i] != 0.0f) {
-            QParams q = {};
-            q.pre = wp.pre;
-            q.sigma = wp.sigma;
-            q.top = (float)s;
-            q.s = s;
-            float v[kPer];
-            load_group<DT>(x, i * d, j0, d, vec, v);
             const uint4 A = philox10(make_uint4(blo, bhi, (uint32_t)i, 0u), k0, k1);
-            float m[kPer];
-            bool tie = false;
-            const bool pre = wp.pre != 1.0f;
-            if (pre)
-                quant_group<GQ_SCHEME_L, true>(v, A, q, m, tie);
-            else
-                quant_group<GQ_SCHEME_L, false>(v, A, q, m, tie);
-            if (tie) {
-                const uint4 B = philox10(make_uint4(blo, bhi, (uint32_t)i, 1u), k0, k1);
-                if (pre)
-                    settle_ties<GQ_SCHEME_L, true>(v, A, B, q, m);
-                else
-                    settle_ties<GQ_SCHEME_L, false>(v, A, B, q, m);
-            }
+            if (H > 0xFFFFu || min_half16(A) <= H) {
+                QParams q = {};
+                q.pre = wp.pre;
+                q.sigma = wp.sigma;
+                q.top = (float)s;
+                q.s = s;
+                float v[kPer];
+                load_group<DT>(x, i * d, j0, d, vec, v);
+                float m[kPer];
+                bool tie = false;
+                const bool pre = wp.pre != 1.0f;
+                if (H <= 0xFFFFu) {
+                    if (pre)
+                        quant_group_sparse<true>(v, A, q, wp.sigma * 0x1p16f, m, tie);
+                    else
+                        quant_group_sparse<false>(v, A, q, wp.sigma * 0x1p16f, m, tie);
+                } else if (pre) {
+                    quant_group<GQ_SCHEME_L, true>(v, A, q, m, tie);
+                } else {
+                    quant_group<GQ_SCHEME_L, false>(v, A, q, m, tie);
+                }
+                if (tie) {
+                    const uint4 B = philox10(make_uint4(blo, bhi, (uint32_t)i, 1u), k0, k1);
+                    if (pre)
+                        settle_ties<GQ_SCHEME_L, true>(v, A, B, q, m);
+                    else
+                        settle_ties<GQ_SCHEME_L, false>(v, A, B, q, m);
+                }
 #pragma unroll
-            for (int k = 0; k < kPer; ++k) {
-                code[k] = (int)copysignf(m[k], v[k]);
-                acc[k] = acc[k] + (double)code[k] * wp.kappa;
+                for (int k = 0; k < kPer; ++k) {
+                    code[k] = (int)copysignf(m[k], v[k]);
+                    acc[k] = acc[k] + (double)code[k] * wp.kappa;
+                }
             }
         }
         if (codes)
@@ -3578,18 +3613,35 @@ int32_t gq_qsgd_local_mean(const void *x, int32_t dtype, int64_t n, int64_t d, i
         return fail(GQ_ERR_ALIGN, "mean is not 16-byte aligned");
     GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
     hipStream_t st = (hipStream_t)stream;
-    GQ_TRY(launch_norm(x, dtype, n, d, 2.0f, 2.0f, true, norms_dev, workspace, s, st));
+    const WsLayout L = ws_layout(n, d);
+    // with room for the span bounds, zero codes are skipped as in the fused pass
+    uint16_t *bounds = (L.total_compress > L.total && workspace_bytes >= L.total_compress)
+                           ? (uint16_t *)((char *)workspace + L.bounds)
+                           : nullptr;
+    GQ_TRY(launch_norm(x, dtype, n, d, 2.0f, 2.0f, true, norms_dev, workspace, s, st, nullptr,
+                       bounds));
     const int64_t tiles = (d + kTile - 1) / kTile;
     if (tiles == 0)
         return ok();
-    const WsLayout L = ws_layout(n, d);
     const WorkerParams *params = (const WorkerParams *)((const char *)workspace + L.params);
     const int64_t rb = codes_or_null ? row_bytes(d, code_bits) : 0;
     const dim3 grid((unsigned)tiles), block(kThreads);
-    if (dtype == GQ_IN_F32)
-        k_local_mean<GQ_IN_F32><<<grid, block, 0, st>>>(x, n, d, s, seed, norms_dev, params, mean, (uint8_t *)codes_or_null, code_bits, rb);
-    else
-        k_local_mean<GQ_IN_BF16><<<grid, block, 0, st>>>(x, n, d, s, seed, norms_dev, params, mean, (uint8_t *)codes_or_null, code_bits, rb);
+    const int64_t bstride = bound_stride(d);
+#define GQ_LOCAL(DT, SK)                                                                          \
+    k_local_mean<DT, SK><<<grid, block, 0, st>>>(x, n, d, s, seed, norms_dev, params, mean,       \
+                                                 (uint8_t *)codes_or_null, code_bits, rb, bounds, \
+                                                 bstride)
+    if (dtype == GQ_IN_F32) {
+        if (bounds)
+            GQ_LOCAL(GQ_IN_F32, true);
+        else
+            GQ_LOCAL(GQ_IN_F32, false);
+    } else if (bounds) {
+        GQ_LOCAL(GQ_IN_BF16, true);
+    } else {
+        GQ_LOCAL(GQ_IN_BF16, false);
+    }
+#undef GQ_LOCAL
     return check_launch("k_local_mean");
 }
 

@@ -340,7 +340,11 @@ int32_t gq_compress_mean_noalloc(const void *x, int32_t dtype, int64_t n, int64_
  * mean[j] = fp32(sum_i fp64(code_ij kappa_i)), kappa_i = fp64(N_i / (n s)),
  * accumulated in fp64 in worker order.  norms_dev: n floats.  If
  * codes_or_null is not NULL it receives the per-worker packed codes at
- * code_bits (gq_min_code_bits(1, s, GQ_SCHEME_L) <= W <= 32).             */
+ * code_bits (gq_min_code_bits(1, s, GQ_SCHEME_L) <= W <= 32).  With a
+ * workspace of gq_compress_workspace_bytes(n, d) it takes the zero-code
+ * skip of gq_compress_mean_skip with each worker's own scale (a worker
+ * whose kappa_i is not finite is read whole); the results are the same
+ * bits.                                                                    */
 int32_t gq_qsgd_local_mean(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
                            uint64_t seed, float *mean, float *norms_dev, void *codes_or_null,
                            int32_t code_bits, void *workspace, int64_t workspace_bytes,

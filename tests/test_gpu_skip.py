@@ -185,3 +185,49 @@ def test_all_zero_and_single_worker():
     check_all(z, 7, 2.0, 2.0, "L", 1, "zeros")
     one = wl.random_rows(1, 70_001, seed=3, scale=0.5)
     check_all(one, 127, 2.0, INF, "L", 2, "one-worker")
+
+
+def check_local(x, s, seed, tag, vs_oracle=True):
+    """The local-norm ablation with the zero-code skip (full workspace)
+    against the same call reading every coordinate (smallest workspace) and
+    the oracle: norms, per-worker codes and mean.  vs_oracle False: only the
+    two device calls are compared (a worker's inf gives N_i = inf on the
+    device and NaN in the oracle's compensated sum, a difference of the
+    norm, not of the skip)."""
+    n, d = x.shape
+    onorms, ocodes, omean = oracle.qsgd_local_mean(x, s, seed)
+    xd = to_dev(x)
+    W = gq.gq_min_code_bits(1, s, "L")
+    small = torch.empty(gq.gq_workspace_bytes(n, d), dtype=torch.uint8, device=DEV)
+    skip_m, skip_n, skip_c = gq.gq_qsgd_local_mean(xd, s, seed, code_bits=W, want_codes=True)
+    full_m, full_n, full_c = gq.gq_qsgd_local_mean(xd, s, seed, code_bits=W, want_codes=True,
+                                                   workspace=small)
+    hs, hf = host(skip_m), host(full_m)
+    assert np.array_equal(hs.view(np.uint32), hf.view(np.uint32)), (tag, "skip vs every coordinate")
+    assert np.array_equal(host(skip_n).view(np.uint32), host(full_n).view(np.uint32)), (tag, "norms")
+    assert np.array_equal(host(skip_c), host(full_c)), (tag, "codes")
+    if vs_oracle:
+        assert np.array_equal(host(skip_n).view(np.uint32), onorms.view(np.uint32)), (tag, "norms")
+        assert np.array_equal(host(skip_c), oracle.pack(ocodes, W)), (tag, "codes vs oracle")
+        assert np.array_equal(hs.view(np.uint32), omean.view(np.uint32)), (tag, "mean vs oracle")
+    log(f"ablation {tag}: n={n} d={d} s={s}: bit-exact")
+
+
+@pytest.mark.parametrize("n,d,dtype,kind", [(4, 65_536, "f32", "plain"), (3, 1, "f32", "plain"),
+                                            (70, 4100, "f32", "mixed"), (9, 10_007, "bf16", "heavy"),
+                                            (130, 1030, "bf16", "mixed")])
+def test_local_ablation_skip(n, d, dtype, kind):
+    check_local(make(kind, n, d, dtype, seed=n * 77 + d), 3, 9 + n, f"{kind}/{dtype}")
+
+
+def test_local_ablation_skip_edges():
+    """A worker of zeros (norm 0: no codes), one with an inf (kappa_i inf:
+    its zero codes add 0 * inf = NaN, so it is read whole), tiny norms."""
+    x = wl.random_rows(5, 5000, seed=12, scale=1e-3)
+    x[1] = 0.0
+    check_local(x, 3, 4, "zero worker")
+    y = x.copy()
+    y[3, 17] = np.float32(np.inf)
+    check_local(y, 3, 5, "inf worker", vs_oracle=False)
+    z = (wl.random_rows(4, 3001, seed=13) * np.float32(1e-38)).astype(np.float32)
+    check_local(z, 7, 6, "tiny norms")
