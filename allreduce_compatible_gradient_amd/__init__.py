@@ -57,6 +57,9 @@ SIGNATURES = {
                                      _vp]),
     "gq_compress_mean_skip": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _u64, _vp, _vp, _i32,
                                      _vp, _vp, _vp]),
+    "gq_norm_term_bounds": (_i32, [_vp, _i32, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _i64, _vp]),
+    "gq_compress_words_skip": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp, _u64, _i64,
+                                      _i32, _vp, _vp]),
     "gq_sums8_bytes": (_i64, [_i64]),
     "gq_compress_sums8": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _u64, _vp, _vp, _vp]),
     "gq_dequantize_sums8": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _u64, _vp, _vp, _vp, _vp]),
@@ -408,6 +411,43 @@ def gq_compress_mean_skip(x: torch.Tensor, s: int, scheme, seed: int, norm: torc
                                        _ptr(bounds), code_bits, _ptr(mean), _ptr(code_sum),
                                        _stream(stream)))
     return mean, code_sum
+
+
+def gq_norm_term_bounds(x: torch.Tensor, q=2.0, p=2.0, *, term=None, bounds=None,
+                        workspace=None, stream=None):
+    """gq_norm_term and, in the same pass, the span bounds of this shard's
+    rows: (term, bounds), as gq_global_norm_bounds lays them out."""
+    dt = _input(x)
+    n, d = x.shape
+    term = (torch.empty(1, dtype=torch.float64, device=x.device) if term is None
+            else _buf(term, 8, "term", x.device, torch.float64))
+    nb = max(gq_span_bounds_bytes(n, d), 0)
+    if bounds is None:
+        bounds = torch.empty(max(nb, 2), dtype=torch.uint8, device=x.device)
+    _buf(bounds, nb, "bounds", x.device)
+    ws = _workspace(workspace, n, d, x.device)
+    _check(lib().gq_norm_term_bounds(_ptr(x), dt, n, d, _order(q), _order(p), _ptr(term),
+                                     _ptr(bounds), _ptr(ws), _nbytes(ws), _stream(stream)))
+    return term, bounds
+
+
+def gq_compress_words_skip(x: torch.Tensor, s: int, scheme, norm: torch.Tensor,
+                           bounds: torch.Tensor, seed: int, code_bits: int, *,
+                           worker_base: int = 0, word_sum=None, stream=None):
+    """gq_compress_words_from_norm with the zero-code skip, given the bounds
+    gq_norm_term_bounds wrote for this x: the same word row."""
+    dt = _input(x)
+    n, d = x.shape
+    rb = max(gq_word_row_bytes(d, code_bits), 0)
+    _norm_in(norm, x.device)
+    _buf(bounds, max(gq_span_bounds_bytes(n, d), 0), "bounds", x.device)
+    if word_sum is None:
+        word_sum = torch.empty(rb // 4, dtype=torch.int32, device=x.device)
+    _buf(word_sum, rb, "word_sum", x.device)
+    _check(lib().gq_compress_words_skip(_ptr(x), dt, n, d, s, _scheme(scheme), _ptr(norm),
+                                        _ptr(bounds), seed, worker_base, code_bits,
+                                        _ptr(word_sum), _stream(stream)))
+    return word_sum
 
 
 def gq_compress_mean(x: torch.Tensor, s: int, q, p, scheme, seed: int, *, code_bits: int = 0,

@@ -1338,7 +1338,7 @@ __device__ __forceinline__ void accumulate_workers_skip(const void *__restrict__
                                                         const uint16_t *__restrict__ bounds,
                                                         int64_t bstride, int64_t span, float sigK,
                                                         bool sparse_ok, float (&accf)[kPer],
-                                                        int (&acci)[kPer])
+                                                        int (&acci)[kPer], uint32_t wb = 0)
 {
     const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
     // one worker's group: quantize and add it when it may hold a non-zero code
@@ -1353,7 +1353,7 @@ __device__ __forceinline__ void accumulate_workers_skip(const void *__restrict__
             else
                 quant_group_sparse<PRE>(v, A, q, sigK, m, tie);
             if (tie) {
-                const uint4 B = philox10(make_uint4(blo, bhi, (uint32_t)i, 1u), k0, k1);
+                const uint4 B = philox10(make_uint4(blo, bhi, wb + (uint32_t)i, 1u), k0, k1);
                 settle_ties<SCH, PRE>(v, A, B, q, m);
             }
 #pragma unroll
@@ -1372,14 +1372,14 @@ __device__ __forceinline__ void accumulate_workers_skip(const void *__restrict__
         // two workers per step: two independent Philox chains in flight
         // (measured 1-4% faster than one)
         for (; r + 1 < cnt; r += 2) {
-            const uint4 A0 = philox10(make_uint4(blo, bhi, (uint32_t)(c + r), 0u), k0, k1);
-            const uint4 A1 = philox10(make_uint4(blo, bhi, (uint32_t)(c + r + 1), 0u), k0, k1);
+            const uint4 A0 = philox10(make_uint4(blo, bhi, wb + (uint32_t)(c + r), 0u), k0, k1);
+            const uint4 A1 = philox10(make_uint4(blo, bhi, wb + (uint32_t)(c + r + 1), 0u), k0, k1);
             row(c + r, __builtin_amdgcn_readlane(Hl, r), A0);
             row(c + r + 1, __builtin_amdgcn_readlane(Hl, r + 1), A1);
         }
         if (r < cnt)
             row(c + r, __builtin_amdgcn_readlane(Hl, r),
-                philox10(make_uint4(blo, bhi, (uint32_t)(c + r), 0u), k0, k1));
+                philox10(make_uint4(blo, bhi, wb + (uint32_t)(c + r), 0u), k0, k1));
     }
 }
 
@@ -2057,13 +2057,17 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_words_lds(
 // (ACC as in k_compress_mean: fp32 sums, int32, or packed 16-bit pairs for
 // bf16 standard dithering), then the biased sums go to LDS and are
 // assembled into word quads as in k_quantize_words.
-template <int DT, int SCH, int FPW, int ACC>
+// SKIP: with pass 1's span bounds, as the fused pass (each 2048-coordinate
+// segment is one fused-pass tile: a wave per 512-coordinate span).
+template <int DT, int SCH, int FPW, int ACC, bool SKIP>
 __global__ __launch_bounds__(kThreads) void k_compress_words(const void *__restrict__ x, int64_t n,
                                                              int64_t d, int s, uint64_t seed,
                                                              int64_t worker_base,
                                                              const float *__restrict__ norm_dev,
                                                              uint32_t *__restrict__ out, int W,
-                                                             uint32_t bias, int64_t rwords)
+                                                             uint32_t bias, int64_t rwords,
+                                                             const uint16_t *__restrict__ bounds,
+                                                             int64_t bstride)
 {
     using E = WordLdsT<FPW>;
     __shared__ alignas(16) E lds[FPW > 1 ? kWordsPerBlock * FPW : 1];
@@ -2073,12 +2077,40 @@ __global__ __launch_bounds__(kThreads) void k_compress_words(const void *__restr
     const bool vec = (d & 7) == 0;
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32), wb = (uint32_t)worker_base;
     uint32_t w1[kPer]; // FPW == 1: the thread's 8 words
-#pragma unroll
+#pragma unroll(SKIP ? 1 : FPW)
     for (int g = 0; g < FPW; ++g) {
         const int rel = g * kWordsPerBlock + (int)threadIdx.x * kPer;
         const int64_t j0 = c_base + rel;
         int acc[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (!q.zero && j0 < d) {
+        const int64_t span = (c_base + g * kWordsPerBlock) / kSpan + (int64_t)(threadIdx.x >> 6);
+        if (SKIP && !q.zero && span * kSpan < d) { // the whole wave
+            const bool live = j0 < d;
+            const float sigK = q.sigma * (SCH == GQ_SCHEME_L ? 0x1p16f : q.p2E16);
+            const bool sparse_ok = sigK < INFINITY;
+            if constexpr (ACC == kAccPk16) {
+                if (q.prescale)
+                    accumulate_workers_pk16<DT, true, true>(x, n, d, j0, vec, q, k0, k1, acc, wb,
+                                                            live, bounds, bstride, span, sparse_ok);
+                else
+                    accumulate_workers_pk16<DT, false, true>(x, n, d, j0, vec, q, k0, k1, acc, wb,
+                                                             live, bounds, bstride, span, sparse_ok);
+            } else {
+                float accf[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+                if (q.prescale)
+                    accumulate_workers_skip<DT, SCH, true, ACC == kAccF32>(
+                        x, n, d, j0, vec, live, q, k0, k1, bounds, bstride, span, sigK, sparse_ok,
+                        accf, acc, wb);
+                else
+                    accumulate_workers_skip<DT, SCH, false, ACC == kAccF32>(
+                        x, n, d, j0, vec, live, q, k0, k1, bounds, bstride, span, sigK, sparse_ok,
+                        accf, acc, wb);
+                if (ACC == kAccF32) {
+#pragma unroll
+                    for (int k = 0; k < kPer; ++k)
+                        acc[k] = (int)accf[k];
+                }
+            }
+        } else if (!SKIP && !q.zero && j0 < d) {
             if constexpr (ACC == kAccPk16) {
                 if (q.prescale)
                     accumulate_workers_pk16<DT, true, false>(x, n, d, j0, vec, q, k0, k1, acc, wb);
@@ -2138,31 +2170,48 @@ __global__ __launch_bounds__(kThreads) void k_compress_words(const void *__restr
 // The accumulator of k_compress_words for one fields-per-word count: packed
 // 16-bit pairs for bf16 standard dithering with n M < 2^15, else fp32 sums
 // while n M <= 2^24 (always true for W <= 16), else int32.
-template <int DT, int SCH, int F>
-void launch_compress_words(dim3 grid, hipStream_t st, bool pk16, bool facc, const void *x,
-                           int64_t n, int64_t d, int s, uint64_t seed, int64_t worker_base,
-                           const float *norm_dev, uint32_t *out, int W, uint32_t bias,
-                           int64_t rwords)
+// bounds != nullptr: the zero-code skip with pass 1's span bounds.
+template <int DT, int SCH, int F, bool SKIP>
+void launch_compress_words_as(dim3 grid, hipStream_t st, bool pk16, bool facc, const void *x,
+                              int64_t n, int64_t d, int s, uint64_t seed, int64_t worker_base,
+                              const float *norm_dev, uint32_t *out, int W, uint32_t bias,
+                              int64_t rwords, const uint16_t *bounds, int64_t bstride)
 {
     const dim3 block(kThreads);
     if constexpr (DT == GQ_IN_BF16 && SCH == GQ_SCHEME_L && F > 1) {
         if (pk16) {
-            k_compress_words<DT, SCH, F, kAccPk16><<<grid, block, 0, st>>>(
-                x, n, d, s, seed, worker_base, norm_dev, out, W, bias, rwords);
+            k_compress_words<DT, SCH, F, kAccPk16, SKIP><<<grid, block, 0, st>>>(
+                x, n, d, s, seed, worker_base, norm_dev, out, W, bias, rwords, bounds, bstride);
             return;
         }
     }
     if constexpr (F > 1) {
-        k_compress_words<DT, SCH, F, kAccF32><<<grid, block, 0, st>>>(
-            x, n, d, s, seed, worker_base, norm_dev, out, W, bias, rwords);
+        k_compress_words<DT, SCH, F, kAccF32, SKIP><<<grid, block, 0, st>>>(
+            x, n, d, s, seed, worker_base, norm_dev, out, W, bias, rwords, bounds, bstride);
     } else {
         if (facc)
-            k_compress_words<DT, SCH, F, kAccF32><<<grid, block, 0, st>>>(
-                x, n, d, s, seed, worker_base, norm_dev, out, W, bias, rwords);
+            k_compress_words<DT, SCH, F, kAccF32, SKIP><<<grid, block, 0, st>>>(
+                x, n, d, s, seed, worker_base, norm_dev, out, W, bias, rwords, bounds, bstride);
         else
-            k_compress_words<DT, SCH, F, kAccInt><<<grid, block, 0, st>>>(
-                x, n, d, s, seed, worker_base, norm_dev, out, W, bias, rwords);
+            k_compress_words<DT, SCH, F, kAccInt, SKIP><<<grid, block, 0, st>>>(
+                x, n, d, s, seed, worker_base, norm_dev, out, W, bias, rwords, bounds, bstride);
     }
+}
+
+template <int DT, int SCH, int F>
+void launch_compress_words(dim3 grid, hipStream_t st, bool pk16, bool facc, const void *x,
+                           int64_t n, int64_t d, int s, uint64_t seed, int64_t worker_base,
+                           const float *norm_dev, uint32_t *out, int W, uint32_t bias,
+                           int64_t rwords, const uint16_t *bounds)
+{
+    if (bounds)
+        launch_compress_words_as<DT, SCH, F, true>(grid, st, pk16, facc, x, n, d, s, seed,
+                                                   worker_base, norm_dev, out, W, bias, rwords,
+                                                   bounds, bound_stride(d));
+    else
+        launch_compress_words_as<DT, SCH, F, false>(grid, st, pk16, facc, x, n, d, s, seed,
+                                                    worker_base, norm_dev, out, W, bias, rwords,
+                                                    nullptr, 0);
 }
 
 // What a native integer SUM over the n rows computes: the word-wise sum
@@ -3098,6 +3147,22 @@ int32_t gq_norm_term(const void *x, int32_t dtype, int64_t n, int64_t d, float q
                        term_dev);
 }
 
+int32_t gq_norm_term_bounds(const void *x, int32_t dtype, int64_t n, int64_t d, float q, float p,
+                            double *term_dev, uint16_t *bounds, void *workspace,
+                            int64_t workspace_bytes, void *stream)
+{
+    GQ_TRY(validate_x(x, dtype, n, d));
+    if (!term_dev || (!bounds && d > 0))
+        return fail(GQ_ERR_NULL, "term_dev or bounds is NULL");
+    if (!order_ok(q) || !order_ok(p))
+        return fail(GQ_ERR_UNSUPPORTED, "q and p must be reals >= 1 or +inf");
+    if (!aligned16(bounds))
+        return fail(GQ_ERR_ALIGN, "bounds is not 16-byte aligned");
+    GQ_TRY(validate_ws(workspace, workspace_bytes, n, d));
+    return launch_norm(x, dtype, n, d, q, p, false, nullptr, workspace, 0, (hipStream_t)stream,
+                       term_dev, d > 0 ? bounds : nullptr);
+}
+
 int32_t gq_norm_from_term(const double *term_dev, float q, float p, float *norm_dev, void *stream)
 {
     if (!term_dev || !norm_dev)
@@ -3289,10 +3354,47 @@ int32_t gq_quantize_words(const void *x, int32_t dtype, int64_t n, int64_t d, in
     return check_launch("k_quantize_words");
 }
 
-int32_t gq_compress_words_from_norm(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
-                                   int32_t scheme, const float *norm_dev, uint64_t seed,
-                                   int64_t worker_base, int32_t code_bits, void *word_sum,
-                                   void *stream)
+// The word-layout compress pass; bounds != nullptr takes the zero-code skip.
+static int32_t compress_words(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                              int32_t scheme, const float *norm_dev, uint64_t seed,
+                              int64_t worker_base, int32_t code_bits, void *word_sum,
+                              const uint16_t *bounds, hipStream_t st)
+{
+    const int64_t rwords = gq_word_row_bytes(d, code_bits) / 4;
+    const int64_t tiles = (rwords + kWordsPerBlock - 1) / kWordsPerBlock;
+    if (tiles == 0)
+        return ok();
+    if (tiles > kMaxGrid)
+        return fail(GQ_ERR_UNSUPPORTED, "d exceeds the launch limit");
+    const uint32_t bias = (uint32_t)(n * top_code(s, scheme)); // < 2^31 by the width rule
+    const dim3 grid((unsigned)tiles);
+    uint32_t *out = (uint32_t *)word_sum;
+    const int64_t nm = n * top_code(s, scheme);
+    const bool facc = nm <= ((int64_t)1 << 24);
+    const bool pk16 = dtype == GQ_IN_BF16 && scheme == GQ_SCHEME_L && nm < ((int64_t)1 << 15);
+#define GQ_CW(F)                                                                               \
+    do {                                                                                       \
+        if (dtype == GQ_IN_F32 && scheme == GQ_SCHEME_L)                                       \
+            launch_compress_words<GQ_IN_F32, GQ_SCHEME_L, F>(grid, st, pk16, facc, x, n, d, s, \
+                seed, worker_base, norm_dev, out, code_bits, bias, rwords, bounds);           \
+        else if (dtype == GQ_IN_F32)                                                           \
+            launch_compress_words<GQ_IN_F32, GQ_SCHEME_E, F>(grid, st, pk16, facc, x, n, d, s, \
+                seed, worker_base, norm_dev, out, code_bits, bias, rwords, bounds);           \
+        else if (scheme == GQ_SCHEME_L)                                                        \
+            launch_compress_words<GQ_IN_BF16, GQ_SCHEME_L, F>(grid, st, pk16, facc, x, n, d,  \
+                s, seed, worker_base, norm_dev, out, code_bits, bias, rwords, bounds);        \
+        else                                                                                   \
+            launch_compress_words<GQ_IN_BF16, GQ_SCHEME_E, F>(grid, st, pk16, facc, x, n, d,  \
+                s, seed, worker_base, norm_dev, out, code_bits, bias, rwords, bounds);        \
+    } while (0)
+    GQ_FPW_SWITCH(word_fields(code_bits), GQ_CW)
+#undef GQ_CW
+    return check_launch("k_compress_words");
+}
+
+static int32_t validate_words_call(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                                   int32_t scheme, const float *norm_dev, int64_t worker_base,
+                                   int32_t code_bits, const void *word_sum)
 {
     GQ_TRY(validate_x(x, dtype, n, d));
     GQ_TRY(validate_scheme(s, scheme));
@@ -3303,37 +3405,33 @@ int32_t gq_compress_words_from_norm(const void *x, int32_t dtype, int64_t n, int
     GQ_TRY(validate_width(n, s, scheme, code_bits));
     if (!aligned16(word_sum))
         return fail(GQ_ERR_ALIGN, "word_sum is not 16-byte aligned");
-    const int64_t rwords = gq_word_row_bytes(d, code_bits) / 4;
-    const int64_t tiles = (rwords + kWordsPerBlock - 1) / kWordsPerBlock;
-    if (tiles == 0)
-        return ok();
-    if (tiles > kMaxGrid)
-        return fail(GQ_ERR_UNSUPPORTED, "d exceeds the launch limit");
-    const uint32_t bias = (uint32_t)(n * top_code(s, scheme)); // < 2^31 by the width rule
-    const dim3 grid((unsigned)tiles);
-    hipStream_t st = (hipStream_t)stream;
-    uint32_t *out = (uint32_t *)word_sum;
-    const int64_t nm = n * top_code(s, scheme);
-    const bool facc = nm <= ((int64_t)1 << 24);
-    const bool pk16 = dtype == GQ_IN_BF16 && scheme == GQ_SCHEME_L && nm < ((int64_t)1 << 15);
-#define GQ_CW(F)                                                                               \
-    do {                                                                                       \
-        if (dtype == GQ_IN_F32 && scheme == GQ_SCHEME_L)                                       \
-            launch_compress_words<GQ_IN_F32, GQ_SCHEME_L, F>(grid, st, pk16, facc, x, n, d, s, \
-                seed, worker_base, norm_dev, out, code_bits, bias, rwords);                   \
-        else if (dtype == GQ_IN_F32)                                                           \
-            launch_compress_words<GQ_IN_F32, GQ_SCHEME_E, F>(grid, st, pk16, facc, x, n, d, s, \
-                seed, worker_base, norm_dev, out, code_bits, bias, rwords);                   \
-        else if (scheme == GQ_SCHEME_L)                                                        \
-            launch_compress_words<GQ_IN_BF16, GQ_SCHEME_L, F>(grid, st, pk16, facc, x, n, d,  \
-                s, seed, worker_base, norm_dev, out, code_bits, bias, rwords);                \
-        else                                                                                   \
-            launch_compress_words<GQ_IN_BF16, GQ_SCHEME_E, F>(grid, st, pk16, facc, x, n, d,  \
-                s, seed, worker_base, norm_dev, out, code_bits, bias, rwords);                \
-    } while (0)
-    GQ_FPW_SWITCH(word_fields(code_bits), GQ_CW)
-#undef GQ_CW
-    return check_launch("k_compress_words");
+    return ok();
+}
+
+int32_t gq_compress_words_from_norm(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                                   int32_t scheme, const float *norm_dev, uint64_t seed,
+                                   int64_t worker_base, int32_t code_bits, void *word_sum,
+                                   void *stream)
+{
+    GQ_TRY(validate_words_call(x, dtype, n, d, s, scheme, norm_dev, worker_base, code_bits,
+                               word_sum));
+    return compress_words(x, dtype, n, d, s, scheme, norm_dev, seed, worker_base, code_bits,
+                          word_sum, nullptr, (hipStream_t)stream);
+}
+
+int32_t gq_compress_words_skip(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                               int32_t scheme, const float *norm_dev, const uint16_t *bounds,
+                               uint64_t seed, int64_t worker_base, int32_t code_bits,
+                               void *word_sum, void *stream)
+{
+    GQ_TRY(validate_words_call(x, dtype, n, d, s, scheme, norm_dev, worker_base, code_bits,
+                               word_sum));
+    if (!bounds && d > 0)
+        return fail(GQ_ERR_NULL, "bounds is NULL");
+    if (!aligned16(bounds))
+        return fail(GQ_ERR_ALIGN, "bounds is not 16-byte aligned");
+    return compress_words(x, dtype, n, d, s, scheme, norm_dev, seed, worker_base, code_bits,
+                          word_sum, d > 0 ? bounds : nullptr, (hipStream_t)stream);
 }
 
 int32_t gq_sum_words(const void *words, int64_t n, int64_t d, int32_t code_bits, void *word_sum,

@@ -261,7 +261,9 @@ def bucket_report(gq, torch, w, xd, stream, steps):
     (after what would be that all-reduce; here the device's own row stands
     in for the sum).  The two all-reduces are not run: the library works on
     one device.  Buckets are the leading 1, 25 and 100 MB of worker 0's row, timed
-    as graph replays of the four launches."""
+    as graph replays of the four launches; "with_skip" times the same share
+    with the term-and-bounds pass and the zero-code skip in place of the
+    first and third launches."""
     out = {}
     W = gq.gq_min_code_bits(w.n, w.s, w.scheme)
     for label, nbytes in (("1MB", 1 << 20), ("25MB", 25 << 20), ("100MB", 100 << 20)):
@@ -273,6 +275,7 @@ def bucket_report(gq, torch, w, xd, stream, steps):
         rb = gq.gq_word_row_bytes(db, W)
         words = torch.empty((1, rb // 4), dtype=torch.int32, device=xd.device)
         mean = torch.empty(db, dtype=torch.float32, device=xd.device)
+        bounds = torch.empty(gq.gq_span_bounds_bytes(1, db), dtype=torch.uint8, device=xd.device)
         parts = {
             "norm_term_us": lambda st: gq.gq_norm_term(b, w.q, w.p, term=term, workspace=ws,
                                                        stream=st),
@@ -286,18 +289,36 @@ def bucket_report(gq, torch, w, xd, stream, steps):
                                                                      mean=mean, stream=st),
         }
 
+        skip_parts = {
+            "norm_term_bounds_us": lambda st: gq.gq_norm_term_bounds(
+                b, w.q, w.p, term=term, bounds=bounds, workspace=ws, stream=st),
+            "norm_from_term_us": parts["norm_from_term_us"],
+            "compress_words_skip_us": lambda st: gq.gq_compress_words_skip(
+                b, w.s, w.scheme, norm, bounds, w.seed, W, word_sum=words[0], stream=st),
+            "dequantize_words_us": parts["dequantize_words_us"],
+        }
+
         def share(st):
             for f in parts.values():
                 f(st)
+
+        def share_skip(st):
+            for f in skip_parts.values():
+                f(st)
         t = _time_us(torch, stream, share, steps)
+        t_skip = _time_us(torch, stream, share_skip, steps)
         # algorithmic bytes: the bucket read twice, the word row written and read, the mean
         alg = 2 * db * w.elem_bytes + 2 * rb + 4 * db
         out[label] = {"elements": db, "code_bits": W, "us": round(t, 3),
                       "bucket_GBs": round(db * w.elem_bytes / (t * 1e-6) / 1e9, 3),
                       "alg_GBs": round(alg / (t * 1e-6) / 1e9, 3),
                       "wire_bytes": rb, "bits_on_wire": round(8.0 * rb / db, 3),
-                      **{k: round(_time_us(torch, stream, f, steps), 3) for k, f in parts.items()}}
-        del b, ws, words, mean
+                      **{k: round(_time_us(torch, stream, f, steps), 3) for k, f in parts.items()},
+                      "with_skip": {
+                          "us": round(t_skip, 3),
+                          **{k: round(_time_us(torch, stream, skip_parts[k], steps), 3)
+                             for k in ("norm_term_bounds_us", "compress_words_skip_us")}}}
+        del b, ws, words, mean, bounds
     return out
 
 
@@ -306,33 +327,52 @@ def words_report(gq, torch, w, xd, stream, steps, norm, mean):
     32-bit word, so that a native uint32 SUM all-reduce adds the codes.
     Times the codes of all n rows, the word-wise sum over the rows (the
     all-reduce's arithmetic, on one device), the same summed row in one pass
-    (what a device holding the n rows sends), and the dequantization, with
-    bits on the wire per coordinate against an int32 container."""
+    (what a device holding the n rows sends) reading every coordinate and
+    with the zero-code skip (given the term-and-bounds pass, timed too), and
+    the dequantization, with bits on the wire per coordinate against an int32
+    container.  The skipped row is checked equal to the dense one."""
     n, d = w.n, w.d
     W = gq.gq_min_code_bits(n, w.s, w.scheme)
     rb = gq.gq_word_row_bytes(d, W)
     words = torch.empty((n, rb // 4), dtype=torch.int32, device=xd.device)
     wsum = torch.empty(rb // 4, dtype=torch.int32, device=xd.device)
+    wskip = torch.empty(rb // 4, dtype=torch.int32, device=xd.device)
+    term = torch.empty(1, dtype=torch.float64, device=xd.device)
+    bounds = torch.empty(gq.gq_span_bounds_bytes(n, d), dtype=torch.uint8, device=xd.device)
+    ws = torch.empty(gq.gq_workspace_bytes(n, d), dtype=torch.uint8, device=xd.device)
+    gq.gq_norm_term_bounds(xd, w.q, w.p, term=term, bounds=bounds, workspace=ws, stream=stream)
     parts = {
         "quantize_words_us": lambda st: gq.gq_quantize_words(xd, w.s, w.scheme, norm, w.seed, W,
                                                              words=words, stream=st),
         "sum_words_us": lambda st: gq.gq_sum_words(words, n, d, W, word_sum=wsum, stream=st),
         "compress_words_us": lambda st: gq.gq_compress_words_from_norm(
             xd, w.s, w.scheme, norm, w.seed, W, word_sum=wsum, stream=st),
+        "norm_term_bounds_us": lambda st: gq.gq_norm_term_bounds(
+            xd, w.q, w.p, term=term, bounds=bounds, workspace=ws, stream=st),
+        "compress_words_skip_us": lambda st: gq.gq_compress_words_skip(
+            xd, w.s, w.scheme, norm, bounds, w.seed, W, word_sum=wskip, stream=st),
         "dequantize_words_us": lambda st: gq.gq_dequantize_words(wsum, n, d, w.s, w.scheme, W,
                                                                  norm, mean=mean, stream=st),
     }
     out = {"code_bits": W, "fields_per_word": 32 // W, "bits_on_wire": 8.0 * rb / d,
            "row_bytes": rb}
     in_bytes = n * d * w.elem_bytes
+    # the skip's rate is still quoted over the input it stands for
     alg = {"quantize_words_us": in_bytes + n * rb, "sum_words_us": (n + 1) * rb,
            "compress_words_us": in_bytes + rb,
+           "norm_term_bounds_us": in_bytes + gq.gq_span_bounds_bytes(n, d),
+           "compress_words_skip_us": in_bytes + rb,
            "dequantize_words_us": rb + 4 * d}
     for k, f in parts.items():
         t = _time_us(torch, stream, f, steps)
         out[k] = round(t, 3)
         out[k.replace("_us", "_alg_GBs")] = round(alg[k] / (t * 1e-6) / 1e9, 1)
-    del words, wsum
+    torch.cuda.synchronize()
+    out["skip_row_equals_dense"] = bool(torch.equal(wskip, wsum))
+    out["device_step_us"] = {
+        "reading_every_coordinate": round(out["norm_term_bounds_us"] + out["compress_words_us"], 3),
+        "with_the_skip": round(out["norm_term_bounds_us"] + out["compress_words_skip_us"], 3)}
+    del words, wsum, wskip, bounds, ws
     return out
 
 

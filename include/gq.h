@@ -266,6 +266,26 @@ int32_t gq_compress_mean_skip(const void *x, int32_t dtype, int64_t n, int64_t d
                               const uint16_t *bounds, int32_t code_bits, float *mean,
                               void *code_sum_or_null, void *stream);
 
+/* The zero-code skip for sharded workers, where each device sums its own
+ * rows into the word layout (Sec. 6's integer Allreduce over devices):
+ *   gq_norm_term_bounds: gq_norm_term (same term, same workspace rule) and
+ *     the span bounds of the device's n rows, as gq_global_norm_bounds
+ *     writes them (row i of the shard is bounds row i).
+ *   gq_compress_words_skip: gq_compress_words_from_norm (same arguments,
+ *     same word row, bit for bit) given N in norm_dev[0] -- the global norm,
+ *     from gq_norm_from_term of the combined terms -- and those bounds for
+ *     this shard's x.  Groups are skipped as in gq_compress_mean_skip; the
+ *     rows' worker indices worker_base + i enter the draws as there.
+ * Errors as gq_norm_term and gq_compress_words_from_norm, plus GQ_ERR_NULL
+ * for a NULL bounds (d > 0) and GQ_ERR_ALIGN for one not 16-byte aligned. */
+int32_t gq_norm_term_bounds(const void *x, int32_t dtype, int64_t n, int64_t d, float q, float p,
+                            double *term_dev, uint16_t *bounds, void *workspace,
+                            int64_t workspace_bytes, void *stream);
+int32_t gq_compress_words_skip(const void *x, int32_t dtype, int64_t n, int64_t d, int32_t s,
+                               int32_t scheme, const float *norm_dev, const uint16_t *bounds,
+                               uint64_t seed, int64_t worker_base, int32_t code_bits,
+                               void *word_sum, void *stream);
+
 /* The whole path: gq_global_norm, then gq_compress_mean_from_norm.
  * Writes N to norm_dev[0] and the dequantized mean to mean[0..d).  With a
  * workspace of gq_compress_workspace_bytes(n, d) it runs as

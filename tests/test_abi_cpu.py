@@ -187,6 +187,22 @@ def test_zero_code_skip_sizes_and_rejects():
     assert L.gq_compress_mean_skip(A, 0, 4, 100, 7, 0, 1, A, B, 0, U, NUL, NUL) == 6
     assert L.gq_compress_mean_skip(A, 0, 4, 100, 7, 0, 1, A, B, 5, A, A, NUL) == 4
     assert L.gq_compress_mean_skip(A, 0, 4, 100, 0, 0, 1, A, B, 0, A, NUL, NUL) == 2
+    # the sharded form: gq_norm_term_bounds(x, dtype, n, d, q, p, term, bounds, ws, ws_bytes,
+    # stream) and gq_compress_words_skip(x, dtype, n, d, s, scheme, norm, bounds, seed,
+    # worker_base, W, word_sum, stream)
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert L.gq_norm_term_bounds(A, 0, 4, 100, 2.0, 2.0, NUL, B, A, ws, NUL) == 1
+    assert L.gq_norm_term_bounds(A, 0, 4, 100, 2.0, 2.0, A, NUL, A, ws, NUL) == 1
+    assert L.gq_norm_term_bounds(A, 0, 4, 100, 2.0, 2.0, A, odd, A, ws, NUL) == 6
+    assert L.gq_norm_term_bounds(A, 0, 4, 100, 0.5, 2.0, A, B, A, ws, NUL) == 3
+    assert L.gq_norm_term_bounds(A, 0, 4, 100, 2.0, 2.0, A, B, A, ws - 1, NUL) == 5
+    assert L.gq_compress_words_skip(A, 0, 4, 100, 7, 0, A, NUL, 1, 0, 6, A, NUL) == 1
+    assert L.gq_compress_words_skip(A, 0, 4, 100, 7, 0, NUL, B, 1, 0, 6, A, NUL) == 1
+    assert L.gq_compress_words_skip(A, 0, 4, 100, 7, 0, A, odd, 1, 0, 6, A, NUL) == 6
+    assert L.gq_compress_words_skip(A, 0, 4, 100, 7, 0, A, B, 1, 0, 6, U, NUL) == 6
+    assert L.gq_compress_words_skip(A, 0, 4, 100, 7, 0, A, B, 1, 0, 5, A, NUL) == 4
+    assert L.gq_compress_words_skip(A, 0, 4, 100, 7, 0, A, B, 1, (1 << 32) - 3, 6, A, NUL) == 2
+    assert L.gq_compress_words_skip(A, 0, 4, 100, 7, 5, A, B, 1, 0, 6, A, NUL) == 2
 
 
 def test_noalloc_entry_point_rejects():

@@ -119,6 +119,7 @@ CASES = [
     (8, 100_000, "bf16", "L", 15, 2.0, 2.0, "heavy"),
     (4, 4096, "f32", "L", 1, 2.0, 2.0, "mixed"),
     (3, 9000, "f32", "L", 127, 1.5, 3.0, "mixed"),
+    (600, 2500, "f32", "E", 16, 2.0, 2.0, "mixed"),  # n M > 2^24: the int32 accumulator
 ]
 
 
