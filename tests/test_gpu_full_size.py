@@ -14,8 +14,9 @@ come from the launch configuration the benchmark times.
   minimal and at the container width, their integer sum
   (`gq_reduce_codes`), and the mean from it (`gq_dequantize`).
 - **Word layout.** Every worker's words (`gq_quantize_words`), their
-  word-wise sum (`gq_sum_words`), the one-pass row
-  (`gq_compress_words_from_norm`) and the mean from it
+  word-wise sum (`gq_sum_words`), the one-pass row reading every
+  coordinate (`gq_compress_words_from_norm`) and with the zero-code skip
+  (`gq_norm_term_bounds`, `gq_compress_words_skip`), and the mean from it
   (`gq_dequantize_words`), all at the minimal width.
 - **The pages' 8-bit format.** Every worker's code bytes
   (`gq_e8_quantize`); the root of the re-rounding tree, unfused and fused
@@ -215,10 +216,13 @@ def test_every_coordinate(key):
     assert np.array_equal(host(wsum).view(np.uint32), owsum), "summed words differ"
     one = gq.gq_compress_words_from_norm(xd, s, w.scheme, norm, seed, Wmin)
     assert np.array_equal(host(one).view(np.uint32), owsum), "one-pass word row differs"
+    _, tb = gq.gq_norm_term_bounds(xd, w.q, w.p)
+    skip = gq.gq_compress_words_skip(xd, s, w.scheme, norm, tb, seed, Wmin)
+    assert np.array_equal(host(skip).view(np.uint32), owsum), "skipped word row differs"
     wmean = gq.gq_dequantize_words(one, n, d, s, w.scheme, Wmin, norm)
     assert same_bytes(host(wmean), omean), "mean from the words differs"
-    compared += 3 * d
-    del gwords, owords, wsum, one, wmean
+    compared += 4 * d
+    del gwords, owords, wsum, one, wmean, skip, tb
 
     # ---- the pages' 8-bit format: root of the re-rounding tree and the mean
     if e8n:
