@@ -560,10 +560,11 @@ __device__ __forceinline__ void wave_lds_fence()
 // 8*t + k) into one packed row.  W = 8/16/32: direct vector stores.  Other
 // W: each wave assembles its whole words in LDS and writes them with 16-byte
 // stores.  Every thread of the block must call this.  Bytes past the row's
-// end are never written; pad fields are zero.
+// end are never written; pad fields are zero.  wave_lds, if given, is this
+// wave's own region of at least 16 W words (else lds + wave 16 W).
 template <bool NT = true>
 __device__ __forceinline__ void store_tile_packed(uint32_t *lds, const int (&val)[kPer], int W, uint8_t *row,
-                                  int64_t tile, int64_t rbytes)
+                                  int64_t tile, int64_t rbytes, uint32_t *wave_lds = nullptr)
 {
     const int t = threadIdx.x;
     const int64_t j0 = tile * kTile + (int64_t)t * kPer;
@@ -619,7 +620,7 @@ __device__ __forceinline__ void store_tile_packed(uint32_t *lds, const int (&val
     // may straddle two words), then writes the region out as 16-byte stores.
     const int lane = t & 63, wave = t >> 6;
     const int nw = 16 * W;
-    uint32_t *wl = lds + wave * nw;
+    uint32_t *wl = wave_lds ? wave_lds : lds + wave * nw;
     for (int j = lane; j < nw; j += 64)
         wl[j] = 0u;
     wave_lds_fence();
@@ -731,6 +732,14 @@ __device__ __forceinline__ float wave_max(float v)
     for (int off = 32; off > 0; off >>= 1)
         v = fmaxf(v, __shfl_xor(v, off));
     return v;
+}
+
+// acc + v^2 in fp64 as one fused multiply-add: the square of a float (24
+// significant bits) is exact in fp64, so the fused form rounds the same
+// single sum as a separate product and add would.
+__device__ __forceinline__ double add_square(double acc, float v)
+{
+    return fma((double)v, (double)v, acc);
 }
 
 // Span bounds.  The largest |x| of 8 widened inputs as an ordered integer:
@@ -854,10 +863,10 @@ __global__ __launch_bounds__(kThreads) void k_norm_partial(const void *__restric
                 mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v0[k]), fabsf(v1[k])),
                                      fmaxf(fabsf(v2[k]), fabsf(v3[k]))));
             } else if (QM == 0) {
-                s0 += (double)v0[k] * (double)v0[k];
-                s1 += (double)v1[k] * (double)v1[k];
-                s0 += (double)v2[k] * (double)v2[k];
-                s1 += (double)v3[k] * (double)v3[k];
+                s0 = add_square(s0, v0[k]);
+                s1 = add_square(s1, v1[k]);
+                s0 = add_square(s0, v2[k]);
+                s1 = add_square(s1, v3[k]);
             } else {
                 s0 += pow(fabs((double)v0[k]), qd);
                 s1 += pow(fabs((double)v1[k]), qd);
@@ -914,7 +923,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_partial(const void *__restric
             if (QINF)
                 mx = fmaxf(mx, fabsf(v[k]));
             else if (QM == 0)
-                s0 += (double)v[k] * (double)v[k];
+                s0 = add_square(s0, v[k]);
             else
                 s0 += pow(fabs((double)v[k]), qd);
         }
@@ -1014,8 +1023,8 @@ __global__ __launch_bounds__(kOsThreads) void k_norm_oneshot(const void *__restr
             if (QINF) {
                 mx = fmaxf(mx, fmaxf(fabsf(v[u][k]), fabsf(v[u][k + 1])));
             } else if (QM == 0) {
-                s0 += (double)v[u][k] * (double)v[u][k];
-                s1 += (double)v[u][k + 1] * (double)v[u][k + 1];
+                s0 = add_square(s0, v[u][k]);
+                s1 = add_square(s1, v[u][k + 1]);
             } else {
                 s0 += pow(fabs((double)v[u][k]), qd);
                 s1 += pow(fabs((double)v[u][k + 1]), qd);
@@ -1327,10 +1336,140 @@ __device__ __forceinline__ void quant_group_sparse(const float (&v)[kPer], const
     tie |= ((uint16_t)mx == 0xFFFFu) | ((uint16_t)max3_lo16(S[3], S[4], S[5]) == 0xFFFFu);
 }
 
+// Candidate queue of the zero-code skip.  A sparse row is tested with one
+// Philox block per lane (its group), and only now and then does a lane's
+// group pass h <= H; quantized in its own lane, that group would run the
+// load and the quantization with the rest of the wave masked off.  Instead
+// each wave queues its passing (row, group) pairs with their draw-0 blocks
+// in LDS, and whenever 64 are waiting every lane takes one: it loads the
+// group, quantizes it and adds its non-zero codes to the span's 512 integer
+// sums in LDS (integer atomic adds: exact in any order).  The queue is
+// drained after every step of two rows, which add at most 128 entries to at
+// most 63 waiting, so 256 slots suffice.
+constexpr int kQueue = 256;
+struct SkipQueue {
+    uint4 A[kQueue];  // draw-0 block of the entry
+    uint2 rg[kQueue]; // row, group of the span (0..63)
+    int sum[kSpan];   // queued codes summed per coordinate of the span
+};
+
+// One queue per wave of the block, shared by every instantiation in a kernel
+// (a kernel that never asks for it allocates no LDS for it).
+__device__ __forceinline__ SkipQueue &wave_skip_queue()
+{
+    __shared__ SkipQueue queues[kThreads / 64];
+    return queues[threadIdx.x >> 6];
+}
+
+template <bool QUEUE>
+__device__ __forceinline__ SkipQueue *wave_skip_queue_if()
+{
+    if constexpr (QUEUE)
+        return &wave_skip_queue();
+    else
+        return nullptr;
+}
+
+// Rows from which the fused pass queues candidates (skip mode 2): with fewer
+// the queue's drains run half-empty (measured on 8 rows: +3-6% against
+// candidates in their own lanes; 16 rows: -7%, 64 rows: -7%).
+constexpr int64_t kQueueMinRows = 16;
+
+// Lanes < count each take entry head + lane of the queue.
+template <int DT, int SCH, bool PRE>
+__device__ __forceinline__ void drain_queue(SkipQueue &sq, uint32_t head, uint32_t count,
+                                            const void *__restrict__ x, int64_t d, int64_t span,
+                                            bool vec, const QParams &q, float sigK, uint32_t k0,
+                                            uint32_t k1, uint32_t wb)
+{
+    const uint32_t lane = threadIdx.x & 63;
+    if (lane < count) {
+        const uint32_t e = (head + lane) % kQueue;
+        const uint4 A = sq.A[e];
+        const uint2 rg = sq.rg[e];
+        const int64_t jg = span * kSpan + 8 * (int64_t)rg.y;
+        float v[kPer], m[kPer];
+        bool tie = false;
+        load_group<DT>(x, (int64_t)rg.x * d, jg, d, vec, v);
+        quant_group_sparse<PRE>(v, A, q, sigK, m, tie);
+        if (tie) {
+            const uint4 B = philox10(make_uint4((uint32_t)((uint64_t)jg >> 3),
+                                                (uint32_t)((uint64_t)jg >> 35), wb + rg.x, 1u),
+                                     k0, k1);
+            settle_ties<SCH, PRE>(v, A, B, q, m);
+        }
+        // every code, zeros included: no per-coordinate branches (measured
+        // 1-3% faster than adding only the non-zero ones)
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            atomicAdd(&sq.sum[8 * rg.y + k], (int)copysignf(m[k], v[k]));
+    }
+}
+
+// The wave's queue state: entries [head, tail) wait (wave-uniform counts).
+template <int DT, int SCH, bool PRE>
+struct SkipQueueWalk {
+    SkipQueue *sq;
+    const void *__restrict__ x;
+    int64_t d, span;
+    bool vec;
+    const QParams &q;
+    float sigK;
+    uint32_t k0, k1, wb;
+    uint32_t head = 0, tail = 0;
+
+    __device__ __forceinline__ void start()
+    {
+        const int b = 8 * (int)(threadIdx.x & 63);
+        *(int4 *)&sq->sum[b] = make_int4(0, 0, 0, 0);
+        *(int4 *)&sq->sum[b + 4] = make_int4(0, 0, 0, 0);
+        wave_lds_fence();
+    }
+    // Row i of a sparse span: queue the lanes whose group passes.
+    __device__ __forceinline__ void offer(int64_t i, bool cand, const uint4 &A)
+    {
+        const uint64_t mask = __ballot(cand);
+        if (cand) {
+            const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+            const uint32_t e = (tail + below) % kQueue;
+            sq->A[e] = A;
+            sq->rg[e] = make_uint2((uint32_t)i, threadIdx.x & 63);
+        }
+        tail += (uint32_t)__popcll(mask);
+    }
+    // Between steps: every lane busy while 64 or more entries wait.
+    __device__ __forceinline__ void drain_full()
+    {
+        while (tail - head >= 64) {
+            wave_lds_fence();
+            drain_queue<DT, SCH, PRE>(*sq, head, 64, x, d, span, vec, q, sigK, k0, k1, wb);
+            head += 64;
+            wave_lds_fence();
+        }
+    }
+    // After the last row: drain the rest; returns this lane's 8 queued sums.
+    __device__ __forceinline__ void finish(int (&qs)[kPer])
+    {
+        drain_full();
+        wave_lds_fence();
+        if (tail != head)
+            drain_queue<DT, SCH, PRE>(*sq, head, tail - head, x, d, span, vec, q, sigK, k0, k1, wb);
+        wave_lds_fence();
+        const int b = 8 * (int)(threadIdx.x & 63);
+        const int4 s0 = *(const int4 *)&sq->sum[b], s1 = *(const int4 *)&sq->sum[b + 4];
+        qs[0] = s0.x; qs[1] = s0.y; qs[2] = s0.z; qs[3] = s0.w;
+        qs[4] = s1.x; qs[5] = s1.y; qs[6] = s1.z; qs[7] = s1.w;
+        wave_lds_fence(); // the next call's clearing comes after these reads
+    }
+};
+
 // accumulate_workers with the zero-code skip: every lane of the wave must be
 // here (the thresholds are shared through lane reads); `live` marks lanes
-// whose group is inside the row.  Rows of a dense span take quant_group.
-template <int DT, int SCH, bool PRE, bool FACC>
+// whose group is inside the row.  Rows of a dense span take quant_group in
+// every lane.  The passing groups of sparse rows are quantized in their own
+// lanes, or with QUEUE through the wave's candidate queue.
+template <int DT, int SCH, bool PRE, bool FACC, bool QUEUE>
 __device__ __forceinline__ void accumulate_workers_skip(const void *__restrict__ x, int64_t n,
                                                         int64_t d, int64_t j0, bool vec,
                                                         bool live, const QParams &q,
@@ -1340,30 +1479,37 @@ __device__ __forceinline__ void accumulate_workers_skip(const void *__restrict__
                                                         bool sparse_ok, float (&accf)[kPer],
                                                         int (&acci)[kPer], uint32_t wb = 0)
 {
+    SkipQueueWalk<DT, SCH, PRE> walk{wave_skip_queue_if<QUEUE>(), x, d, span, vec, q, sigK, k0, k1,
+                                     wb};
+    if (QUEUE)
+        walk.start();
     const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
-    // one worker's group: quantize and add it when it may hold a non-zero code
-    auto row = [&](int64_t i, uint32_t H, const uint4 &A) {
-        const bool dense = H > 0xFFFFu;
-        if (live && (dense || min_half16(A) <= H)) {
-            float v[kPer], m[kPer];
-            bool tie = false;
-            load_group<DT>(x, i * d, j0, d, vec, v);
-            if (dense)
-                quant_group<SCH, PRE, false>(v, A, q, m, tie);
-            else
-                quant_group_sparse<PRE>(v, A, q, sigK, m, tie);
-            if (tie) {
-                const uint4 B = philox10(make_uint4(blo, bhi, wb + (uint32_t)i, 1u), k0, k1);
-                settle_ties<SCH, PRE>(v, A, B, q, m);
-            }
-#pragma unroll
-            for (int k = 0; k < kPer; ++k) {
-                if (FACC)
-                    accf[k] = fmaf(copysignf(1.0f, v[k]), m[k], accf[k]);
-                else
-                    acci[k] += (int)copysignf(m[k], v[k]);
-            }
+    // one worker's group in its own lane
+    auto own = [&](int64_t i, bool dense, const uint4 &A) {
+        float v[kPer], m[kPer];
+        bool tie = false;
+        load_group<DT>(x, i * d, j0, d, vec, v);
+        if (dense)
+            quant_group<SCH, PRE, false>(v, A, q, m, tie);
+        else
+            quant_group_sparse<PRE>(v, A, q, sigK, m, tie);
+        if (tie) {
+            const uint4 B = philox10(make_uint4(blo, bhi, wb + (uint32_t)i, 1u), k0, k1);
+            settle_ties<SCH, PRE>(v, A, B, q, m);
         }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            if (FACC)
+                accf[k] = fmaf(copysignf(1.0f, v[k]), m[k], accf[k]);
+            else
+                acci[k] += (int)copysignf(m[k], v[k]);
+        }
+    };
+    auto row = [&](int64_t i, uint32_t H, const uint4 &A) {
+        if (QUEUE && H <= 0xFFFFu)
+            walk.offer(i, live && min_half16(A) <= H, A);
+        else if (live && (H > 0xFFFFu || min_half16(A) <= H))
+            own(i, H > 0xFFFFu, A);
     };
     for (int64_t c = 0; c < n; c += 64) {
         const uint32_t Hl = span_threshold<PRE>(bounds, bstride, span, c, n, q, sigK, sparse_ok);
@@ -1376,10 +1522,23 @@ __device__ __forceinline__ void accumulate_workers_skip(const void *__restrict__
             const uint4 A1 = philox10(make_uint4(blo, bhi, wb + (uint32_t)(c + r + 1), 0u), k0, k1);
             row(c + r, __builtin_amdgcn_readlane(Hl, r), A0);
             row(c + r + 1, __builtin_amdgcn_readlane(Hl, r + 1), A1);
+            if (QUEUE)
+                walk.drain_full();
         }
         if (r < cnt)
             row(c + r, __builtin_amdgcn_readlane(Hl, r),
                 philox10(make_uint4(blo, bhi, wb + (uint32_t)(c + r), 0u), k0, k1));
+    }
+    if (QUEUE) {
+        int qs[kPer];
+        walk.finish(qs);
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            if (FACC)
+                accf[k] += (float)qs[k]; // integers below 2^24: exact
+            else
+                acci[k] += qs[k];
+        }
     }
 }
 
@@ -1508,9 +1667,11 @@ __device__ __forceinline__ void accumulate_workers_pk16(const void *__restrict__
         acc[2 * p + 1] = acc2[p].y;
     }
 }
-// SKIP: with pass 1's span bounds (u16 [n][bstride]), groups whose codes are
-// provably all 0 are neither loaded nor quantized (the zero-code skip).
-template <int DT, int SCH, int ACC, bool SKIP>
+// SKIP 1 or 2: with pass 1's span bounds (u16 [n][bstride]), groups whose
+// codes are provably all 0 are neither loaded nor quantized (the zero-code
+// skip); 2 quantizes the remaining groups of sparse rows through the wave's
+// candidate queue, 1 in their own lanes.
+template <int DT, int SCH, int ACC, int SKIP>
 __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restrict__ x, int64_t n,
                                                             int64_t d, int s, uint64_t seed,
                                                             const float *__restrict__ norm_dev,
@@ -1524,7 +1685,9 @@ __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restri
     // measured -6% on this pass for fp32 at 0.8-16 GB (4 and 5 blocks alike,
     // 6 no gain); bf16, bound by vector ALU work, needs the full residency
     // (5 blocks: +15%).  Only the code-sum packing uses the first 8 KB.
-    __shared__ alignas(16) uint32_t lds[DT == GQ_IN_F32 && !SKIP ? 8192 : kTile];
+    // With the candidate queue each wave packs in its own queue (free by then).
+    constexpr bool QUEUED = SKIP == 2 && ACC != kAccPk16;
+    __shared__ alignas(16) uint32_t lds[QUEUED ? 4 : DT == GQ_IN_F32 && !SKIP ? 8192 : kTile];
     // Reverse of pass 1's order: pass 1's blocks finish on the last chunks of
     // every row, so starting pass 2 there re-reads data the memory-side cache
     // still holds (measured: -7% time on an 0.8 GB input, neutral on 7-16 GB).
@@ -1550,10 +1713,10 @@ __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restri
                     accumulate_workers_pk16<DT, false, true>(x, n, d, j0, vec, q, k0, k1, acc, 0u,
                                                              live, bounds, bstride, span, sparse_ok);
             } else if (q.prescale)
-                accumulate_workers_skip<DT, SCH, true, ACC == kAccF32>(
+                accumulate_workers_skip<DT, SCH, true, ACC == kAccF32, QUEUED>(
                     x, n, d, j0, vec, live, q, k0, k1, bounds, bstride, span, sigK, sparse_ok, accf, acc);
             else
-                accumulate_workers_skip<DT, SCH, false, ACC == kAccF32>(
+                accumulate_workers_skip<DT, SCH, false, ACC == kAccF32, QUEUED>(
                     x, n, d, j0, vec, live, q, k0, k1, bounds, bstride, span, sigK, sparse_ok, accf, acc);
             if (ACC == kAccF32) {
 #pragma unroll
@@ -1587,7 +1750,8 @@ __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restri
         store_mean8(mean, j0, d, m);
     }
     if (code_sum)
-        store_tile_packed(lds, acc, W, code_sum, tile, row_bytes(d, W));
+        store_tile_packed(lds, acc, W, code_sum, tile, row_bytes(d, W),
+                          QUEUED ? (uint32_t *)wave_skip_queue().sum : nullptr);
 }
 
 // Many workers (n >= kSums8MinN, fp32): the compress step in two kernels.
@@ -2057,9 +2221,10 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_words_lds(
 // (ACC as in k_compress_mean: fp32 sums, int32, or packed 16-bit pairs for
 // bf16 standard dithering), then the biased sums go to LDS and are
 // assembled into word quads as in k_quantize_words.
-// SKIP: with pass 1's span bounds, as the fused pass (each 2048-coordinate
-// segment is one fused-pass tile: a wave per 512-coordinate span).
-template <int DT, int SCH, int FPW, int ACC, bool SKIP>
+// SKIP 1 or 2: with pass 1's span bounds, as the fused pass (each
+// 2048-coordinate segment is one fused-pass tile: a wave per 512-coordinate
+// span).
+template <int DT, int SCH, int FPW, int ACC, int SKIP>
 __global__ __launch_bounds__(kThreads) void k_compress_words(const void *__restrict__ x, int64_t n,
                                                              int64_t d, int s, uint64_t seed,
                                                              int64_t worker_base,
@@ -2097,11 +2262,11 @@ __global__ __launch_bounds__(kThreads) void k_compress_words(const void *__restr
             } else {
                 float accf[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
                 if (q.prescale)
-                    accumulate_workers_skip<DT, SCH, true, ACC == kAccF32>(
+                    accumulate_workers_skip<DT, SCH, true, ACC == kAccF32, SKIP == 2>(
                         x, n, d, j0, vec, live, q, k0, k1, bounds, bstride, span, sigK, sparse_ok,
                         accf, acc, wb);
                 else
-                    accumulate_workers_skip<DT, SCH, false, ACC == kAccF32>(
+                    accumulate_workers_skip<DT, SCH, false, ACC == kAccF32, SKIP == 2>(
                         x, n, d, j0, vec, live, q, k0, k1, bounds, bstride, span, sigK, sparse_ok,
                         accf, acc, wb);
                 if (ACC == kAccF32) {
@@ -2171,7 +2336,9 @@ __global__ __launch_bounds__(kThreads) void k_compress_words(const void *__restr
 // 16-bit pairs for bf16 standard dithering with n M < 2^15, else fp32 sums
 // while n M <= 2^24 (always true for W <= 16), else int32.
 // bounds != nullptr: the zero-code skip with pass 1's span bounds.
-template <int DT, int SCH, int F, bool SKIP>
+// SKIP: 0 none, 1 candidates in their own lanes, 2 through the queue (the
+// packed accumulators keep their own lanes).
+template <int DT, int SCH, int F, int SKIP>
 void launch_compress_words_as(dim3 grid, hipStream_t st, bool pk16, bool facc, const void *x,
                               int64_t n, int64_t d, int s, uint64_t seed, int64_t worker_base,
                               const float *norm_dev, uint32_t *out, int W, uint32_t bias,
@@ -2180,7 +2347,7 @@ void launch_compress_words_as(dim3 grid, hipStream_t st, bool pk16, bool facc, c
     const dim3 block(kThreads);
     if constexpr (DT == GQ_IN_BF16 && SCH == GQ_SCHEME_L && F > 1) {
         if (pk16) {
-            k_compress_words<DT, SCH, F, kAccPk16, SKIP><<<grid, block, 0, st>>>(
+            k_compress_words<DT, SCH, F, kAccPk16, SKIP ? 1 : 0><<<grid, block, 0, st>>>(
                 x, n, d, s, seed, worker_base, norm_dev, out, W, bias, rwords, bounds, bstride);
             return;
         }
@@ -2204,14 +2371,18 @@ void launch_compress_words(dim3 grid, hipStream_t st, bool pk16, bool facc, cons
                            const float *norm_dev, uint32_t *out, int W, uint32_t bias,
                            int64_t rwords, const uint16_t *bounds)
 {
-    if (bounds)
-        launch_compress_words_as<DT, SCH, F, true>(grid, st, pk16, facc, x, n, d, s, seed,
-                                                   worker_base, norm_dev, out, W, bias, rwords,
-                                                   bounds, bound_stride(d));
+    if (bounds && n >= kQueueMinRows)
+        launch_compress_words_as<DT, SCH, F, 2>(grid, st, pk16, facc, x, n, d, s, seed,
+                                                worker_base, norm_dev, out, W, bias, rwords,
+                                                bounds, bound_stride(d));
+    else if (bounds)
+        launch_compress_words_as<DT, SCH, F, 1>(grid, st, pk16, facc, x, n, d, s, seed,
+                                                worker_base, norm_dev, out, W, bias, rwords,
+                                                bounds, bound_stride(d));
     else
-        launch_compress_words_as<DT, SCH, F, false>(grid, st, pk16, facc, x, n, d, s, seed,
-                                                    worker_base, norm_dev, out, W, bias, rwords,
-                                                    nullptr, 0);
+        launch_compress_words_as<DT, SCH, F, 0>(grid, st, pk16, facc, x, n, d, s, seed,
+                                                worker_base, norm_dev, out, W, bias, rwords,
+                                                nullptr, 0);
 }
 
 // What a native integer SUM over the n rows computes: the word-wise sum
@@ -2998,15 +3169,20 @@ int32_t launch_compress(const void *x, int32_t dtype, int64_t n, int64_t d, int3
     const int64_t nm = n * top_code(s, scheme);
     const bool facc = nm <= ((int64_t)1 << 24);
     const bool pk16 = dtype == GQ_IN_BF16 && scheme == GQ_SCHEME_L && nm < ((int64_t)1 << 15);
+    // skip modes as in k_compress_mean: the queue from kQueueMinRows rows
+    // (never for the packed accumulators)
+    const bool queue = n >= kQueueMinRows;
 #define GQ_COMPRESS(DT, SCH, ACC)                                                                 \
     do {                                                                                          \
-        if (bounds)                                                                               \
-            k_compress_mean<DT, SCH, ACC, true><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, \
-                                                                        mean, cs, W, bounds, bstride); \
+        if (bounds && queue && ACC != kAccPk16)                                                   \
+            k_compress_mean<DT, SCH, ACC, ACC == kAccPk16 ? 1 : 2><<<grid, block, 0, st>>>(        \
+                x, n, d, s, seed, norm_dev, mean, cs, W, bounds, bstride);                        \
+        else if (bounds)                                                                          \
+            k_compress_mean<DT, SCH, ACC, 1><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev,  \
+                                                                     mean, cs, W, bounds, bstride); \
         else                                                                                      \
-            k_compress_mean<DT, SCH, ACC, false><<<grid, block, 0, st>>>(x, n, d, s, seed,         \
-                                                                         norm_dev, mean, cs, W,   \
-                                                                         nullptr, 0);             \
+            k_compress_mean<DT, SCH, ACC, 0><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev,  \
+                                                                     mean, cs, W, nullptr, 0);    \
     } while (0)
 #define GQ_COMPRESS_DT(DT)                          \
     do {                                            \
