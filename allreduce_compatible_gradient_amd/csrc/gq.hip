@@ -718,12 +718,35 @@ __device__ __forceinline__ void load_tile_fields(uint32_t *lds, const uint8_t *r
     wave_lds_fence();
 }
 
+// One DPP move of a double (both halves, the same pattern; every source lane
+// of the patterns used here lies in the same row of 16).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the wave (every lane active), in a fixed order: within each row
+// of 16 lanes the partners lane ^ 1, lane ^ 2, the mirrored 8-lane half and
+// the mirrored row (each lane adds the same two values, so every lane of a
+// row ends with the row's sum), then the four rows read from lanes 0, 16, 32
+// and 48 and added as (r0 + r1) + (r2 + r3).  The result is in every lane.
 __device__ __forceinline__ double wave_sum(double v)
 {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        v += __shfl_xor(v, off);
-    return v;
+    v += dpp_f64<0xB1>(v);  // quad_perm 1,0,3,2
+    v += dpp_f64<0x4E>(v);  // quad_perm 2,3,0,1
+    v += dpp_f64<0x141>(v); // row_half_mirror
+    v += dpp_f64<0x140>(v); // row_mirror
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    auto row = [&](int lane) {
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, lane);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), lane);
+        return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+    };
+    return (row(0) + row(16)) + (row(32) + row(48));
 }
 
 __device__ __forceinline__ float wave_max(float v)
@@ -1340,40 +1363,26 @@ __device__ __forceinline__ void quant_group_sparse(const float (&v)[kPer], const
 // Philox block per lane (its group), and only now and then does a lane's
 // group pass h <= H; quantized in its own lane, that group would run the
 // load and the quantization with the rest of the wave masked off.  Instead
-// each wave queues its passing (row, group) pairs with their draw-0 blocks
-// in LDS, and whenever 64 are waiting every lane takes one: it loads the
-// group, quantizes it and adds its non-zero codes to the span's 512 integer
-// sums in LDS (integer atomic adds: exact in any order).  The queue is
-// drained after every step of two rows, which add at most 128 entries to at
-// most 63 waiting, so 256 slots suffice.
+// each wave queues its passing (row, group) pairs in LDS, and whenever 64
+// are waiting every lane takes one: it draws the group's block again, loads
+// the group, quantizes it and adds its codes to the span's 512 integer sums
+// in LDS (integer atomic adds: exact in any order).  Drawing again costs
+// less than keeping the blocks: 16 KB of LDS per block instead of 32 KB
+// leaves room for more waves (measured 2-7% faster).  The queue is drained
+// after every step of two rows, which add at most 128 entries to at most 63
+// waiting, so 256 slots suffice.
 constexpr int kQueue = 256;
 struct SkipQueue {
-    uint4 A[kQueue];  // draw-0 block of the entry
     uint2 rg[kQueue]; // row, group of the span (0..63)
     int sum[kSpan];   // queued codes summed per coordinate of the span
 };
 
-// One queue per wave of the block, shared by every instantiation in a kernel
-// (a kernel that never asks for it allocates no LDS for it).
+// One queue per wave of the block, shared by every instantiation in a kernel.
 __device__ __forceinline__ SkipQueue &wave_skip_queue()
 {
     __shared__ SkipQueue queues[kThreads / 64];
     return queues[threadIdx.x >> 6];
 }
-
-template <bool QUEUE>
-__device__ __forceinline__ SkipQueue *wave_skip_queue_if()
-{
-    if constexpr (QUEUE)
-        return &wave_skip_queue();
-    else
-        return nullptr;
-}
-
-// Rows from which the fused pass queues candidates (skip mode 2): with fewer
-// the queue's drains run half-empty (measured on 8 rows: +3-6% against
-// candidates in their own lanes; 16 rows: -7%, 64 rows: -7%).
-constexpr int64_t kQueueMinRows = 16;
 
 // Lanes < count each take entry head + lane of the queue.
 template <int DT, int SCH, bool PRE>
@@ -1385,9 +1394,10 @@ __device__ __forceinline__ void drain_queue(SkipQueue &sq, uint32_t head, uint32
     const uint32_t lane = threadIdx.x & 63;
     if (lane < count) {
         const uint32_t e = (head + lane) % kQueue;
-        const uint4 A = sq.A[e];
         const uint2 rg = sq.rg[e];
         const int64_t jg = span * kSpan + 8 * (int64_t)rg.y;
+        const uint4 A = philox10(make_uint4((uint32_t)((uint64_t)jg >> 3),
+                                            (uint32_t)((uint64_t)jg >> 35), wb + rg.x, 0u), k0, k1);
         float v[kPer], m[kPer];
         bool tie = false;
         load_group<DT>(x, (int64_t)rg.x * d, jg, d, vec, v);
@@ -1426,14 +1436,13 @@ struct SkipQueueWalk {
         wave_lds_fence();
     }
     // Row i of a sparse span: queue the lanes whose group passes.
-    __device__ __forceinline__ void offer(int64_t i, bool cand, const uint4 &A)
+    __device__ __forceinline__ void offer(int64_t i, bool cand)
     {
         const uint64_t mask = __ballot(cand);
         if (cand) {
             const uint32_t below = __builtin_amdgcn_mbcnt_hi(
                 (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
             const uint32_t e = (tail + below) % kQueue;
-            sq->A[e] = A;
             sq->rg[e] = make_uint2((uint32_t)i, threadIdx.x & 63);
         }
         tail += (uint32_t)__popcll(mask);
@@ -1467,9 +1476,9 @@ struct SkipQueueWalk {
 // accumulate_workers with the zero-code skip: every lane of the wave must be
 // here (the thresholds are shared through lane reads); `live` marks lanes
 // whose group is inside the row.  Rows of a dense span take quant_group in
-// every lane.  The passing groups of sparse rows are quantized in their own
-// lanes, or with QUEUE through the wave's candidate queue.
-template <int DT, int SCH, bool PRE, bool FACC, bool QUEUE>
+// every lane; the passing groups of sparse rows go through the wave's
+// candidate queue.
+template <int DT, int SCH, bool PRE, bool FACC>
 __device__ __forceinline__ void accumulate_workers_skip(const void *__restrict__ x, int64_t n,
                                                         int64_t d, int64_t j0, bool vec,
                                                         bool live, const QParams &q,
@@ -1479,20 +1488,15 @@ __device__ __forceinline__ void accumulate_workers_skip(const void *__restrict__
                                                         bool sparse_ok, float (&accf)[kPer],
                                                         int (&acci)[kPer], uint32_t wb = 0)
 {
-    SkipQueueWalk<DT, SCH, PRE> walk{wave_skip_queue_if<QUEUE>(), x, d, span, vec, q, sigK, k0, k1,
-                                     wb};
-    if (QUEUE)
-        walk.start();
+    SkipQueueWalk<DT, SCH, PRE> walk{&wave_skip_queue(), x, d, span, vec, q, sigK, k0, k1, wb};
+    walk.start();
     const uint32_t blo = (uint32_t)((uint64_t)j0 >> 3), bhi = (uint32_t)((uint64_t)j0 >> 35);
-    // one worker's group in its own lane
-    auto own = [&](int64_t i, bool dense, const uint4 &A) {
+    // one worker's group of a dense span, in its own lane
+    auto own = [&](int64_t i, const uint4 &A) {
         float v[kPer], m[kPer];
         bool tie = false;
         load_group<DT>(x, i * d, j0, d, vec, v);
-        if (dense)
-            quant_group<SCH, PRE, false>(v, A, q, m, tie);
-        else
-            quant_group_sparse<PRE>(v, A, q, sigK, m, tie);
+        quant_group<SCH, PRE, false>(v, A, q, m, tie);
         if (tie) {
             const uint4 B = philox10(make_uint4(blo, bhi, wb + (uint32_t)i, 1u), k0, k1);
             settle_ties<SCH, PRE>(v, A, B, q, m);
@@ -1506,10 +1510,10 @@ __device__ __forceinline__ void accumulate_workers_skip(const void *__restrict__
         }
     };
     auto row = [&](int64_t i, uint32_t H, const uint4 &A) {
-        if (QUEUE && H <= 0xFFFFu)
-            walk.offer(i, live && min_half16(A) <= H, A);
-        else if (live && (H > 0xFFFFu || min_half16(A) <= H))
-            own(i, H > 0xFFFFu, A);
+        if (H <= 0xFFFFu)
+            walk.offer(i, live && min_half16(A) <= H);
+        else if (live)
+            own(i, A);
     };
     for (int64_t c = 0; c < n; c += 64) {
         const uint32_t Hl = span_threshold<PRE>(bounds, bstride, span, c, n, q, sigK, sparse_ok);
@@ -1522,23 +1526,20 @@ __device__ __forceinline__ void accumulate_workers_skip(const void *__restrict__
             const uint4 A1 = philox10(make_uint4(blo, bhi, wb + (uint32_t)(c + r + 1), 0u), k0, k1);
             row(c + r, __builtin_amdgcn_readlane(Hl, r), A0);
             row(c + r + 1, __builtin_amdgcn_readlane(Hl, r + 1), A1);
-            if (QUEUE)
-                walk.drain_full();
+            walk.drain_full();
         }
         if (r < cnt)
             row(c + r, __builtin_amdgcn_readlane(Hl, r),
                 philox10(make_uint4(blo, bhi, wb + (uint32_t)(c + r), 0u), k0, k1));
     }
-    if (QUEUE) {
-        int qs[kPer];
-        walk.finish(qs);
+    int qs[kPer];
+    walk.finish(qs);
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            if (FACC)
-                accf[k] += (float)qs[k]; // integers below 2^24: exact
-            else
-                acci[k] += qs[k];
-        }
+    for (int k = 0; k < kPer; ++k) {
+        if (FACC)
+            accf[k] += (float)qs[k]; // integers below 2^24: exact
+        else
+            acci[k] += qs[k];
     }
 }
 
@@ -1633,27 +1634,34 @@ __device__ __forceinline__ void accumulate_workers_pk16(const void *__restrict__
 #pragma unroll
     for (int p = 0; p < kPer / 2; ++p)
         acc2[p] = as_i16x2(0u);
+    int qs[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
     if constexpr (SKIP) {
+        SkipQueueWalk<DT, GQ_SCHEME_L, PRE> walk{&wave_skip_queue(), x, d, span, vec, q, sigma16,
+                                                 k0, k1, wb};
+        walk.start();
         for (int64_t c = 0; c < n; c += 64) {
             const uint32_t Hl = span_threshold<PRE>(bounds, bstride, span, c, n, q, sigma16, sparse_ok);
             const int cnt = (int)(n - c < 64 ? n - c : 64);
             auto row = [&](int64_t i, uint32_t H, const uint4 &A) {
-                if (live && (H > 0xFFFFu || min_half16(A) <= H))
+                if (H <= 0xFFFFu)
+                    walk.offer(i, live && min_half16(A) <= H);
+                else if (live)
                     pk16_row<DT, PRE>(x, d, j0, vec, i, A, q, sigma16, top16, blo, bhi,
                                       wb + (uint32_t)i, k0, k1, acc2);
             };
             int r = 0;
-            // two workers per step: two independent Philox chains in flight
             for (; r + 1 < cnt; r += 2) {
                 const uint4 A0 = philox10(make_uint4(blo, bhi, wb + (uint32_t)(c + r), 0u), k0, k1);
                 const uint4 A1 = philox10(make_uint4(blo, bhi, wb + (uint32_t)(c + r + 1), 0u), k0, k1);
                 row(c + r, __builtin_amdgcn_readlane(Hl, r), A0);
                 row(c + r + 1, __builtin_amdgcn_readlane(Hl, r + 1), A1);
+                walk.drain_full();
             }
             if (r < cnt)
                 row(c + r, __builtin_amdgcn_readlane(Hl, r),
                     philox10(make_uint4(blo, bhi, wb + (uint32_t)(c + r), 0u), k0, k1));
         }
+        walk.finish(qs);
     } else {
         for (int64_t i = 0; i < n; ++i) {
             const uint4 A = philox10(make_uint4(blo, bhi, wb + (uint32_t)i, 0u), k0, k1);
@@ -1663,16 +1671,18 @@ __device__ __forceinline__ void accumulate_workers_pk16(const void *__restrict__
     }
 #pragma unroll
     for (int p = 0; p < kPer / 2; ++p) {
-        acc[2 * p] = acc2[p].x;
-        acc[2 * p + 1] = acc2[p].y;
+        acc[2 * p] = acc2[p].x + qs[2 * p];
+        acc[2 * p + 1] = acc2[p].y + qs[2 * p + 1];
     }
 }
-// SKIP 1 or 2: with pass 1's span bounds (u16 [n][bstride]), groups whose
-// codes are provably all 0 are neither loaded nor quantized (the zero-code
-// skip); 2 quantizes the remaining groups of sparse rows through the wave's
-// candidate queue, 1 in their own lanes.
-template <int DT, int SCH, int ACC, int SKIP>
-__global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restrict__ x, int64_t n,
+// SKIP: with pass 1's span bounds (u16 [n][bstride]), groups whose codes are
+// provably all 0 are neither loaded nor quantized (the zero-code skip); the
+// rest of sparse spans go through the wave's candidate queue.
+// With SKIP and standard dithering the registers are capped for 6 waves per
+// SIMD (measured 2-5% faster than 5; exponential dithering would spill).
+template <int DT, int SCH, int ACC, bool SKIP>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(SKIP && SCH == GQ_SCHEME_L ? 6 : 1))) void k_compress_mean(const void *__restrict__ x, int64_t n,
                                                             int64_t d, int s, uint64_t seed,
                                                             const float *__restrict__ norm_dev,
                                                             float *__restrict__ mean,
@@ -1685,9 +1695,8 @@ __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restri
     // measured -6% on this pass for fp32 at 0.8-16 GB (4 and 5 blocks alike,
     // 6 no gain); bf16, bound by vector ALU work, needs the full residency
     // (5 blocks: +15%).  Only the code-sum packing uses the first 8 KB.
-    // With the candidate queue each wave packs in its own queue (free by then).
-    constexpr bool QUEUED = SKIP == 2 && ACC != kAccPk16;
-    __shared__ alignas(16) uint32_t lds[QUEUED ? 4 : DT == GQ_IN_F32 && !SKIP ? 8192 : kTile];
+    // With SKIP each wave packs in its own candidate queue (free by then).
+    __shared__ alignas(16) uint32_t lds[SKIP ? 4 : DT == GQ_IN_F32 ? 8192 : kTile];
     // Reverse of pass 1's order: pass 1's blocks finish on the last chunks of
     // every row, so starting pass 2 there re-reads data the memory-side cache
     // still holds (measured: -7% time on an 0.8 GB input, neutral on 7-16 GB).
@@ -1713,10 +1722,10 @@ __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restri
                     accumulate_workers_pk16<DT, false, true>(x, n, d, j0, vec, q, k0, k1, acc, 0u,
                                                              live, bounds, bstride, span, sparse_ok);
             } else if (q.prescale)
-                accumulate_workers_skip<DT, SCH, true, ACC == kAccF32, QUEUED>(
+                accumulate_workers_skip<DT, SCH, true, ACC == kAccF32>(
                     x, n, d, j0, vec, live, q, k0, k1, bounds, bstride, span, sigK, sparse_ok, accf, acc);
             else
-                accumulate_workers_skip<DT, SCH, false, ACC == kAccF32, QUEUED>(
+                accumulate_workers_skip<DT, SCH, false, ACC == kAccF32>(
                     x, n, d, j0, vec, live, q, k0, k1, bounds, bstride, span, sigK, sparse_ok, accf, acc);
             if (ACC == kAccF32) {
 #pragma unroll
@@ -1751,7 +1760,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_mean(const void *__restri
     }
     if (code_sum)
         store_tile_packed(lds, acc, W, code_sum, tile, row_bytes(d, W),
-                          QUEUED ? (uint32_t *)wave_skip_queue().sum : nullptr);
+                          SKIP ? (uint32_t *)wave_skip_queue().sum : nullptr);
 }
 
 // Many workers (n >= kSums8MinN, fp32): the compress step in two kernels.
@@ -2221,10 +2230,9 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_words_lds(
 // (ACC as in k_compress_mean: fp32 sums, int32, or packed 16-bit pairs for
 // bf16 standard dithering), then the biased sums go to LDS and are
 // assembled into word quads as in k_quantize_words.
-// SKIP 1 or 2: with pass 1's span bounds, as the fused pass (each
-// 2048-coordinate segment is one fused-pass tile: a wave per 512-coordinate
-// span).
-template <int DT, int SCH, int FPW, int ACC, int SKIP>
+// SKIP: with pass 1's span bounds, as the fused pass (each 2048-coordinate
+// segment is one fused-pass tile: a wave per 512-coordinate span).
+template <int DT, int SCH, int FPW, int ACC, bool SKIP>
 __global__ __launch_bounds__(kThreads) void k_compress_words(const void *__restrict__ x, int64_t n,
                                                              int64_t d, int s, uint64_t seed,
                                                              int64_t worker_base,
@@ -2262,11 +2270,11 @@ __global__ __launch_bounds__(kThreads) void k_compress_words(const void *__restr
             } else {
                 float accf[kPer] = {0, 0, 0, 0, 0, 0, 0, 0};
                 if (q.prescale)
-                    accumulate_workers_skip<DT, SCH, true, ACC == kAccF32, SKIP == 2>(
+                    accumulate_workers_skip<DT, SCH, true, ACC == kAccF32>(
                         x, n, d, j0, vec, live, q, k0, k1, bounds, bstride, span, sigK, sparse_ok,
                         accf, acc, wb);
                 else
-                    accumulate_workers_skip<DT, SCH, false, ACC == kAccF32, SKIP == 2>(
+                    accumulate_workers_skip<DT, SCH, false, ACC == kAccF32>(
                         x, n, d, j0, vec, live, q, k0, k1, bounds, bstride, span, sigK, sparse_ok,
                         accf, acc, wb);
                 if (ACC == kAccF32) {
@@ -2336,9 +2344,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_words(const void *__restr
 // 16-bit pairs for bf16 standard dithering with n M < 2^15, else fp32 sums
 // while n M <= 2^24 (always true for W <= 16), else int32.
 // bounds != nullptr: the zero-code skip with pass 1's span bounds.
-// SKIP: 0 none, 1 candidates in their own lanes, 2 through the queue (the
-// packed accumulators keep their own lanes).
-template <int DT, int SCH, int F, int SKIP>
+template <int DT, int SCH, int F, bool SKIP>
 void launch_compress_words_as(dim3 grid, hipStream_t st, bool pk16, bool facc, const void *x,
                               int64_t n, int64_t d, int s, uint64_t seed, int64_t worker_base,
                               const float *norm_dev, uint32_t *out, int W, uint32_t bias,
@@ -2347,7 +2353,7 @@ void launch_compress_words_as(dim3 grid, hipStream_t st, bool pk16, bool facc, c
     const dim3 block(kThreads);
     if constexpr (DT == GQ_IN_BF16 && SCH == GQ_SCHEME_L && F > 1) {
         if (pk16) {
-            k_compress_words<DT, SCH, F, kAccPk16, SKIP ? 1 : 0><<<grid, block, 0, st>>>(
+            k_compress_words<DT, SCH, F, kAccPk16, SKIP><<<grid, block, 0, st>>>(
                 x, n, d, s, seed, worker_base, norm_dev, out, W, bias, rwords, bounds, bstride);
             return;
         }
@@ -2371,18 +2377,14 @@ void launch_compress_words(dim3 grid, hipStream_t st, bool pk16, bool facc, cons
                            const float *norm_dev, uint32_t *out, int W, uint32_t bias,
                            int64_t rwords, const uint16_t *bounds)
 {
-    if (bounds && n >= kQueueMinRows)
-        launch_compress_words_as<DT, SCH, F, 2>(grid, st, pk16, facc, x, n, d, s, seed,
-                                                worker_base, norm_dev, out, W, bias, rwords,
-                                                bounds, bound_stride(d));
-    else if (bounds)
-        launch_compress_words_as<DT, SCH, F, 1>(grid, st, pk16, facc, x, n, d, s, seed,
-                                                worker_base, norm_dev, out, W, bias, rwords,
-                                                bounds, bound_stride(d));
+    if (bounds)
+        launch_compress_words_as<DT, SCH, F, true>(grid, st, pk16, facc, x, n, d, s, seed,
+                                                   worker_base, norm_dev, out, W, bias, rwords,
+                                                   bounds, bound_stride(d));
     else
-        launch_compress_words_as<DT, SCH, F, 0>(grid, st, pk16, facc, x, n, d, s, seed,
-                                                worker_base, norm_dev, out, W, bias, rwords,
-                                                nullptr, 0);
+        launch_compress_words_as<DT, SCH, F, false>(grid, st, pk16, facc, x, n, d, s, seed,
+                                                    worker_base, norm_dev, out, W, bias, rwords,
+                                                    nullptr, 0);
 }
 
 // What a native integer SUM over the n rows computes: the word-wise sum
@@ -3169,20 +3171,15 @@ int32_t launch_compress(const void *x, int32_t dtype, int64_t n, int64_t d, int3
     const int64_t nm = n * top_code(s, scheme);
     const bool facc = nm <= ((int64_t)1 << 24);
     const bool pk16 = dtype == GQ_IN_BF16 && scheme == GQ_SCHEME_L && nm < ((int64_t)1 << 15);
-    // skip modes as in k_compress_mean: the queue from kQueueMinRows rows
-    // (never for the packed accumulators)
-    const bool queue = n >= kQueueMinRows;
 #define GQ_COMPRESS(DT, SCH, ACC)                                                                 \
     do {                                                                                          \
-        if (bounds && queue && ACC != kAccPk16)                                                   \
-            k_compress_mean<DT, SCH, ACC, ACC == kAccPk16 ? 1 : 2><<<grid, block, 0, st>>>(        \
-                x, n, d, s, seed, norm_dev, mean, cs, W, bounds, bstride);                        \
-        else if (bounds)                                                                          \
-            k_compress_mean<DT, SCH, ACC, 1><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev,  \
-                                                                     mean, cs, W, bounds, bstride); \
+        if (bounds)                                                                               \
+            k_compress_mean<DT, SCH, ACC, true><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev, \
+                                                                        mean, cs, W, bounds, bstride); \
         else                                                                                      \
-            k_compress_mean<DT, SCH, ACC, 0><<<grid, block, 0, st>>>(x, n, d, s, seed, norm_dev,  \
-                                                                     mean, cs, W, nullptr, 0);    \
+            k_compress_mean<DT, SCH, ACC, false><<<grid, block, 0, st>>>(x, n, d, s, seed,         \
+                                                                         norm_dev, mean, cs, W,   \
+                                                                         nullptr, 0);             \
     } while (0)
 #define GQ_COMPRESS_DT(DT)                          \
     do {                                            \
