@@ -29,7 +29,7 @@
 //                    with n s < 2^15 (vector-ALU bound), the rounding is one
 //                    integer add per coordinate and pairs of coordinates are
 //                    signed and summed in packed int16 lanes.
-//   k_norm_oneshot / k_norm_mid: pass 1 for fp32 inputs above 1 GiB, 16 KB
+//   k_norm_oneshot / k_norm_mid: pass 1 for inputs above 256 MiB, 16 KB
 //                    one-shot blocks, then a fixed-order middle reduction.
 //   k_quantize / k_reduce_codes / k_dequantize: the same steps unfused, with
 //                    W-bit codes packed through LDS into coalesced words.
@@ -173,17 +173,17 @@ NormGeom norm_geom(int64_t n, int64_t d)
     return g;
 }
 
-// Pass 1 for fp32 inputs above 1 GiB: one-shot blocks of 512 threads reading
+// Pass 1 for inputs above 256 MiB: one-shot blocks of 512 threads reading
 // 16 KB of one row each (row-major block order, one partial per block), then
 // a middle kernel that reduces every 2048 consecutive partials of a row in a
-// fixed order.  Measured on the 7 and 16 GB inputs: the whole operation
-// -2.5%.  Smaller inputs and bf16 keep the chunk-major order, which ends on
-// the columns pass 2 starts with (re-read from the memory-side cache): it
-// measured faster on the 0.8 GB input, and for bf16 the one-shot pass was
-// no faster while the whole operation lost 2%.
+// fixed order.  Measured on the 7 and 16 GB fp32 inputs: the whole operation
+// -2.5%; with the wave sums by DPP moves, on the 5.7 GB bf16 input the pass
+// 978 -> 920 us (whole operation -4.5%) and on the 0.8 GB fp32 input
+// 146 -> 134 us (whole operation -2%).  Smaller inputs keep the chunk-major
+// blocks: fewer, longer-lived blocks and no middle launch.
 constexpr int kOsThreads = 512;
 constexpr int64_t kOsBlockBytes = 16 * 1024;
-constexpr double kOsMinBytes = 1073741824.0;
+constexpr double kOsMinBytes = 268435456.0;
 constexpr int kMidThreads = 256;
 constexpr int64_t kMidPer = 8 * kMidThreads; // partials per middle block
 
@@ -194,7 +194,7 @@ struct OneShotGeom {
 OneShotGeom oneshot_geom(int64_t n, int64_t d, int64_t elem_bytes)
 {
     OneShotGeom o{false, kOsBlockBytes / elem_bytes, 0, 0};
-    if (elem_bytes != 4 || (double)n * (double)d * (double)elem_bytes <= kOsMinBytes)
+    if ((double)n * (double)d * (double)elem_bytes <= kOsMinBytes)
         return o;
     o.on = true;
     o.bpr = (d + o.span - 1) / o.span;

@@ -442,9 +442,9 @@ def workload_config(w, wmin):
 
 
 def norm_pass_kernel(w):
-    """The kernel that reads x in pass 1: one-shot 16 KB blocks for fp32 inputs
-    above 1 GiB, chunk-major blocks otherwise."""
-    big = w.dtype == "f32" and w.n * w.d * 4 > (1 << 30)
+    """The kernel that reads x in pass 1: one-shot 16 KB blocks for inputs
+    above 256 MiB, chunk-major blocks otherwise."""
+    big = w.n * w.d * w.elem_bytes > (1 << 28)
     return "k_norm_oneshot" if big else "k_norm_partial"
 
 

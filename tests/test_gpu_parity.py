@@ -387,10 +387,10 @@ def test_local_qsgd_matches_oracle(n, d, dtype):
 
 
 # ---------------------------------------------------------------------------
-# fp32 inputs above 1 GiB take the one-shot norm pass (16 KB blocks, a
-# middle reduction): ragged, unaligned and aligned rows, every kind of order,
-# and the per-worker norms of the ablation; a bf16 input of the same size
-# stays on the chunk-major pass.
+# Inputs above 256 MiB take the one-shot norm pass (16 KB blocks, a middle
+# reduction): ragged, unaligned and aligned rows, every kind of order, and
+# the per-worker norms of the ablation; the bf16 case (just above 1 GiB,
+# ragged rows) reads two groups per thread.
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("n,d,dtype,q,p", [(3, 89_478_487, "f32", 2.0, 2.0),
