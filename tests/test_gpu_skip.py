@@ -9,7 +9,9 @@ span's largest |x| computed in numpy.  Cases aim at the skip's own edges:
 spans where some t reaches the first level (dense) beside sparse ones, inf
 and NaN inputs, more than 64 workers (thresholds are shared 64 rows at a
 time), ragged rows, norms below 2^-64 (the exact pre-scale), a scaled sigma
-that overflows fp32, bf16 inputs on both accumulators, and code sums.
+that overflows fp32, bf16 inputs on both accumulators, code sums, and
+sparse spans where most groups pass (the per-wave candidate queue filled
+and drained thousands of times).
 """
 import math
 import sys
@@ -120,6 +122,11 @@ CASES = [
     (4, 4096, "f32", "L", 1, 2.0, 2.0, "mixed"),
     (3, 9000, "f32", "L", 127, 1.5, 3.0, "mixed"),
     (600, 2500, "f32", "E", 16, 2.0, 2.0, "mixed"),  # n M > 2^24: the int32 accumulator
+    # sparse spans whose thresholds let most groups through: thousands of
+    # queue entries per span, the candidate ring wrapping many times
+    (200, 1030, "f32", "L", 1, 2.0, INF, "plain"),
+    (200, 2048, "bf16", "L", 1, 2.0, INF, "plain"),
+    (150, 700, "f32", "E", 3, 2.0, INF, "plain"),
 ]
 
 
