@@ -1697,9 +1697,10 @@ __attribute__((amdgpu_waves_per_eu(SKIP && SCH == GQ_SCHEME_L ? 6 : 1))) void k_
     // (5 blocks: +15%).  Only the code-sum packing uses the first 8 KB.
     // With SKIP each wave packs in its own candidate queue (free by then).
     __shared__ alignas(16) uint32_t lds[SKIP ? 4 : DT == GQ_IN_F32 ? 8192 : kTile];
-    // Reverse of pass 1's order: pass 1's blocks finish on the last chunks of
-    // every row, so starting pass 2 there re-reads data the memory-side cache
-    // still holds (measured: -7% time on an 0.8 GB input, neutral on 7-16 GB).
+    // Reverse of pass 1's order: the chunk-major pass 1 (inputs up to 256 MiB)
+    // finishes on the last chunks of every row, so starting pass 2 there
+    // re-reads data the memory-side cache still holds (measured: -7% time on
+    // an 0.8 GB input when it took that pass; neutral on 7-16 GB).
     const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;
     const int64_t j0 = tile * kTile + (int64_t)threadIdx.x * kPer;
     const QParams q = make_qparams(*norm_dev, n, s, SCH);
